@@ -1,0 +1,16 @@
+"""fp64 CPU oracle for relative attention -- test infrastructure only.
+
+Only ``tests/``, ``__graft_entry__.smoke()`` and the ``cpu_baseline`` leg of
+``bench.py`` may import this package.  The product path never does.
+"""
+
+from .relattn_oracle import (  # noqa: F401
+    attention_weights,
+    brute_force_prefill,
+    decode,
+    logit_rows,
+    prefill,
+    rel_logits,
+    scale_factor,
+    sheared_bias,
+)

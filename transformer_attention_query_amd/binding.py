@@ -1,0 +1,240 @@
+"""ctypes binding for ``librelattn.so`` (the C ABI declared in include/relattn.h).
+
+Argument marshalling only: every step of the computation runs in the HIP
+kernels behind the C ABI.  torch supplies device memory (``torch.empty`` for
+outputs and the decode workspace) and the stream (the caller's current
+stream).  There is no CPU or eager fallback: if the library cannot be loaded,
+or a call returns an error, a ``RelAttnError`` is raised.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+import threading
+from typing import Optional, Tuple
+
+import torch
+
+__all__ = ["RelAttnError", "library_path", "load_library", "prefill", "decode", "decode_plan",
+           "rel_logits", "scale_factor", "version"]
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB_NAME = "librelattn.so"
+
+RA_BF16 = 1
+RA_F32 = 2
+_DTYPE_CODE = {torch.bfloat16: RA_BF16, torch.float32: RA_F32}
+
+
+class RelAttnError(RuntimeError):
+    """A non-zero return from the library, with its message."""
+
+
+def library_path() -> str:
+    return os.environ.get("RELATTN_LIBRARY", os.path.join(_HERE, _LIB_NAME))
+
+
+_lib = None
+_lock = threading.Lock()
+
+
+def _declare(lib):
+    c = ctypes
+    vp, i32, i64, f32, sz = c.c_void_p, c.c_int, c.c_longlong, c.c_float, c.c_size_t
+    lib.rel_attn_prefill.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32,
+                                     f32, i32, i32, i32, vp]
+    lib.rel_attn_prefill.restype = i32
+    lib.rel_attn_decode_plan.argtypes = [i32, i32, i32, i32, i32, i32, i32,
+                                         c.POINTER(i32), c.POINTER(sz)]
+    lib.rel_attn_decode_plan.restype = i32
+    lib.rel_attn_decode.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32,
+                                    f32, i32, i32, i32, i32, vp, sz, vp]
+    lib.rel_attn_decode.restype = i32
+    lib.rel_logits.argtypes = [vp, vp, vp, i32, i64, i32, i32, i32, i32, i64, vp]
+    lib.rel_logits.restype = i32
+    lib.rel_attn_last_error.argtypes = []
+    lib.rel_attn_last_error.restype = c.c_char_p
+    lib.rel_attn_version.argtypes = []
+    lib.rel_attn_version.restype = i32
+    lib.rel_attn_scale_factor.argtypes = [i32, i64]
+    lib.rel_attn_scale_factor.restype = c.c_double
+    return lib
+
+
+def load_library():
+    """Load (once) and return the ctypes handle; raise if the library is missing."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    with _lock:
+        if _lib is None:
+            path = library_path()
+            if not os.path.exists(path):
+                raise RelAttnError(
+                    f"{path} not found: build the HIP library first "
+                    "(python -m transformer_attention_query_amd.build)")
+            _lib = _declare(ctypes.CDLL(path))
+    return _lib
+
+
+def _check(rc: int):
+    if rc != 0:
+        msg = load_library().rel_attn_last_error()
+        raise RelAttnError(f"relattn error {rc}: {msg.decode() if msg else ''}")
+
+
+def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:
+    return None if t is None else t.data_ptr()
+
+
+def _stream(device: torch.device) -> int:
+    return torch.cuda.current_stream(device).cuda_stream
+
+
+def _need(t: torch.Tensor, name: str, dtype: torch.dtype, device: torch.device, ndim: int):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a tensor")
+    if t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} has dtype {t.dtype}, expected {dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if t.dim() != ndim:
+        raise ValueError(f"{name} must have {ndim} dims, got {tuple(t.shape)}")
+
+
+def version() -> int:
+    return load_library().rel_attn_version()
+
+
+def scale_factor(seq_len: int, log_scale: bool) -> float:
+    """The library's length-dependent log-scale s for a sequence of ``seq_len`` tokens."""
+    return float(load_library().rel_attn_scale_factor(1 if log_scale else 0, int(seq_len)))
+
+
+def prefill(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, r: Optional[torch.Tensor],
+            P_cols: Optional[torch.Tensor], alpha: float, rel_extent: int, window: int = 0,
+            log_scale: bool = False, return_lse: bool = True,
+            out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None
+            ) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+    """Relative-attention prefill on the current stream.
+
+    q [B,T,Hq,D], k/v [B,T,Hkv,D], r [B,T,Hq,d_r], P_cols [E,d_r] (row d = the
+    projection vector of distance d), all of one dtype (bf16 or fp32) on one GPU.
+    Returns out [B,T,Hq,D] (input dtype) and lse [B,Hq,T] fp32 (or None).
+    """
+    lib = load_library()
+    dev = q.device
+    dt = q.dtype
+    if dt not in _DTYPE_CODE:
+        raise TypeError(f"unsupported dtype {dt}")
+    _need(q, "q", dt, dev, 4)
+    _need(k, "k", dt, dev, 4)
+    _need(v, "v", dt, dev, 4)
+    B, T, Hq, D = q.shape
+    Hkv = k.shape[2]
+    if k.shape != (B, T, Hkv, D) or v.shape != k.shape:
+        raise ValueError(f"k/v shape {tuple(k.shape)}/{tuple(v.shape)} does not match q {tuple(q.shape)}")
+    d_r = 0
+    if rel_extent > 0:
+        _need(r, "r", dt, dev, 4)
+        _need(P_cols, "P_cols", dt, dev, 2)
+        d_r = r.shape[3]
+        if r.shape[:3] != (B, T, Hq):
+            raise ValueError(f"r shape {tuple(r.shape)} does not match q")
+        if P_cols.shape != (rel_extent, d_r):
+            raise ValueError(f"P_cols must be [rel_extent={rel_extent}, d_r={d_r}], got {tuple(P_cols.shape)}")
+    else:
+        r = None
+        P_cols = None
+    if out is None:
+        out = torch.empty_like(q)
+    else:
+        _need(out, "out", dt, dev, 4)
+    if return_lse and lse is None:
+        lse = torch.empty(B, Hq, T, dtype=torch.float32, device=dev)
+    elif not return_lse:
+        lse = None
+    _check(lib.rel_attn_prefill(_ptr(q), _ptr(k), _ptr(v), _ptr(r), _ptr(P_cols), _ptr(out), _ptr(lse),
+                                _DTYPE_CODE[dt], B, T, Hq, Hkv, D, d_r, float(alpha), int(rel_extent),
+                                int(window), 1 if log_scale else 0, _stream(dev)))
+    return out, lse
+
+
+def decode_plan(B: int, L: int, Hq: int, Hkv: int, D: int = 128, num_splits: int = 0,
+                window: int = 0) -> Tuple[int, int]:
+    """(num_splits, workspace_bytes) the decode call will use; a pure function of the shape."""
+    lib = load_library()
+    ns = ctypes.c_int(0)
+    ws = ctypes.c_size_t(0)
+    _check(lib.rel_attn_decode_plan(B, L, Hq, Hkv, D, int(num_splits), int(window),
+                                    ctypes.byref(ns), ctypes.byref(ws)))
+    return ns.value, ws.value
+
+
+def decode(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, r: Optional[torch.Tensor],
+           P_cols: Optional[torch.Tensor], alpha: float, rel_extent: int, window: int = 0,
+           log_scale: bool = False, num_splits: int = 0, return_lse: bool = True,
+           workspace: Optional[torch.Tensor] = None
+           ) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+    """Split-KV decode of one query token per sequence at position L-1.
+
+    q [B,Hq,D], k/v cache [B,L,Hkv,D], r [B,Hq,d_r], P_cols [E,d_r].
+    Returns out [B,Hq,D] and lse [B,Hq] fp32 (or None).
+    """
+    lib = load_library()
+    dev = q.device
+    dt = q.dtype
+    if dt not in _DTYPE_CODE:
+        raise TypeError(f"unsupported dtype {dt}")
+    _need(q, "q", dt, dev, 3)
+    _need(k, "k", dt, dev, 4)
+    _need(v, "v", dt, dev, 4)
+    B, Hq, D = q.shape
+    L, Hkv = k.shape[1], k.shape[2]
+    if k.shape != (B, L, Hkv, D) or v.shape != k.shape:
+        raise ValueError(f"k/v shape {tuple(k.shape)} does not match q {tuple(q.shape)}")
+    d_r = 0
+    if rel_extent > 0:
+        _need(r, "r", dt, dev, 3)
+        _need(P_cols, "P_cols", dt, dev, 2)
+        d_r = r.shape[2]
+        if r.shape[:2] != (B, Hq):
+            raise ValueError(f"r shape {tuple(r.shape)} does not match q")
+        if P_cols.shape != (rel_extent, d_r):
+            raise ValueError(f"P_cols must be [rel_extent={rel_extent}, d_r={d_r}], got {tuple(P_cols.shape)}")
+    else:
+        r = None
+        P_cols = None
+    ns, ws_bytes = decode_plan(B, L, Hq, Hkv, D, num_splits, window)
+    if workspace is None:
+        workspace = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
+    out = torch.empty_like(q)
+    lse = torch.empty(B, Hq, dtype=torch.float32, device=dev) if return_lse else None
+    _check(lib.rel_attn_decode(_ptr(q), _ptr(k), _ptr(v), _ptr(r), _ptr(P_cols), _ptr(out), _ptr(lse),
+                               _DTYPE_CODE[dt], B, L, Hq, Hkv, D, d_r, float(alpha), int(rel_extent),
+                               int(window), 1 if log_scale else 0, ns, _ptr(workspace),
+                               workspace.numel() * workspace.element_size(), _stream(dev)))
+    return out, lse
+
+
+def rel_logits(r: torch.Tensor, P_cols: torch.Tensor, log_scale: bool = False,
+               seq_len: int = 0) -> torch.Tensor:
+    """Dense relative logits s * r . P[:, d] for every d < E: r [n,H,d_r] -> [n,H,E] fp32."""
+    lib = load_library()
+    dev = r.device
+    dt = r.dtype
+    if dt not in _DTYPE_CODE:
+        raise TypeError(f"unsupported dtype {dt}")
+    _need(r, "r", dt, dev, 3)
+    _need(P_cols, "P_cols", dt, dev, 2)
+    n, H, d_r = r.shape
+    E = P_cols.shape[0]
+    if P_cols.shape[1] != d_r:
+        raise ValueError("P_cols must be [E, d_r]")
+    out = torch.empty(n, H, E, dtype=torch.float32, device=dev)
+    _check(lib.rel_logits(_ptr(r), _ptr(P_cols), _ptr(out), _DTYPE_CODE[dt], n, H, d_r, E,
+                          1 if log_scale else 0, int(seq_len if seq_len else n), _stream(dev)))
+    return out

@@ -1,0 +1,119 @@
+"""Seeded synthetic inputs for relative attention, and the named workloads.
+
+This module only draws random numbers and lays them out; it holds none of
+the attention arithmetic, so both the HIP path and the CPU oracle can be fed
+from it without sharing any computation.
+
+Recipe (the same for every workload): a CPU ``torch.Generator`` seeded with
+``seed`` draws, in this order and as float32 standard normals, q, k, v, r and
+then P in the shapes below; P is multiplied by ``p_std`` (0.02, i.e.
+P ~ N(0, 0.02^2)); every tensor is then rounded to the workload dtype.
+
+* prefill: q [B,T,Hq,D], k [B,T,Hkv,D], v [B,T,Hkv,D], r [B,T,Hq,d_r], P [d_r,E]
+* decode:  q [B,Hq,D],   k [B,L,Hkv,D], v [B,L,Hkv,D], r [B,Hq,d_r],   P [d_r,E]
+
+P is drawn in the orientation of the method's notation (column d holds the
+projection for distance d).  The library takes it distance-major, as
+``P_cols`` [E, d_r] with ``P_cols[d] = P[:, d]``: the same numbers, stored so
+that the d_r coefficients of one distance are contiguous.
+"""
+
+from __future__ import annotations
+
+import math
+from dataclasses import dataclass, field
+from typing import Dict, Optional
+
+import torch
+
+__all__ = ["Workload", "WORKLOADS", "make_prefill_inputs", "make_decode_inputs", "make_inputs",
+           "torch_dtype"]
+
+
+def torch_dtype(name: str) -> torch.dtype:
+    return {"bf16": torch.bfloat16, "fp32": torch.float32}[name]
+
+
+@dataclass(frozen=True)
+class Workload:
+    """One named relative-attention workload (shapes, masks and dtype)."""
+    name: str
+    kind: str            # "prefill" or "decode"
+    dtype: str           # "bf16" or "fp32"
+    B: int
+    T: int               # prefill: sequence length; decode: kv length L
+    Hq: int
+    Hkv: int
+    D: int
+    d_r: int
+    E: int               # rel_extent
+    W: int = 0           # sliding window (keys incl. self); 0 = full causal
+    log_scale: bool = False
+    alpha: float = 1.0 / math.sqrt(128.0)
+    num_splits: int = 0  # decode only; 0 = library's choice
+    notes: str = field(default="", compare=False)
+
+
+# The five workloads the kernels are specified and measured on.
+WORKLOADS: Dict[str, Workload] = {
+    "tiny_fp32": Workload(
+        "tiny_fp32", "prefill", "fp32", B=1, T=256, Hq=4, Hkv=1, D=128, d_r=32, E=64,
+        notes="tiny full-causal layer in fp32, GQA 4:1"),
+    "swa_prefill_8k": Workload(
+        "swa_prefill_8k", "prefill", "bf16", B=1, T=8192, Hq=16, Hkv=2, D=128, d_r=128, E=1024, W=1024,
+        notes="sliding-window layer, 1024 keys incl. self, GQA 8:1"),
+    "full_prefill_32k_log": Workload(
+        "full_prefill_32k_log", "prefill", "bf16", B=2, T=32768, Hq=16, Hkv=2, D=128, d_r=128, E=1024,
+        log_scale=True, notes="full causal layer with the length log-scale (s = 1.25)"),
+    "decode_64x8k": Workload(
+        "decode_64x8k", "decode", "bf16", B=64, T=8192, Hq=16, Hkv=2, D=128, d_r=128, E=1024,
+        notes="64 sequences x 1 token, kv length 8192, split-KV"),
+    "decode_1x1m_log": Workload(
+        "decode_1x1m_log", "decode", "bf16", B=1, T=1 << 20, Hq=16, Hkv=2, D=128, d_r=128, E=1024,
+        log_scale=True, notes="1 sequence x 1 token, kv length 2^20, log-scale s = 5/3"),
+}
+
+
+def _draw(gen: torch.Generator, shape) -> torch.Tensor:
+    return torch.randn(*shape, generator=gen, dtype=torch.float32)
+
+
+def make_prefill_inputs(B: int, T: int, Hq: int, Hkv: int, D: int, d_r: int, E: int,
+                        dtype: str = "bf16", seed: int = 0, p_std: float = 0.02,
+                        device: Optional[str] = None) -> Dict[str, torch.Tensor]:
+    """Seeded prefill inputs (see the module docstring for the recipe)."""
+    gen = torch.Generator("cpu").manual_seed(seed)
+    dt = torch_dtype(dtype)
+    q = _draw(gen, (B, T, Hq, D)).to(dt)
+    k = _draw(gen, (B, T, Hkv, D)).to(dt)
+    v = _draw(gen, (B, T, Hkv, D)).to(dt)
+    r = _draw(gen, (B, T, Hq, d_r)).to(dt)
+    P = (_draw(gen, (d_r, E)) * p_std).to(dt)
+    out = {"q": q, "k": k, "v": v, "r": r, "P": P, "P_cols": P.t().contiguous()}
+    if device is not None:
+        out = {n: t.to(device) for n, t in out.items()}
+    return out
+
+
+def make_decode_inputs(B: int, L: int, Hq: int, Hkv: int, D: int, d_r: int, E: int,
+                       dtype: str = "bf16", seed: int = 0, p_std: float = 0.02,
+                       device: Optional[str] = None) -> Dict[str, torch.Tensor]:
+    """Seeded decode inputs: one query token per sequence, KV cache of length L."""
+    gen = torch.Generator("cpu").manual_seed(seed)
+    dt = torch_dtype(dtype)
+    q = _draw(gen, (B, Hq, D)).to(dt)
+    k = _draw(gen, (B, L, Hkv, D)).to(dt)
+    v = _draw(gen, (B, L, Hkv, D)).to(dt)
+    r = _draw(gen, (B, Hq, d_r)).to(dt)
+    P = (_draw(gen, (d_r, E)) * p_std).to(dt)
+    out = {"q": q, "k": k, "v": v, "r": r, "P": P, "P_cols": P.t().contiguous()}
+    if device is not None:
+        out = {n: t.to(device) for n, t in out.items()}
+    return out
+
+
+def make_inputs(w: Workload, seed: int = 0, device: Optional[str] = None) -> Dict[str, torch.Tensor]:
+    """Inputs of a named workload."""
+    if w.kind == "prefill":
+        return make_prefill_inputs(w.B, w.T, w.Hq, w.Hkv, w.D, w.d_r, w.E, w.dtype, seed, device=device)
+    return make_decode_inputs(w.B, w.T, w.Hq, w.Hkv, w.D, w.d_r, w.E, w.dtype, seed, device=device)
