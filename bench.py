@@ -1,0 +1,242 @@
+"""Benchmark of the relative-attention hot path on one MI355X.
+
+A step is one prefill call (the whole forward: scores, relative bias, mask,
+online softmax, PV, epilogue) of the sliding-window layer (B=1, T=8192,
+Hq=16, Hkv=2, D=128, d_r=128, rel_extent=1024, window=1024, bf16) on inputs
+already resident in HBM.  The line also reports the split-KV decode of 64
+sequences x 8192 keys (KV GB/s), each against its roofline, and the fp64 CPU
+oracle timed on a bounded sample of the prefill workload.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA, published
+PEAK_HBM_GBPS = 8000.0      # MI355X HBM3E, published
+PREFILL_WORKLOAD = "swa_prefill_8k"
+DECODE_WORKLOAD = "decode_64x8k"
+PREFILL_KERNEL = "prefill_kernel"
+DECODE_KERNEL = "decode_split_kernel"
+
+
+def prefill_work(T: int, Hq: int, D: int, d_r: int, E: int, W: int, rows=None):
+    """Algorithmic flops of a prefill: 4*D per visible (i, j, h) pair (q.k and
+    p.v) plus 2*d_r per needed relative-logit entry (r.P for distances
+    0..min(i, E-1) that the mask leaves visible).  Masked pairs, skipped tiles
+    and softmax arithmetic are not counted."""
+    if rows is None:
+        rows = range(T)
+    pairs = 0
+    rel = 0
+    for i in rows:
+        vis = i + 1 if W == 0 else min(i + 1, W)
+        pairs += vis
+        rel += min(vis, E)
+    return Hq * (pairs * 4 * D + rel * 2 * d_r), Hq * pairs, Hq * rel
+
+
+def decode_bytes(B: int, L: int, Hq: int, Hkv: int, D: int, d_r: int, E: int, W: int, elem: int = 2):
+    """Algorithmic HBM bytes of a decode: K and V of every visible key, plus
+    q, r and out of every sequence and P once."""
+    vis = L if W == 0 else min(L, W)
+    kv = B * vis * Hkv * D * 2 * elem
+    per_seq = B * Hq * (D + d_r + D) * elem
+    return kv + per_seq + E * d_r * elem, kv
+
+
+def _src_hash(*names):
+    h = hashlib.sha256()
+    for n in names:
+        with open(os.path.join(ROOT, "transformer_attention_query_amd", "csrc", n), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def _traffic(kernel: str, src_hash: str):
+    """Measured HBM bytes per launch from the committed counter summary, if it
+    was taken on the current kernel source; else None."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    try:
+        data = json.load(open(path))
+    except (OSError, ValueError):
+        return None
+    ent = data.get(kernel)
+    if not ent or ent.get("src_hash") != src_hash:
+        return None
+    return ent.get("bytes_per_launch")
+
+
+def _time_launches(fn, steps: int, warmup: int, stream, before=None):
+    """Run fn() warmup times, then `steps` times between synchronisations.
+    Returns (total ms over the steps, list of per-launch ms from event pairs)."""
+    import torch
+    for i in range(warmup):
+        if before:
+            before(i)
+        fn(i)
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0.record(stream)
+    for i in range(steps):
+        if before:
+            before(i)
+        ev[i][0].record(stream)
+        fn(i)
+        ev[i][1].record(stream)
+    t1.record(stream)
+    torch.cuda.synchronize()
+    return t0.elapsed_time(t1), [a.elapsed_time(b) for a, b in ev]
+
+
+def bench_prefill(steps: int, warmup: int):
+    import torch
+    import transformer_attention_query_amd as ra
+    from transformer_attention_query_amd import inputs as tinputs
+
+    w = tinputs.WORKLOADS[PREFILL_WORKLOAD]
+    x = {n: t.cuda() for n, t in tinputs.make_inputs(w, seed=0).items()}
+    out = torch.empty_like(x["q"])
+    lse = torch.empty(w.B, w.Hq, w.T, dtype=torch.float32, device="cuda")
+    stream = torch.cuda.current_stream()
+
+    def step(_i):
+        ra.prefill(x["q"], x["k"], x["v"], x["r"], x["P_cols"], w.alpha, w.E, w.W, w.log_scale, out=out, lse=lse)
+
+    total_ms, per = _time_launches(step, steps, warmup, stream)
+    flops, pairs, rel = prefill_work(w.T, w.Hq, w.D, w.d_r, w.E, w.W)
+    flops *= w.B
+    ms_step = total_ms / steps
+    kernel_ms = sum(per) / len(per)
+    return w, flops, ms_step, kernel_ms, per
+
+
+def bench_decode(steps: int, warmup: int):
+    import torch
+    import transformer_attention_query_amd as ra
+    from transformer_attention_query_amd import inputs as tinputs
+
+    w = tinputs.WORKLOADS[DECODE_WORKLOAD]
+    x = {n: t.cuda() for n, t in tinputs.make_inputs(w, seed=0).items()}
+    # Two copies of the cache, used alternately: each launch reads 512 MiB, so
+    # the copy it reads was last touched two launches ago, far beyond the 256 MB
+    # MALL and the L2s.
+    k2 = [x["k"], x["k"].clone()]
+    v2 = [x["v"], x["v"].clone()]
+    ns, ws_bytes = ra.decode_plan(w.B, w.T, w.Hq, w.Hkv, w.D, w.num_splits, w.W)
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device="cuda")
+    stream = torch.cuda.current_stream()
+
+    def step(i):
+        ra.decode(x["q"], k2[i % 2], v2[i % 2], x["r"], x["P_cols"], w.alpha, w.E, w.W, w.log_scale,
+                  num_splits=ns, workspace=ws)
+
+    total_ms, per = _time_launches(step, steps, warmup, stream)
+    nbytes, kv = decode_bytes(w.B, w.T, w.Hq, w.Hkv, w.D, w.d_r, w.E, w.W)
+    return w, nbytes, kv, total_ms / steps, sum(per) / len(per), ns
+
+
+def cpu_baseline(target_s: float = 15.0):
+    """The fp64 oracle, as it stands, on query rows of the prefill workload."""
+    import torch
+    import oracle
+    from transformer_attention_query_amd import inputs as tinputs
+
+    w = tinputs.WORKLOADS[PREFILL_WORKLOAD]
+    x = tinputs.make_inputs(w, seed=0)
+    threads = torch.get_num_threads()
+    stride_rows = lambda n: list(range(w.T - 1, -1, -max(1, w.T // n)))[:n]  # noqa: E731
+    # calibrate on a few rows, then run a sample sized for about target_s
+    t = time.perf_counter()
+    oracle.prefill(x["q"], x["k"], x["v"], x["r"], x["P"], w.alpha, w.E, w.W, w.log_scale, rows=stride_rows(8))
+    per_row = (time.perf_counter() - t) / 8
+    n = int(max(8, min(w.T, target_s / max(per_row, 1e-6))))
+    rows = stride_rows(n)
+    t = time.perf_counter()
+    oracle.prefill(x["q"], x["k"], x["v"], x["r"], x["P"], w.alpha, w.E, w.W, w.log_scale, rows=rows)
+    dt = time.perf_counter() - t
+    flops, _, _ = prefill_work(w.T, w.Hq, w.D, w.d_r, w.E, w.W, rows=rows)
+    return {"value": flops * w.B / dt / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+            "sample": f"{len(rows)} of {w.T} query rows (all {w.Hq} heads, evenly spaced) of {w.name}, "
+                      f"fp64 torch-CPU oracle, {dt:.1f} s wall"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-decode", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py measures one GPU only: the relative-attention kernels run on a single MI355X "
+              "and this build has no multi-GPU path (--gpus must be 1)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import transformer_attention_query_amd as ra
+    ra.load_library()  # fail loudly if the HIP library is missing
+    if not torch.cuda.is_available():
+        print("no GPU visible", file=sys.stderr)
+        sys.exit(1)
+
+    w, flops, ms_step, kernel_ms, per = bench_prefill(args.steps, args.warmup)
+    print(f"# prefill {w.name}: {ms_step * 1e3:.1f} us/step, kernel {kernel_ms * 1e3:.1f} us "
+          f"(min {min(per) * 1e3:.1f}, max {max(per) * 1e3:.1f})", file=sys.stderr, flush=True)
+    value = flops / (ms_step * 1e-3) / 1e12
+    achieved = flops / (kernel_ms * 1e-3) / 1e12
+    line = {
+        "metric": "relative-attention prefill TFLOP/s + decode KV GB/s (% of MI355X peak)",
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": w.name, "B": w.B, "T": w.T, "Hq": w.Hq, "Hkv": w.Hkv, "D": w.D, "d_r": w.d_r,
+                   "rel_extent": w.E, "window": w.W, "log_scale": w.log_scale, "alpha": "1/sqrt(128)",
+                   "algorithmic_flops": flops},
+        "roofline": {"bound": "mfma", "kernel": PREFILL_KERNEL, "achieved": round(achieved, 2),
+                     "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+                     "traffic": _traffic(PREFILL_KERNEL, _src_hash("prefill.hip", "device_common.hpp")),
+                     "avg_launch_us": round(kernel_ms * 1e3, 2)},
+    }
+    if not args.no_decode:
+        dw, nbytes, kv, d_ms, d_kernel_ms, ns = bench_decode(args.steps, args.warmup)
+        gbps = nbytes / (d_ms * 1e-3) / 1e9
+        kgbps = nbytes / (d_kernel_ms * 1e-3) / 1e9
+        print(f"# decode {dw.name}: {d_ms * 1e3:.1f} us/step ({ns} splits)", file=sys.stderr, flush=True)
+        line["decode"] = {"workload": dw.name, "value": round(gbps, 1), "unit": "GB/s", "ms_per_step": round(d_ms, 5),
+                          "num_splits": ns, "algorithmic_bytes": nbytes,
+                          "roofline": {"bound": "hbm", "kernel": DECODE_KERNEL + "+merge", "achieved": round(kgbps, 1),
+                                       "peak": PEAK_HBM_GBPS, "unit": "GB/s",
+                                       "frac": round(kgbps / PEAK_HBM_GBPS, 4),
+                                       "traffic": _traffic(DECODE_KERNEL, _src_hash("decode.hip", "device_common.hpp")),
+                                       "avg_launch_us": round(d_kernel_ms * 1e3, 2)}}
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline()
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,129 @@
+/*
+ * relattn.h -- C ABI of the MI355X (gfx950) relative-attention forward library.
+ *
+ * The operation (page "SGLang and Miles Add Day-0 Support for Inkling",
+ * section "Attention with Relative Positional Embedding"):
+ *
+ *   rel_logits(t,h,d) = r[t,h,:] . P[:,d]                      for d in [0, E)
+ *   l(i,j,h) = s*alpha * q[i,h,:] . k[j,g(h),:]
+ *              + [0 <= i-j < E] * s * rel_logits(i,h,i-j)
+ *   out[i,h,:] = sum_j softmax_j(l(i,.,h)) * v[j,g(h),:]
+ *
+ * with keys j > i masked (causal) and, for a sliding-window layer, keys with
+ * i-j >= window masked too ("Attention layout" paragraph of that section).
+ * s is the length-dependent log-scale on q and on the relative logits; the
+ * pages give no formula, this library uses s = max(1, ln(Lseq)/ln(4096)) when
+ * log_scale is set and s = 1 otherwise (Lseq = T for prefill, L for decode,
+ * seq_len for rel_logits).  GQA: g(h) = h / (Hq/Hkv).
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * - Every tensor is caller-owned device memory, row-major and contiguous, with
+ *   a 16-byte aligned base address.  Inputs are read only; outputs are fully
+ *   overwritten and must not alias an input.
+ * - dtype: RA_BF16 or RA_F32 for q, k, v, r, P and out (one dtype per call);
+ *   lse and the rel_logits output are always float32.
+ * - P is passed distance-major: P_cols[E][d_r] with P_cols[d][c] = P[c][d],
+ *   i.e. row d holds the d_r coefficients that r is dotted with for distance d
+ *   (the layout of a linear-layer weight mapping d_r features to E outputs).
+ * - Supported shapes: D == 128; d_r a multiple of 16 with 16 <= d_r <= 128
+ *   (ignored when rel_extent == 0); Hq % Hkv == 0.  Others return
+ *   RA_ERR_UNSUPPORTED.
+ * - Work is enqueued on `stream` (a hipStream_t; NULL = the legacy default
+ *   stream) and the call returns without synchronising, copying to the host or
+ *   reading device data on the host, so calls can be captured in a hipGraph.
+ *   The library allocates no device memory and keeps no per-pointer state.
+ * - Errors: argument errors are detected on the host before any HIP call and
+ *   return a negative code; a failed launch returns RA_ERR_HIP.  In both cases
+ *   rel_attn_last_error() returns a message for the calling thread.  The
+ *   library never aborts or prints.  A device fault surfaces at the caller's
+ *   next synchronisation, as with any HIP kernel.
+ * - Results are deterministic: the same inputs give the same bits (no atomics,
+ *   fixed reduction orders).
+ */
+#ifndef RELATTN_H
+#define RELATTN_H
+
+#include <stddef.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum {
+  RA_OK = 0,
+  RA_ERR_INVALID_ARG = -1, /* null/misaligned pointer, negative or inconsistent size */
+  RA_ERR_UNSUPPORTED = -2, /* legal but not implemented (D != 128, d_r outside range, ...) */
+  RA_ERR_WORKSPACE = -3,   /* decode workspace missing or smaller than the plan */
+  RA_ERR_HIP = -4          /* a HIP runtime call or kernel launch failed */
+};
+
+enum { RA_BF16 = 1, RA_F32 = 2 };
+
+/*
+ * Prefill (self-attention over positions 0..T-1 of each sequence).
+ *   q   [B, T, Hq, D]       k, v [B, T, Hkv, D]       r [B, T, Hq, d_r]
+ *   P_cols [E, d_r]         out [B, T, Hq, D] (dtype)  lse [B, Hq, T] float32 or NULL
+ * alpha: the attention scale (e.g. 1/sqrt(D)).  rel_extent E >= 0 (0 = no
+ * relative bias; r and P_cols may then be NULL).  window >= 0 (0 = full
+ * causal; W >= 1 keeps keys with 0 <= i-j < W).  log_scale: 0 or 1.
+ * lse[b,h,i] = natural log of sum_j exp(l(i,j,h)).
+ * B == 0 or T == 0 is a no-op that returns RA_OK.
+ */
+int rel_attn_prefill(const void* q, const void* k, const void* v, const void* r,
+                     const void* P_cols, void* out, float* lse, int dtype,
+                     int B, int T, int Hq, int Hkv, int D, int d_r,
+                     float alpha, int rel_extent, int window, int log_scale,
+                     void* stream);
+
+/*
+ * Decode plan: a pure function of the shape.  Writes the number of KV splits
+ * the decode call will use (num_splits_req > 0 forces that many, clamped to
+ * the number of visible keys; 0 lets the library choose from B*Hkv, the
+ * visible length min(L, window) and the GPU size) and the workspace size in
+ * bytes the caller must provide for it.
+ */
+int rel_attn_decode_plan(int B, int L, int Hq, int Hkv, int D, int num_splits_req, int window,
+                         int* num_splits_out, size_t* workspace_bytes_out);
+
+/*
+ * Decode: one query token per sequence, at position L-1 of its KV cache
+ * (the cache already holds that token's own k and v).
+ *   q [B, Hq, D]   k, v [B, L, Hkv, D]   r [B, Hq, d_r]   P_cols [E, d_r]
+ *   out [B, Hq, D] (dtype)   lse [B, Hq] float32 or NULL
+ * num_splits and workspace come from rel_attn_decode_plan with the same shape
+ * (workspace: device memory, 256-byte aligned, at least workspace_bytes; its
+ * contents on entry are ignored and on return are unspecified).  The KV range
+ * is split into num_splits chunks; each chunk's partial softmax state is
+ * merged by log-sum-exp in a second kernel on the same stream.
+ */
+int rel_attn_decode(const void* q, const void* k, const void* v, const void* r,
+                    const void* P_cols, void* out, float* lse, int dtype,
+                    int B, int L, int Hq, int Hkv, int D, int d_r,
+                    float alpha, int rel_extent, int window, int log_scale,
+                    int num_splits, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Dense relative logits (eq. for rel_logits in the same section):
+ *   out[t, h, d] = s * sum_c r[t, h, c] * P_cols[d, c]   for every d < rel_extent
+ *   r [n_tok, H, d_r] (dtype)   P_cols [E, d_r] (dtype)   out [n_tok, H, E] float32
+ * s = max(1, ln(seq_len)/ln(4096)) when log_scale, else 1.  No masking.
+ */
+int rel_logits(const void* r, const void* P_cols, float* out, int dtype,
+               long long n_tok, int H, int d_r, int rel_extent, int log_scale,
+               long long seq_len, void* stream);
+
+/* The log-scale factor s the library applies for a sequence of seq_len tokens. */
+double rel_attn_scale_factor(int log_scale, long long seq_len);
+
+/* Message for the calling thread's last non-zero return ("" if none). */
+const char* rel_attn_last_error(void);
+
+/* Library version, major*10000 + minor*100 + patch. */
+int rel_attn_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* RELATTN_H */

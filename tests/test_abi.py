@@ -1,0 +1,200 @@
+"""C-ABI checks that need no GPU: the library loads, exports every function
+include/relattn.h declares, rejects bad arguments on the host before any HIP
+call, plans decode splits as a pure function of the shape, and applies the
+log-scale reading."""
+
+import ctypes
+import os
+import re
+import threading
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "relattn.h")
+
+RA_OK, RA_ERR_INVALID_ARG, RA_ERR_UNSUPPORTED, RA_ERR_WORKSPACE = 0, -1, -2, -3
+RA_BF16, RA_F32 = 1, 2
+FAKE = 0x10000  # 16-byte aligned, never dereferenced: every call below fails validation first
+
+
+@pytest.fixture(scope="session")
+def lib():
+    from transformer_attention_query_amd import binding
+    if not os.path.exists(binding.library_path()):
+        from transformer_attention_query_amd import build
+        build.build(verbose=False)
+    return binding.load_library()
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(\w+)\s*\(", text, flags=re.M)))
+
+
+def test_header_declares_the_boundary():
+    names = _declared_functions()
+    for n in ("rel_attn_prefill", "rel_attn_decode", "rel_attn_decode_plan", "rel_logits",
+              "rel_attn_last_error", "rel_attn_version", "rel_attn_scale_factor"):
+        assert n in names
+
+
+def test_every_declared_symbol_is_exported(lib):
+    for n in _declared_functions():
+        assert hasattr(lib, n), f"{n} declared in relattn.h but not exported"
+
+
+def test_version(lib):
+    assert lib.rel_attn_version() >= 100
+
+
+def _prefill(lib, **kw):
+    a = dict(q=FAKE, k=FAKE + 16, v=FAKE + 32, r=FAKE + 48, P=FAKE + 64, out=FAKE + 80, lse=None,
+             dtype=RA_BF16, B=1, T=16, Hq=4, Hkv=2, D=128, d_r=32, alpha=0.1, E=8, W=0, ls=0)
+    a.update(kw)
+    return lib.rel_attn_prefill(a["q"], a["k"], a["v"], a["r"], a["P"], a["out"], a["lse"], a["dtype"],
+                                a["B"], a["T"], a["Hq"], a["Hkv"], a["D"], a["d_r"], a["alpha"], a["E"],
+                                a["W"], a["ls"], None)
+
+
+def _err(lib):
+    return lib.rel_attn_last_error().decode()
+
+
+@pytest.mark.parametrize("kw,code,frag", [
+    (dict(dtype=7), RA_ERR_INVALID_ARG, "dtype"),
+    (dict(B=-1), RA_ERR_INVALID_ARG, "B ="),
+    (dict(T=-3), RA_ERR_INVALID_ARG, "T ="),
+    (dict(Hq=6, Hkv=4), RA_ERR_INVALID_ARG, "multiple"),
+    (dict(Hkv=0), RA_ERR_INVALID_ARG, "positive"),
+    (dict(E=-1), RA_ERR_INVALID_ARG, "rel_extent"),
+    (dict(W=-2), RA_ERR_INVALID_ARG, "window"),
+    (dict(ls=2), RA_ERR_INVALID_ARG, "log_scale"),
+    (dict(alpha=float("nan")), RA_ERR_INVALID_ARG, "alpha"),
+    (dict(D=64), RA_ERR_UNSUPPORTED, "head dim"),
+    (dict(d_r=24), RA_ERR_UNSUPPORTED, "d_r"),
+    (dict(d_r=256), RA_ERR_UNSUPPORTED, "d_r"),
+    (dict(q=None), RA_ERR_INVALID_ARG, "q is NULL"),
+    (dict(out=None), RA_ERR_INVALID_ARG, "out is NULL"),
+    (dict(r=None), RA_ERR_INVALID_ARG, "r is NULL"),
+    (dict(P=None), RA_ERR_INVALID_ARG, "P_cols is NULL"),
+    (dict(k=FAKE + 2), RA_ERR_INVALID_ARG, "aligned"),
+    (dict(lse=FAKE + 4), RA_ERR_INVALID_ARG, "aligned"),
+    (dict(out=FAKE), RA_ERR_INVALID_ARG, "alias"),
+])
+def test_prefill_rejects_bad_arguments(lib, kw, code, frag):
+    assert _prefill(lib, **kw) == code
+    assert frag in _err(lib)
+
+
+def test_prefill_empty_is_a_noop(lib):
+    assert _prefill(lib, B=0) == RA_OK
+    assert _prefill(lib, T=0) == RA_OK
+    assert _err(lib) == ""
+
+
+def test_prefill_without_bias_needs_no_r_or_P(lib):
+    # E = 0: r and P may be NULL and d_r is not checked; T = 0 keeps it off the GPU
+    assert _prefill(lib, E=0, r=None, P=None, d_r=0, T=0) == RA_OK
+
+
+def _plan(lib, B, L, Hq, Hkv, req=0, W=0, D=128):
+    ns = ctypes.c_int(-1)
+    ws = ctypes.c_size_t(0)
+    rc = lib.rel_attn_decode_plan(B, L, Hq, Hkv, D, req, W, ctypes.byref(ns), ctypes.byref(ws))
+    return rc, ns.value, ws.value
+
+
+def test_decode_plan_is_pure_and_sized():
+    from transformer_attention_query_amd import binding
+    lib = binding.load_library()
+    for (B, L, Hq, Hkv) in [(64, 8192, 16, 2), (1, 1 << 20, 16, 2), (3, 77, 8, 8), (1, 1, 4, 1)]:
+        a = _plan(lib, B, L, Hq, Hkv)
+        b = _plan(lib, B, L, Hq, Hkv)
+        assert a == b and a[0] == RA_OK
+        ns = a[1]
+        assert 1 <= ns <= (L + 31) // 32
+        assert a[2] == ns * B * Hq * (128 + 2) * 4
+    # forced split counts are honoured up to one 32-key step per split
+    for req in (1, 2, 3, 7, 64):
+        rc, ns, _ = _plan(lib, 2, 3000, 16, 2, req)
+        assert rc == RA_OK and ns <= req
+    rc, ns, _ = _plan(lib, 1, 40, 16, 2, 64)
+    assert ns == 2                      # 40 keys -> two 32-key steps at most
+    # a window limits the visible range
+    rc, ns, _ = _plan(lib, 1, 100000, 16, 2, 0, 64)
+    assert ns <= 2
+
+
+@pytest.mark.parametrize("args,code", [
+    ((1, 0, 16, 2), RA_ERR_INVALID_ARG),
+    ((-1, 10, 16, 2), RA_ERR_INVALID_ARG),
+    ((1, 10, 16, 3), RA_ERR_INVALID_ARG),
+])
+def test_decode_plan_rejects(lib, args, code):
+    assert _plan(lib, *args)[0] == code
+
+
+def test_decode_plan_rejects_other_head_dims(lib):
+    assert _plan(lib, 1, 10, 16, 2, D=64)[0] == RA_ERR_UNSUPPORTED
+
+
+def _decode(lib, **kw):
+    a = dict(q=FAKE, k=FAKE + 16, v=FAKE + 32, r=FAKE + 48, P=FAKE + 64, out=FAKE + 80, lse=None,
+             dtype=RA_BF16, B=2, L=300, Hq=16, Hkv=2, D=128, d_r=128, alpha=0.1, E=64, W=0, ls=0,
+             ns=0, ws=None, wsb=0)
+    a.update(kw)
+    return lib.rel_attn_decode(a["q"], a["k"], a["v"], a["r"], a["P"], a["out"], a["lse"], a["dtype"],
+                               a["B"], a["L"], a["Hq"], a["Hkv"], a["D"], a["d_r"], a["alpha"], a["E"],
+                               a["W"], a["ls"], a["ns"], a["ws"], a["wsb"], None)
+
+
+def test_decode_workspace_errors(lib):
+    assert _decode(lib) == RA_ERR_WORKSPACE and "NULL" in _err(lib)
+    assert _decode(lib, ws=FAKE + 512 + 16, wsb=1 << 30) == RA_ERR_WORKSPACE and "256-byte" in _err(lib)
+    _, ns, need = _plan(lib, 2, 300, 16, 2)
+    assert _decode(lib, ws=FAKE * 16, wsb=need - 1) == RA_ERR_WORKSPACE and "smaller" in _err(lib)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(L=0), RA_ERR_INVALID_ARG),
+    (dict(ns=-1), RA_ERR_INVALID_ARG),
+    (dict(dtype=0), RA_ERR_INVALID_ARG),
+    (dict(D=256), RA_ERR_UNSUPPORTED),
+    (dict(v=None), RA_ERR_INVALID_ARG),
+])
+def test_decode_rejects_bad_arguments(lib, kw, code):
+    assert _decode(lib, **kw) == code
+
+
+def test_rel_logits_rejects_bad_arguments(lib):
+    f = lib.rel_logits
+    assert f(FAKE, FAKE + 16, FAKE + 32, 3, 10, 2, 32, 64, 0, 10, None) == RA_ERR_INVALID_ARG
+    assert f(FAKE, FAKE + 16, FAKE + 32, RA_BF16, -1, 2, 32, 64, 0, 10, None) == RA_ERR_INVALID_ARG
+    assert f(FAKE, FAKE + 16, FAKE + 32, RA_BF16, 10, 2, 32, 0, 0, 10, None) == RA_ERR_INVALID_ARG
+    assert f(FAKE, FAKE + 16, FAKE + 32, RA_BF16, 10, 2, 40, 64, 0, 10, None) == RA_ERR_UNSUPPORTED
+    assert f(None, FAKE + 16, FAKE + 32, RA_BF16, 10, 2, 32, 64, 0, 10, None) == RA_ERR_INVALID_ARG
+    assert f(FAKE, FAKE + 16, FAKE + 32, RA_BF16, 0, 2, 32, 64, 0, 10, None) == RA_OK
+
+
+def test_last_error_is_per_thread(lib):
+    assert _prefill(lib, dtype=9) == RA_ERR_INVALID_ARG
+    seen = {}
+
+    def other():
+        seen["msg"] = lib.rel_attn_last_error().decode()
+
+    t = threading.Thread(target=other)
+    t.start()
+    t.join()
+    assert seen["msg"] == ""
+    assert "dtype" in _err(lib)
+
+
+def test_scale_factor_reading(lib):
+    f = lib.rel_attn_scale_factor
+    assert f(0, 1 << 20) == 1.0
+    assert f(1, 4096) == 1.0 and f(1, 100) == 1.0
+    assert abs(f(1, 32768) - 1.25) < 1e-15
+    assert abs(f(1, 1 << 20) - 5.0 / 3.0) < 1e-15

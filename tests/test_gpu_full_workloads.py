@@ -1,0 +1,54 @@
+"""GPU parity at the full sizes of the five named workloads, in the launch
+configuration bench.py times.  Where the oracle cannot finish the whole
+output quickly (the 8K sliding-window and 2x32K causal prefills) it checks
+sampled query rows, chosen to include every tile edge, the rel_extent and
+window edges and the last row; decode is compared in full."""
+
+import random
+
+import pytest
+import torch
+
+import oracle
+import transformer_attention_query_amd as ra
+from transformer_attention_query_amd import inputs as tinputs
+from parity import assert_close
+
+pytestmark = pytest.mark.gpu
+
+
+def _rows(T, extra, seed):
+    base = {0, 1, 31, 32, 63, 64, 127, 128, 129, 1023, 1024, 1025, 2047, 2048, T // 2, T - 2, T - 1}
+    rng = random.Random(seed)
+    base |= {rng.randrange(T) for _ in range(extra)}
+    return sorted(r for r in base if r < T)
+
+
+@pytest.mark.parametrize("name", ["tiny_fp32", "swa_prefill_8k", "full_prefill_32k_log"])
+def test_prefill_workload(name):
+    w = tinputs.WORKLOADS[name]
+    x = tinputs.make_inputs(w, seed=0)
+    xd = {n: t.cuda() for n, t in x.items()}
+    out, lse = ra.prefill(xd["q"], xd["k"], xd["v"], xd["r"], xd["P_cols"], w.alpha, w.E, w.W, w.log_scale)
+    torch.cuda.synchronize()
+    del xd
+    if w.T <= 256:
+        ref, lref = oracle.prefill(x["q"], x["k"], x["v"], x["r"], x["P"], w.alpha, w.E, w.W, w.log_scale)
+        assert_close(out, ref, x["q"].dtype, name, lse, lref)
+        return
+    rows = _rows(w.T, 24, 1)
+    ref, lref = oracle.prefill(x["q"], x["k"], x["v"], x["r"], x["P"], w.alpha, w.E, w.W, w.log_scale, rows=rows)
+    assert_close(out[:, rows], ref, x["q"].dtype, name, lse[:, :, rows], lref)
+
+
+@pytest.mark.parametrize("name", ["decode_64x8k", "decode_1x1m_log"])
+def test_decode_workload(name):
+    w = tinputs.WORKLOADS[name]
+    x = tinputs.make_inputs(w, seed=0)
+    xd = {n: t.cuda() for n, t in x.items()}
+    out, lse = ra.decode(xd["q"], xd["k"], xd["v"], xd["r"], xd["P_cols"], w.alpha, w.E, w.W, w.log_scale,
+                         num_splits=w.num_splits)
+    torch.cuda.synchronize()
+    del xd
+    ref, lref = oracle.decode(x["q"], x["k"], x["v"], x["r"], x["P"], w.alpha, w.E, w.W, w.log_scale)
+    assert_close(out, ref, x["q"].dtype, name, lse, lref)

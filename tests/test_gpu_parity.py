@@ -1,0 +1,184 @@
+"""GPU parity: the HIP path through the C ABI against the fp64 oracle, element
+by element, on seeded inputs spanning several tiles, ragged tails and the
+degenerate cases (T = 1, window 1, rel_extent 0 or beyond T, MHA, wide GQA)."""
+
+import zlib
+
+import pytest
+import torch
+
+import oracle
+import transformer_attention_query_amd as ra
+from transformer_attention_query_amd import inputs as tinputs
+from parity import TOL, assert_close, err_stats
+
+pytestmark = pytest.mark.gpu
+
+ALPHA = 1.0 / 128 ** 0.5
+
+
+def _cuda(x):
+    return {n: t.cuda() for n, t in x.items()}
+
+
+def _run_prefill(x, alpha, E, W, ls):
+    out, lse = ra.prefill(x["q"], x["k"], x["v"], x["r"], x["P_cols"], alpha, E, W, ls)
+    torch.cuda.synchronize()
+    return out, lse
+
+
+# name, dtype, B, T, Hq, Hkv, d_r, E, W, log_scale
+PREFILL_CASES = [
+    ("tiny_fp32_workload", "fp32", 1, 256, 4, 1, 32, 64, 0, False),
+    ("T1", "bf16", 1, 1, 8, 1, 32, 16, 0, False),
+    ("T17_mha", "bf16", 2, 17, 3, 3, 16, 5, 0, False),
+    ("T100_E1", "bf16", 1, 100, 4, 2, 64, 1, 0, False),
+    ("T255_W5", "bf16", 1, 255, 4, 1, 32, 40, 5, False),
+    ("T300_W1", "bf16", 1, 300, 2, 1, 48, 10, 1, False),
+    ("T1000_W100", "bf16", 2, 1000, 8, 1, 128, 300, 100, False),
+    ("T700_E0", "bf16", 1, 700, 4, 2, 32, 0, 0, False),
+    ("T600_E_beyond_T", "bf16", 1, 600, 4, 1, 128, 2000, 0, False),
+    ("T513_W200_E64", "bf16", 1, 513, 16, 2, 128, 64, 200, False),
+    ("T1100_E1024_W1024", "bf16", 1, 1100, 8, 1, 128, 1024, 1024, False),
+    ("fp32_T300_W70", "fp32", 1, 300, 4, 2, 64, 100, 70, False),
+    ("fp32_T129", "fp32", 2, 129, 2, 1, 16, 7, 0, False),
+]
+
+
+@pytest.mark.parametrize("case", PREFILL_CASES, ids=[c[0] for c in PREFILL_CASES])
+def test_prefill_matches_oracle(case):
+    name, dt, B, T, Hq, Hkv, d_r, E, W, ls = case
+    x = tinputs.make_prefill_inputs(B, T, Hq, Hkv, 128, d_r, max(E, 1), dt, seed=zlib.crc32(name.encode()) % 1000)
+    if E == 0:
+        x["P_cols"] = x["P_cols"][:0]
+    xd = _cuda(x)
+    out, lse = _run_prefill(xd, ALPHA, E, W, ls)
+    ref, lref = oracle.prefill(x["q"], x["k"], x["v"], x["r"], x["P"], ALPHA, E, W, ls)
+    assert_close(out, ref, x["q"].dtype, name, lse, lref)
+
+
+@pytest.mark.parametrize("W", [0, 300])
+@pytest.mark.parametrize("variant", ["P_x50", "alpha_0"])
+def test_prefill_bias_sensitivity(variant, W):
+    """Large-bias variants where a shear or rel_extent slip changes the output by O(1)."""
+    T, E = 777, 200
+    x = tinputs.make_prefill_inputs(1, T, 8, 2, 128, 64, E, "bf16", seed=5)
+    alpha = ALPHA
+    if variant == "P_x50":
+        x["P"] = (x["P"].float() * 50).to(torch.bfloat16)
+        x["P_cols"] = x["P"].t().contiguous()
+    else:
+        alpha = 0.0
+        x["P"] = (x["P"].float() * 25).to(torch.bfloat16)
+        x["P_cols"] = x["P"].t().contiguous()
+    out, lse = _run_prefill(_cuda(x), alpha, E, W, False)
+    ref, lref = oracle.prefill(x["q"], x["k"], x["v"], x["r"], x["P"], alpha, E, W)
+    assert_close(out, ref, torch.bfloat16, variant, lse, lref)
+
+
+def test_prefill_log_scale_sampled_rows():
+    T, E = 5000, 300
+    x = tinputs.make_prefill_inputs(1, T, 4, 1, 128, 64, E, "bf16", seed=11)
+    out, lse = _run_prefill(_cuda(x), ALPHA, E, 0, True)
+    rows = [0, 1, 299, 300, 301, 2047, 4095, 4096, 4999]
+    ref, lref = oracle.prefill(x["q"], x["k"], x["v"], x["r"], x["P"], ALPHA, E, 0, True, rows=rows)
+    assert_close(out[:, rows], ref, torch.bfloat16, "log-scale", lse[:, :, rows], lref)
+
+
+def test_prefill_weights_via_identity_v():
+    """V = identity makes each output row the attention-weight row: masked
+    weights are exactly zero and each row sums to one."""
+    T = 100
+    x = tinputs.make_prefill_inputs(1, T, 2, 1, 128, 32, 30, "bf16", seed=2)
+    eye = torch.zeros(1, T, 1, 128, dtype=torch.bfloat16)
+    eye[0, :, 0, :T] = torch.eye(T, dtype=torch.bfloat16)
+    x["v"] = eye
+    W = 17
+    out, _ = _run_prefill(_cuda(x), ALPHA, 30, W, False)
+    o = out.float().cpu()[0]                     # [T, H, 128]
+    i = torch.arange(T)[:, None]
+    j = torch.arange(128)[None, :]
+    masked = (j > i) | (i - j >= W)
+    assert torch.all(o[masked[:, None, :].expand(-1, 2, -1)] == 0)
+    assert torch.allclose(o.sum(-1), torch.ones(T, 2), atol=2e-2)
+    w = oracle.attention_weights(x["q"], x["k"], x["r"], x["P"], ALPHA, 30, W)[0]   # [H, T, T]
+    assert_close(o[:, :, :T].permute(1, 0, 2), w, torch.bfloat16, "weights")
+
+
+def test_prefill_is_deterministic():
+    x = _cuda(tinputs.make_prefill_inputs(1, 1500, 8, 1, 128, 128, 512, "bf16", seed=3))
+    a, la = _run_prefill(x, ALPHA, 512, 0, False)
+    b, lb = _run_prefill(x, ALPHA, 512, 0, False)
+    assert torch.equal(a.view(torch.int16), b.view(torch.int16)) and torch.equal(la, lb)
+
+
+# ---------------------------------------------------------------- decode
+
+# name, dtype, B, L, Hq, Hkv, d_r, E, W, log_scale, num_splits
+DECODE_CASES = [
+    ("L1", "bf16", 2, 1, 16, 2, 128, 64, 0, False, 0),
+    ("L33_mha", "bf16", 3, 33, 4, 4, 32, 10, 0, False, 0),
+    ("L1000_W100", "bf16", 2, 1000, 16, 2, 128, 300, 100, False, 0),
+    ("L5000_log_s7", "bf16", 1, 5000, 8, 1, 64, 1024, 0, True, 7),
+    ("G32_s3", "bf16", 1, 700, 32, 1, 16, 50, 0, False, 3),
+    ("E0", "bf16", 2, 400, 16, 2, 128, 0, 0, False, 0),
+    ("E_beyond_L", "bf16", 1, 300, 16, 2, 128, 1024, 0, False, 2),
+    ("fp32", "fp32", 2, 513, 8, 2, 32, 64, 0, False, 0),
+    ("fp32_W50_s5", "fp32", 1, 777, 4, 1, 48, 100, 50, False, 5),
+]
+
+
+@pytest.mark.parametrize("case", DECODE_CASES, ids=[c[0] for c in DECODE_CASES])
+def test_decode_matches_oracle(case):
+    name, dt, B, L, Hq, Hkv, d_r, E, W, ls, ns = case
+    x = tinputs.make_decode_inputs(B, L, Hq, Hkv, 128, d_r, max(E, 1), dt, seed=zlib.crc32(name.encode()) % 1000)
+    if E == 0:
+        x["P_cols"] = x["P_cols"][:0]
+    xd = _cuda(x)
+    out, lse = ra.decode(xd["q"], xd["k"], xd["v"], xd["r"], xd["P_cols"], ALPHA, E, W, ls, num_splits=ns)
+    torch.cuda.synchronize()
+    ref, lref = oracle.decode(x["q"], x["k"], x["v"], x["r"], x["P"], ALPHA, E, W, ls)
+    assert_close(out, ref, x["q"].dtype, name, lse, lref)
+
+
+def test_decode_split_invariance():
+    x = _cuda(tinputs.make_decode_inputs(2, 3000, 16, 2, 128, 128, 1024, "fp32", seed=4))
+    outs = []
+    for ns in (1, 2, 3, 7, 64, 0):
+        o, l = ra.decode(x["q"], x["k"], x["v"], x["r"], x["P_cols"], ALPHA, 1024, 0, False, num_splits=ns)
+        outs.append((o.cpu(), l.cpu()))
+    torch.cuda.synchronize()
+    o0, l0 = outs[0]
+    for o, l in outs[1:]:
+        assert err_stats(o, o0)[0] <= 1e-5 and err_stats(l, l0)[0] <= 1e-5
+
+
+@pytest.mark.parametrize("ls,W", [(False, 0), (True, 0), (False, 64)])
+def test_decode_equals_last_prefill_row(ls, W):
+    L = 4500 if ls else 1300
+    x = tinputs.make_prefill_inputs(1, L, 8, 2, 128, 64, 256, "fp32", seed=6)
+    xd = _cuda(x)
+    pre, lpre = _run_prefill(xd, ALPHA, 256, W, ls)
+    dec, ldec = ra.decode(xd["q"][:, L - 1].contiguous(), xd["k"], xd["v"], xd["r"][:, L - 1].contiguous(),
+                          xd["P_cols"], ALPHA, 256, W, ls)
+    torch.cuda.synchronize()
+    assert err_stats(dec, pre[:, L - 1])[0] <= 1e-4
+    assert err_stats(ldec, lpre[:, :, L - 1])[0] <= 2e-5
+
+
+# ---------------------------------------------------------------- rel_logits
+
+@pytest.mark.parametrize("dt,n,H,d_r,E,ls,seq", [
+    ("bf16", 300, 4, 128, 1000, False, 0),
+    ("bf16", 77, 16, 32, 33, True, 32768),
+    ("fp32", 129, 2, 48, 130, False, 0),
+])
+def test_rel_logits_matches_oracle(dt, n, H, d_r, E, ls, seq):
+    x = tinputs.make_prefill_inputs(1, n, H, 1, 128, d_r, E, dt, seed=n)
+    r = x["r"][0]                                     # [n, H, d_r]
+    got = ra.rel_logits(r.cuda(), x["P_cols"].cuda(), ls, seq)
+    torch.cuda.synchronize()
+    s = oracle.scale_factor(seq if seq else n, ls)
+    ref = oracle.rel_logits(r, x["P"], s)
+    bound = 4 * d_r * 2.0 ** -24 * s * (r.double().abs() @ x["P"].double().abs()) + 1e-30
+    assert torch.all((got.double().cpu() - ref).abs() <= bound)

@@ -1,0 +1,185 @@
+// Host side of the C ABI declared in include/relattn.h: argument checks (all
+// before any HIP call), the log-scale factor, decode planning, launches and
+// per-thread error messages.  No device memory is allocated here and no
+// device data is read on the host.
+#include "relattn.h"
+
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdint>
+#include <cstdio>
+
+#include "relattn_internal.hpp"
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+int fail(int code, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+  return code;
+}
+
+int ok() {
+  g_err[0] = '\0';
+  return RA_OK;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+int check_ptr(const void* p, const char* name, bool required) {
+  if (p == nullptr) {
+    if (required) return fail(RA_ERR_INVALID_ARG, "%s is NULL", name);
+    return RA_OK;
+  }
+  if (!aligned16(p)) return fail(RA_ERR_INVALID_ARG, "%s is not 16-byte aligned", name);
+  return RA_OK;
+}
+
+double scale_of(int log_scale, long long len) {
+  if (!log_scale || len <= 1) return 1.0;
+  const double s = std::log((double)len) / std::log(4096.0);
+  return s > 1.0 ? s : 1.0;
+}
+
+// Checks common to prefill and decode.
+int check_common(int dtype, int B, int Tl, int Hq, int Hkv, int D, int d_r, float alpha, int rel_extent,
+                 int window, int log_scale, const char* len_name) {
+  if (dtype != RA_BF16 && dtype != RA_F32) return fail(RA_ERR_INVALID_ARG, "dtype %d is not RA_BF16 or RA_F32", dtype);
+  if (B < 0) return fail(RA_ERR_INVALID_ARG, "B = %d < 0", B);
+  if (Tl < 0) return fail(RA_ERR_INVALID_ARG, "%s = %d < 0", len_name, Tl);
+  if (Hq <= 0 || Hkv <= 0) return fail(RA_ERR_INVALID_ARG, "Hq = %d and Hkv = %d must be positive", Hq, Hkv);
+  if (Hq % Hkv != 0) return fail(RA_ERR_INVALID_ARG, "Hq = %d is not a multiple of Hkv = %d", Hq, Hkv);
+  if (rel_extent < 0) return fail(RA_ERR_INVALID_ARG, "rel_extent = %d < 0", rel_extent);
+  if (window < 0) return fail(RA_ERR_INVALID_ARG, "window = %d < 0", window);
+  if (log_scale != 0 && log_scale != 1) return fail(RA_ERR_INVALID_ARG, "log_scale = %d is not 0 or 1", log_scale);
+  if (!std::isfinite(alpha)) return fail(RA_ERR_INVALID_ARG, "alpha is not finite");
+  if (D != relattn::kHeadDim) return fail(RA_ERR_UNSUPPORTED, "head dim D = %d: only 128 is supported", D);
+  if (rel_extent > 0) {
+    if (d_r <= 0 || d_r % 16 != 0 || d_r > relattn::kMaxDr)
+      return fail(RA_ERR_UNSUPPORTED, "d_r = %d: supported values are multiples of 16 in [16, 128]", d_r);
+  }
+  return RA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* rel_attn_last_error(void) { return g_err; }
+
+int rel_attn_version(void) { return 100; }  // 0.1.0
+
+double rel_attn_scale_factor(int log_scale, long long seq_len) { return scale_of(log_scale, seq_len); }
+
+int rel_attn_prefill(const void* q, const void* k, const void* v, const void* r, const void* P_cols, void* out,
+                     float* lse, int dtype, int B, int T, int Hq, int Hkv, int D, int d_r, float alpha,
+                     int rel_extent, int window, int log_scale, void* stream) {
+  int rc = check_common(dtype, B, T, Hq, Hkv, D, d_r, alpha, rel_extent, window, log_scale, "T");
+  if (rc) return rc;
+  if ((rc = check_ptr(q, "q", true)) || (rc = check_ptr(k, "k", true)) || (rc = check_ptr(v, "v", true)) ||
+      (rc = check_ptr(out, "out", true)) || (rc = check_ptr(lse, "lse", false)) ||
+      (rc = check_ptr(r, "r", rel_extent > 0)) || (rc = check_ptr(P_cols, "P_cols", rel_extent > 0)))
+    return rc;
+  if (out == q || out == k || out == v || out == r) return fail(RA_ERR_INVALID_ARG, "out aliases an input");
+  if ((long long)T * Hq > 0x7fffffffLL / relattn::kHeadDim)
+    return fail(RA_ERR_UNSUPPORTED, "T * Hq = %lld too large for one launch", (long long)T * Hq);
+  if (B == 0 || T == 0) return ok();
+
+  const double s = scale_of(log_scale, T);
+  relattn::PrefillArgs a;
+  a.q = q; a.k = k; a.v = v; a.r = r; a.pc = P_cols; a.out = out; a.lse = lse;
+  a.B = B; a.T = T; a.Hq = Hq; a.Hkv = Hkv; a.d_r = rel_extent > 0 ? d_r : 16; a.E = rel_extent; a.W = window;
+  a.c1 = (float)(s * (double)alpha * 1.4426950408889634);
+  a.c2 = (float)(s * 1.4426950408889634);
+  hipError_t e = relattn::launch_prefill(dtype, a, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(RA_ERR_HIP, "prefill launch failed: %s", hipGetErrorString(e));
+  return ok();
+}
+
+int rel_attn_decode_plan(int B, int L, int Hq, int Hkv, int D, int num_splits_req, int window,
+                         int* num_splits_out, size_t* workspace_bytes_out) {
+  if (num_splits_out == nullptr || workspace_bytes_out == nullptr)
+    return fail(RA_ERR_INVALID_ARG, "num_splits_out and workspace_bytes_out must not be NULL");
+  if (B < 0) return fail(RA_ERR_INVALID_ARG, "B = %d < 0", B);
+  if (L <= 0) return fail(RA_ERR_INVALID_ARG, "L = %d: the cache must hold at least the query's own token", L);
+  if (Hq <= 0 || Hkv <= 0 || Hq % Hkv != 0)
+    return fail(RA_ERR_INVALID_ARG, "Hq = %d, Hkv = %d: need positive Hq multiple of Hkv", Hq, Hkv);
+  if (window < 0) return fail(RA_ERR_INVALID_ARG, "window = %d < 0", window);
+  if (num_splits_req < 0) return fail(RA_ERR_INVALID_ARG, "num_splits = %d < 0", num_splits_req);
+  if (D != relattn::kHeadDim) return fail(RA_ERR_UNSUPPORTED, "head dim D = %d: only 128 is supported", D);
+  relattn::DecodePlan pl = relattn::plan_decode(B, L, Hq, Hkv, num_splits_req, window);
+  *num_splits_out = pl.n_split;
+  *workspace_bytes_out = pl.ws_bytes;
+  return ok();
+}
+
+int rel_attn_decode(const void* q, const void* k, const void* v, const void* r, const void* P_cols, void* out,
+                    float* lse, int dtype, int B, int L, int Hq, int Hkv, int D, int d_r, float alpha,
+                    int rel_extent, int window, int log_scale, int num_splits, void* workspace,
+                    size_t workspace_bytes, void* stream) {
+  int rc = check_common(dtype, B, L, Hq, Hkv, D, d_r, alpha, rel_extent, window, log_scale, "L");
+  if (rc) return rc;
+  if (L == 0) return fail(RA_ERR_INVALID_ARG, "L = 0: the cache must hold at least the query's own token");
+  if ((rc = check_ptr(q, "q", true)) || (rc = check_ptr(k, "k", true)) || (rc = check_ptr(v, "v", true)) ||
+      (rc = check_ptr(out, "out", true)) || (rc = check_ptr(lse, "lse", false)) ||
+      (rc = check_ptr(r, "r", rel_extent > 0)) || (rc = check_ptr(P_cols, "P_cols", rel_extent > 0)))
+    return rc;
+  if (out == q || out == k || out == v || out == r) return fail(RA_ERR_INVALID_ARG, "out aliases an input");
+  if (num_splits < 0) return fail(RA_ERR_INVALID_ARG, "num_splits = %d < 0", num_splits);
+  relattn::DecodePlan pl = relattn::plan_decode(B, L, Hq, Hkv, num_splits, window);
+  if (B == 0) return ok();
+  if (workspace == nullptr) return fail(RA_ERR_WORKSPACE, "workspace is NULL (need %zu bytes)", pl.ws_bytes);
+  if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0)
+    return fail(RA_ERR_WORKSPACE, "workspace is not 256-byte aligned");
+  if (workspace_bytes < pl.ws_bytes)
+    return fail(RA_ERR_WORKSPACE, "workspace of %zu bytes is smaller than the %zu the plan needs", workspace_bytes,
+                pl.ws_bytes);
+  if ((long long)B * L > 0x7fffffffLL)
+    return fail(RA_ERR_UNSUPPORTED, "B * L = %lld too large", (long long)B * L);
+
+  const double s = scale_of(log_scale, L);
+  relattn::DecodeArgs a;
+  a.q = q; a.k = k; a.v = v; a.r = r; a.pc = P_cols; a.out = out; a.lse = lse;
+  a.ws = static_cast<float*>(workspace);
+  a.B = B; a.L = L; a.Hq = Hq; a.Hkv = Hkv; a.d_r = rel_extent > 0 ? d_r : 16; a.E = rel_extent; a.W = window;
+  a.c1 = (float)(s * (double)alpha * 1.4426950408889634);
+  a.c2 = (float)(s * 1.4426950408889634);
+  a.n_split = pl.n_split;
+  a.chunk = pl.chunk;
+  a.kv_lo = pl.kv_lo;
+  a.n_hg = pl.n_hg;
+  hipError_t e = relattn::launch_decode(dtype, a, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(RA_ERR_HIP, "decode launch failed: %s", hipGetErrorString(e));
+  return ok();
+}
+
+int rel_logits(const void* r, const void* P_cols, float* out, int dtype, long long n_tok, int H, int d_r,
+               int rel_extent, int log_scale, long long seq_len, void* stream) {
+  if (dtype != RA_BF16 && dtype != RA_F32) return fail(RA_ERR_INVALID_ARG, "dtype %d is not RA_BF16 or RA_F32", dtype);
+  if (n_tok < 0 || H <= 0) return fail(RA_ERR_INVALID_ARG, "n_tok = %lld, H = %d", n_tok, H);
+  if (rel_extent <= 0) return fail(RA_ERR_INVALID_ARG, "rel_extent = %d must be positive", rel_extent);
+  if (log_scale != 0 && log_scale != 1) return fail(RA_ERR_INVALID_ARG, "log_scale = %d is not 0 or 1", log_scale);
+  if (d_r <= 0 || d_r % 16 != 0 || d_r > relattn::kMaxDr)
+    return fail(RA_ERR_UNSUPPORTED, "d_r = %d: supported values are multiples of 16 in [16, 128]", d_r);
+  int rc;
+  if ((rc = check_ptr(r, "r", true)) || (rc = check_ptr(P_cols, "P_cols", true)) || (rc = check_ptr(out, "out", true)))
+    return rc;
+  if (rel_extent > 65535 * 128) return fail(RA_ERR_UNSUPPORTED, "rel_extent = %d too large", rel_extent);
+  if (n_tok == 0) return ok();
+  relattn::RelLogitsArgs a;
+  a.r = r; a.pc = P_cols; a.out = out;
+  a.n_rows = n_tok * H;
+  a.d_r = d_r; a.E = rel_extent;
+  a.s = (float)scale_of(log_scale, seq_len);
+  hipError_t e = relattn::launch_rel_logits(dtype, a, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(RA_ERR_HIP, "rel_logits launch failed: %s", hipGetErrorString(e));
+  return ok();
+}
+
+}  // extern "C"

@@ -1,0 +1,78 @@
+// Dense relative logits for gfx950 (page "SGLang and Miles Add Day-0 Support
+// for Inkling", section "Attention with Relative Positional Embedding", eq.
+// for rel_logits; the SGLang section "Relative Logits Optimization" runs this
+// projection as its own step on a second stream):
+//   out[row, d] = s * sum_c r[row, c] * P_cols[d, c],   row = (token, head)
+// A plain MFMA GEMM [n_rows x d_r] x [d_r x E] with fp32 output.  Both
+// operands are contiguous along the contraction, so lanes load their
+// 16-byte MFMA fragments straight from global memory (P_cols is small and
+// stays in L2); the fp32 output dominates the traffic.
+#include "device_common.hpp"
+#include "relattn_internal.hpp"
+
+namespace relattn {
+namespace {
+
+constexpr int kRlWaves = 4;
+constexpr int kRlRows = 32 * kRlWaves;  // rows per workgroup
+constexpr int kRlCols = 128;            // distances per workgroup
+
+template <typename T>
+__global__ __launch_bounds__(kRlWaves * 64) void rel_logits_kernel(RelLogitsArgs p) {
+  const int tid = threadIdx.x;
+  const int w = tid >> 6;
+  const int lane = tid & 63;
+  const int h2 = lane >> 5;
+  const int a = lane & 31;
+  const int d_r = p.d_r, E = p.E;
+  const int nk = d_r / 16;
+
+  const long long row0 = (long long)blockIdx.x * kRlRows + 32 * w;
+  const int col0 = blockIdx.y * kRlCols;
+  const T* rg = static_cast<const T*>(p.r);
+  const T* pcg = static_cast<const T*>(p.pc);
+
+  const long long arow = row0 + a;
+  const bool aok = arow < p.n_rows;
+  v8_t<T> areg[kMaxDr / 16];
+#pragma unroll
+  for (int kk = 0; kk < kMaxDr / 16; ++kk)
+    areg[kk] = ld8_or_zero<T>(rg + (aok ? arow : 0) * d_r + kk * 16 + 8 * h2, aok && kk < nk);
+
+#pragma unroll
+  for (int cb = 0; cb < kRlCols / 32; ++cb) {
+    const int col = col0 + cb * 32 + a;
+    const bool bok = col < E;
+    const T* prow = pcg + size_t(bok ? col : 0) * d_r + 8 * h2;
+    f32x16 acc = zero16();
+#pragma unroll
+    for (int kk = 0; kk < kMaxDr / 16; ++kk)
+      if (kk < nk) mma32(areg[kk], ld8_or_zero<T>(prow + kk * 16, bok), acc);
+    // accumulator v of lane (h2, a): row 8*(v/4) + 4*h2 + v%4, column a
+    if (bok) {
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const long long row = row0 + 8 * (v >> 2) + 4 * h2 + (v & 3);
+        if (row < p.n_rows) p.out[row * E + col] = acc[v] * p.s;
+      }
+    }
+  }
+}
+
+template <typename T>
+hipError_t launch_rel_logits_t(const RelLogitsArgs& a, hipStream_t stream) {
+  const long long gx = (a.n_rows + kRlRows - 1) / kRlRows;
+  const int gy = (a.E + kRlCols - 1) / kRlCols;
+  if (gx > 0x7fffffffLL || gy > 65535) return hipErrorInvalidConfiguration;
+  hipLaunchKernelGGL(rel_logits_kernel<T>, dim3((unsigned)gx, (unsigned)gy), dim3(kRlWaves * 64), 0, stream, a);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_rel_logits(int dtype, const RelLogitsArgs& a, hipStream_t stream) {
+  if (dtype == 1) return launch_rel_logits_t<__bf16>(a, stream);
+  return launch_rel_logits_t<float>(a, stream);
+}
+
+}  // namespace relattn

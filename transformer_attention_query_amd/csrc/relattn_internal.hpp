@@ -1,0 +1,71 @@
+// Internal declarations shared by the host API (api.cpp) and the HIP kernel
+// sources.  Not part of the public ABI (that is include/relattn.h).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace relattn {
+
+constexpr int kHeadDim = 128;
+constexpr int kMaxDr = 128;
+
+// Prefill launch description.  Pointers are device pointers; c1 and c2 fold
+// the log-scale s, alpha and log2(e) so the kernels work in base 2:
+//   c1 = s * alpha * log2(e)   multiplies q.k
+//   c2 = s * log2(e)           multiplies r.P
+struct PrefillArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  const void* r;
+  const void* pc;   // P_cols [E, d_r]
+  void* out;
+  float* lse;       // may be null
+  int B, T, Hq, Hkv, d_r, E, W;
+  float c1, c2;
+};
+
+struct DecodeArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  const void* r;
+  const void* pc;
+  void* out;
+  float* lse;       // may be null
+  float* ws;        // workspace base (float)
+  int B, L, Hq, Hkv, d_r, E, W;
+  float c1, c2;
+  int n_split;      // splits of the visible key range
+  int chunk;        // keys per split (multiple of 32)
+  int kv_lo;        // first visible key (L - W for a window, else 0)
+  int n_hg;         // groups of 16 query heads per kv head
+};
+
+struct RelLogitsArgs {
+  const void* r;
+  const void* pc;
+  float* out;
+  long long n_rows;  // n_tok * H
+  int d_r, E;
+  float s;
+};
+
+// Decode planning shared by rel_attn_decode_plan and rel_attn_decode.
+struct DecodePlan {
+  int n_split;
+  int chunk;
+  int kv_lo;
+  int n_hg;
+  size_t ws_bytes;
+};
+DecodePlan plan_decode(int B, int L, int Hq, int Hkv, int num_splits_req, int window);
+
+// Launchers: return hipSuccess or the launch error.  dtype: 1 = bf16, 2 = fp32.
+hipError_t launch_prefill(int dtype, const PrefillArgs& a, hipStream_t stream);
+hipError_t launch_decode(int dtype, const DecodeArgs& a, hipStream_t stream);
+hipError_t launch_rel_logits(int dtype, const RelLogitsArgs& a, hipStream_t stream);
+
+}  // namespace relattn
