@@ -137,7 +137,7 @@ def bench_decode(steps: int, warmup: int):
     # MALL and the L2s.
     k2 = [x["k"], x["k"].clone()]
     v2 = [x["v"], x["v"].clone()]
-    ns, ws_bytes = ra.decode_plan(w.B, w.T, w.Hq, w.Hkv, w.D, w.num_splits, w.W)
+    ns, ws_bytes = ra.decode_plan(w.B, w.T, w.Hq, w.Hkv, w.D, w.num_splits, w.W, w.E)
     ws = torch.empty(ws_bytes, dtype=torch.uint8, device="cuda")
     stream = torch.cuda.current_stream()
 

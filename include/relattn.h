@@ -78,13 +78,15 @@ int rel_attn_prefill(const void* q, const void* k, const void* v, const void* r,
 
 /*
  * Decode plan: a pure function of the shape.  Writes the number of KV splits
- * the decode call will use (num_splits_req > 0 forces that many, clamped to
- * the number of visible keys; 0 lets the library choose from B*Hkv, the
- * visible length min(L, window) and the GPU size) and the workspace size in
- * bytes the caller must provide for it.
+ * the decode call will use (num_splits_req > 0 asks for that many; the plan
+ * may use fewer so that every split holds at least one 32-key step; 0 lets
+ * the library choose from B*Hkv, the visible length min(L, window) and the GPU
+ * size) and the workspace size in bytes the caller must provide: the split
+ * partials plus one row of relative logits per (sequence, query head),
+ * padded (all zeros when rel_extent == 0).
  */
 int rel_attn_decode_plan(int B, int L, int Hq, int Hkv, int D, int num_splits_req, int window,
-                         int* num_splits_out, size_t* workspace_bytes_out);
+                         int rel_extent, int* num_splits_out, size_t* workspace_bytes_out);
 
 /*
  * Decode: one query token per sequence, at position L-1 of its KV cache
@@ -95,7 +97,10 @@ int rel_attn_decode_plan(int B, int L, int Hq, int Hkv, int D, int num_splits_re
  * (workspace: device memory, 256-byte aligned, at least workspace_bytes; its
  * contents on entry are ignored and on return are unspecified).  The KV range
  * is split into num_splits chunks; each chunk's partial softmax state is
- * merged by log-sum-exp in a second kernel on the same stream.
+ * merged by log-sum-exp in a last kernel on the same stream.  A first
+ * kernel writes each (sequence, head)'s relative-logit row s * r.P[:, d] into
+ * the workspace (zeros when rel_extent == 0); the split kernel adds it by
+ * distance.
  */
 int rel_attn_decode(const void* q, const void* k, const void* v, const void* r,
                     const void* P_cols, void* out, float* lse, int dtype,

@@ -99,10 +99,10 @@ def test_prefill_without_bias_needs_no_r_or_P(lib):
     assert _prefill(lib, E=0, r=None, P=None, d_r=0, T=0) == RA_OK
 
 
-def _plan(lib, B, L, Hq, Hkv, req=0, W=0, D=128):
+def _plan(lib, B, L, Hq, Hkv, req=0, W=0, D=128, E=0):
     ns = ctypes.c_int(-1)
     ws = ctypes.c_size_t(0)
-    rc = lib.rel_attn_decode_plan(B, L, Hq, Hkv, D, req, W, ctypes.byref(ns), ctypes.byref(ws))
+    rc = lib.rel_attn_decode_plan(B, L, Hq, Hkv, D, req, W, E, ctypes.byref(ns), ctypes.byref(ws))
     return rc, ns.value, ws.value
 
 
@@ -115,13 +115,17 @@ def test_decode_plan_is_pure_and_sized():
         assert a == b and a[0] == RA_OK
         ns = a[1]
         assert 1 <= ns <= (L + 31) // 32
-        assert a[2] == ns * B * Hq * (128 + 2) * 4
+        partial = (ns * B * Hq * (128 + 2) * 4 + 255) // 256 * 256
+        assert a[2] >= partial + B * Hq * 32 * 4   # split partials + one (zero) bias row per head
+        # with a relative extent the workspace adds one bias row per (sequence, head)
+        rc, ns2, ws2 = _plan(lib, B, L, Hq, Hkv, E=1024)
+        assert rc == RA_OK and ns2 == ns and ws2 >= partial + B * Hq * 1024 * 4
     # forced split counts are honoured up to one 32-key step per split
     for req in (1, 2, 3, 7, 64):
         rc, ns, _ = _plan(lib, 2, 3000, 16, 2, req)
         assert rc == RA_OK and ns <= req
-    rc, ns, _ = _plan(lib, 1, 40, 16, 2, 64)
-    assert ns == 2                      # 40 keys -> two 32-key steps at most
+    rc, ns, _ = _plan(lib, 1, 300, 16, 2, 64)
+    assert ns == 2                      # splits hold whole 256-key quanta: 300 keys -> 2
     # a window limits the visible range
     rc, ns, _ = _plan(lib, 1, 100000, 16, 2, 0, 64)
     assert ns <= 2
@@ -131,6 +135,7 @@ def test_decode_plan_is_pure_and_sized():
     ((1, 0, 16, 2), RA_ERR_INVALID_ARG),
     ((-1, 10, 16, 2), RA_ERR_INVALID_ARG),
     ((1, 10, 16, 3), RA_ERR_INVALID_ARG),
+    ((1, 10, 16, 2, 0, 0, 128, -1), RA_ERR_INVALID_ARG),
 ])
 def test_decode_plan_rejects(lib, args, code):
     assert _plan(lib, *args)[0] == code
@@ -153,7 +158,7 @@ def _decode(lib, **kw):
 def test_decode_workspace_errors(lib):
     assert _decode(lib) == RA_ERR_WORKSPACE and "NULL" in _err(lib)
     assert _decode(lib, ws=FAKE + 512 + 16, wsb=1 << 30) == RA_ERR_WORKSPACE and "256-byte" in _err(lib)
-    _, ns, need = _plan(lib, 2, 300, 16, 2)
+    _, ns, need = _plan(lib, 2, 300, 16, 2, E=64)
     assert _decode(lib, ws=FAKE * 16, wsb=need - 1) == RA_ERR_WORKSPACE and "smaller" in _err(lib)
 
 

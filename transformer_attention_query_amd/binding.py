@@ -45,7 +45,7 @@ def _declare(lib):
     lib.rel_attn_prefill.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32,
                                      f32, i32, i32, i32, vp]
     lib.rel_attn_prefill.restype = i32
-    lib.rel_attn_decode_plan.argtypes = [i32, i32, i32, i32, i32, i32, i32,
+    lib.rel_attn_decode_plan.argtypes = [i32, i32, i32, i32, i32, i32, i32, i32,
                                          c.POINTER(i32), c.POINTER(sz)]
     lib.rel_attn_decode_plan.restype = i32
     lib.rel_attn_decode.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32,
@@ -164,12 +164,12 @@ def prefill(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, r: Optional[torch
 
 
 def decode_plan(B: int, L: int, Hq: int, Hkv: int, D: int = 128, num_splits: int = 0,
-                window: int = 0) -> Tuple[int, int]:
+                window: int = 0, rel_extent: int = 0) -> Tuple[int, int]:
     """(num_splits, workspace_bytes) the decode call will use; a pure function of the shape."""
     lib = load_library()
     ns = ctypes.c_int(0)
     ws = ctypes.c_size_t(0)
-    _check(lib.rel_attn_decode_plan(B, L, Hq, Hkv, D, int(num_splits), int(window),
+    _check(lib.rel_attn_decode_plan(B, L, Hq, Hkv, D, int(num_splits), int(window), int(rel_extent),
                                     ctypes.byref(ns), ctypes.byref(ws)))
     return ns.value, ws.value
 
@@ -208,7 +208,7 @@ def decode(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, r: Optional[torch.
     else:
         r = None
         P_cols = None
-    ns, ws_bytes = decode_plan(B, L, Hq, Hkv, D, num_splits, window)
+    ns, ws_bytes = decode_plan(B, L, Hq, Hkv, D, num_splits, window, rel_extent)
     if workspace is None:
         workspace = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
     out = torch.empty_like(q)

@@ -25,8 +25,10 @@ SOURCES = ["api.cpp", "prefill.hip", "decode.hip", "rel_logits.hip"]
 ARCH = "gfx950"
 
 # Packed fp32 VALU ops are switched off for every device pass (the compiler
-# would otherwise form v_pk_* from ordinary float code).
-DEVICE_FLAGS = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
+# would otherwise form v_pk_* from ordinary float code).  MFMAs are kept in
+# their VGPR form: the kernels fit in 256 VGPRs, and the AGPR form would cost
+# accumulator copies on every VALU touch.
+DEVICE_FLAGS = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops", "-mllvm", "-amdgpu-mfma-vgpr-form"]
 COMMON_FLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-I", INCLUDE, "-I", CSRC,
                 "-Wall", "-Wno-unused-function"]
 

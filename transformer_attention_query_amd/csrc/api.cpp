@@ -102,7 +102,7 @@ int rel_attn_prefill(const void* q, const void* k, const void* v, const void* r,
   return ok();
 }
 
-int rel_attn_decode_plan(int B, int L, int Hq, int Hkv, int D, int num_splits_req, int window,
+int rel_attn_decode_plan(int B, int L, int Hq, int Hkv, int D, int num_splits_req, int window, int rel_extent,
                          int* num_splits_out, size_t* workspace_bytes_out) {
   if (num_splits_out == nullptr || workspace_bytes_out == nullptr)
     return fail(RA_ERR_INVALID_ARG, "num_splits_out and workspace_bytes_out must not be NULL");
@@ -112,8 +112,9 @@ int rel_attn_decode_plan(int B, int L, int Hq, int Hkv, int D, int num_splits_re
     return fail(RA_ERR_INVALID_ARG, "Hq = %d, Hkv = %d: need positive Hq multiple of Hkv", Hq, Hkv);
   if (window < 0) return fail(RA_ERR_INVALID_ARG, "window = %d < 0", window);
   if (num_splits_req < 0) return fail(RA_ERR_INVALID_ARG, "num_splits = %d < 0", num_splits_req);
+  if (rel_extent < 0) return fail(RA_ERR_INVALID_ARG, "rel_extent = %d < 0", rel_extent);
   if (D != relattn::kHeadDim) return fail(RA_ERR_UNSUPPORTED, "head dim D = %d: only 128 is supported", D);
-  relattn::DecodePlan pl = relattn::plan_decode(B, L, Hq, Hkv, num_splits_req, window);
+  relattn::DecodePlan pl = relattn::plan_decode(B, L, Hq, Hkv, num_splits_req, window, rel_extent);
   *num_splits_out = pl.n_split;
   *workspace_bytes_out = pl.ws_bytes;
   return ok();
@@ -132,7 +133,7 @@ int rel_attn_decode(const void* q, const void* k, const void* v, const void* r, 
     return rc;
   if (out == q || out == k || out == v || out == r) return fail(RA_ERR_INVALID_ARG, "out aliases an input");
   if (num_splits < 0) return fail(RA_ERR_INVALID_ARG, "num_splits = %d < 0", num_splits);
-  relattn::DecodePlan pl = relattn::plan_decode(B, L, Hq, Hkv, num_splits, window);
+  relattn::DecodePlan pl = relattn::plan_decode(B, L, Hq, Hkv, num_splits, window, rel_extent);
   if (B == 0) return ok();
   if (workspace == nullptr) return fail(RA_ERR_WORKSPACE, "workspace is NULL (need %zu bytes)", pl.ws_bytes);
   if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0)
@@ -154,6 +155,9 @@ int rel_attn_decode(const void* q, const void* k, const void* v, const void* r, 
   a.chunk = pl.chunk;
   a.kv_lo = pl.kv_lo;
   a.n_hg = pl.n_hg;
+  a.rl_base = pl.rl_base;
+  a.rl_stride = pl.rl_stride;
+  a.rl = reinterpret_cast<const float*>(static_cast<char*>(workspace) + pl.ws_partial_bytes);
   hipError_t e = relattn::launch_decode(dtype, a, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return fail(RA_ERR_HIP, "decode launch failed: %s", hipGetErrorString(e));
   return ok();
@@ -177,6 +181,7 @@ int rel_logits(const void* r, const void* P_cols, float* out, int dtype, long lo
   a.n_rows = n_tok * H;
   a.d_r = d_r; a.E = rel_extent;
   a.s = (float)scale_of(log_scale, seq_len);
+  a.out_cols = rel_extent; a.out_stride = rel_extent; a.rev_base = 0;
   hipError_t e = relattn::launch_rel_logits(dtype, a, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return fail(RA_ERR_HIP, "rel_logits launch failed: %s", hipGetErrorString(e));
   return ok();

@@ -5,19 +5,22 @@
 // Inkling", section "Attention with Relative Positional Embedding"; for the
 // single query i = L-1 the bias of key j is s * r.P[:, L-1-j] when
 // L-1-j < E.  The visible keys (all of them, or the last `window`) are cut
-// into num_splits contiguous chunks ("num_splits" split-KV of the vLLM page,
-// section on the sheared-bias FA4 kernel); each wave owns one (sequence, kv
-// head, group of up to 16 query heads, split) and streams its chunk of K and
-// V exactly once for every query head of the group.  The partial softmax
-// states (unnormalised o, running max m, sum l) go to the caller's workspace
-// and a second kernel merges them by log-sum-exp.
+// into num_splits contiguous chunks (the split-KV "num_splits" of the vLLM
+// page, section on the sheared-bias FA4 kernel); each wave owns one
+// (sequence, kv head, group of up to 16 query heads, split) and streams its
+// chunk of K and V exactly once for every query head of the group.  The
+// partial softmax states (unnormalised o, running max m, sum l) go to the
+// caller's workspace and a second kernel merges them by log-sum-exp.
 //
 // Per 32-key step a wave computes S^T = K Q^T with 16x16x32 MFMAs (rows =
 // keys, columns = query heads, padded to 16), adds the bias rows produced by
 // R^T = P_rows r^T where each lane's A-operand row is the P row of its own
-// key's distance (no shear is needed for a single query), applies the online
-// softmax, and accumulates O^T = V^T P^T.  V is transposed through a
-// wave-private LDS buffer.
+// key's distance (a single query needs no shear), applies the online softmax
+// and accumulates O^T = V^T P^T.  The wave keeps two 32-key steps of K and V
+// in flight in registers (ping-pong, no copies), so HBM latency overlaps the
+// previous step's work.  V goes through a wave-private LDS tile: bf16 tiles
+// are stored row-major and read as MFMA fragments with the gfx950 transpose
+// read (ds_read_b64_tr_b16); fp32 tiles are stored transposed.
 #include "device_common.hpp"
 #include "relattn_internal.hpp"
 
@@ -26,65 +29,115 @@ namespace {
 
 constexpr int kDecWaves = 4;
 constexpr int kDecKeys = 32;  // keys per step
+constexpr int kDecDepth = 2;  // steps in flight per wave (a ring of register buffers)
+// Keys per split are a multiple of this: every wave of the workgroup runs the
+// same whole number of ring turns.
+constexpr int kDecSplitQuantum = kDecWaves * kDecKeys * kDecDepth;
+constexpr float kLazyRescale = 8.0f;  // log2 units: p may reach 2^8 before O is rescaled
 
-template <typename T>
-struct DecodeCfg {
-  static constexpr int PAD = 16 / sizeof(T);
-  static constexpr int VS = kDecKeys + PAD;  // V^T row stride (elements)
-  static constexpr size_t LDS_WAVE = size_t(kHeadDim) * VS * sizeof(T);
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef short s16x8 __attribute__((ext_vector_type(8)));
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+
+__device__ __forceinline__ s16x4 lds_read_tr(const __bf16* p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (lds_s16x4*)((__attribute__((address_space(3))) char*)((__attribute__((address_space(3))) void*)p)));
+}
+
+// V staging.  k-slot 8*g + t of the PV MFMA (lane group g = lane/16) holds
+// key 4*g + t (t < 4) or 16 + 4*g + (t-4) (t >= 4): the keys lane (g, c)
+// holds in its two S^T accumulators.  Lane (g, c) loaded keys 8g..8g+7, d-chunk c.
+template <typename T> struct DecV;
+
+template <> struct DecV<__bf16> {
+  // Row-major [32 keys][144]: 288-byte rows put the 8 rows a half-wave
+  // transpose read touches in 8 distinct 32-byte bank groups.
+  static constexpr int ROW = 144;
+  static constexpr size_t BYTES = size_t(kDecKeys) * ROW * sizeof(__bf16);
+  __device__ static void stage(__bf16* buf, const bf16x8 (&vd)[8], int g, int c) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) st8<__bf16>(buf + (8 * g + i) * ROW + 8 * c, vd[i]);
+  }
+  // Transpose read: within each 16-lane group, result lane 4i+e element k is
+  // element e of the 8 bytes addressed by lane i+4k.  Lane (g, s) therefore
+  // addresses row (4g + s/4) [then +16], columns 16*db + 4*(s%4) .. +3, and
+  // receives V[key(g, t)][16*db + s] for t = 0..7.
+  __device__ static bf16x8 frag(const __bf16* buf, int db, int g, int s) {
+    const __bf16* p0 = buf + (4 * g + (s >> 2)) * ROW + 16 * db + 4 * (s & 3);
+    const s16x4 a = lds_read_tr(p0);
+    const s16x4 b = lds_read_tr(p0 + 16 * ROW);
+    const s16x8 ab = __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7);
+    return __builtin_bit_cast(bf16x8, ab);
+  }
 };
 
-// Slot of key kappa (0..31) in a V^T row: k-slot 8*g + t of the PV MFMA holds
-// key 4*g + t (t < 4) or 16 + 4*g + (t-4) (t >= 4), the keys lane (g, c)
-// holds in its two S^T accumulators.
-__device__ __forceinline__ int dec_vt_pos(int kappa) {
-  const int blk = kappa >> 4, r16 = kappa & 15;
-  return 8 * (r16 >> 2) + 4 * blk + (r16 & 3);
-}
-
-// Write elements e of four consecutive keys' V vectors into one V^T row.
-__device__ __forceinline__ void put4(__bf16* dst, const bf16x8 (&x)[8], int base, int e) {
-  bf16x4 y;
-  y[0] = x[base + 0][e];
-  y[1] = x[base + 1][e];
-  y[2] = x[base + 2][e];
-  y[3] = x[base + 3][e];
-  *reinterpret_cast<bf16x4*>(dst) = y;
-}
-__device__ __forceinline__ void put4(float* dst, const f32x8 (&x)[8], int base, int e) {
-  f32x4 y;
-  y[0] = x[base + 0][e];
-  y[1] = x[base + 1][e];
-  y[2] = x[base + 2][e];
-  y[3] = x[base + 3][e];
-  *reinterpret_cast<f32x4*>(dst) = y;
-}
+template <> struct DecV<float> {
+  // Transposed [128 d][36]: slot of key kappa = 8*((kappa%16)/4) + 4*(kappa/16) + kappa%4.
+  static constexpr int VS = kDecKeys + 4;
+  static constexpr size_t BYTES = size_t(kHeadDim) * VS * sizeof(float);
+  __device__ static void put4(float* dst, const f32x8 (&x)[8], int base, int e) {
+    f32x4 y;
+    y[0] = x[base + 0][e];
+    y[1] = x[base + 1][e];
+    y[2] = x[base + 2][e];
+    y[3] = x[base + 3][e];
+    *reinterpret_cast<f32x4*>(dst) = y;
+  }
+  __device__ static void stage(float* buf, const f32x8 (&vd)[8], int g, int c) {
+    const int pos0 = 16 * (g & 1) + 4 * (g >> 1);  // keys 8g .. 8g+3
+    const int pos1 = pos0 + 8;                      // keys 8g+4 .. 8g+7
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      float* row = buf + (8 * c + e) * VS;
+      put4(row + pos0, vd, 0, e);
+      put4(row + pos1, vd, 4, e);
+    }
+  }
+  __device__ static f32x8 frag(const float* buf, int db, int g, int s) {
+    return ld8<float>(buf + (16 * db + s) * VS + 8 * g);
+  }
+};
 
 template <typename T>
-__global__ __launch_bounds__(kDecWaves * 64) void decode_split_kernel(DecodeArgs p) {
-  using C = DecodeCfg<T>;
+struct Chunk {
+  v8_t<T> k[2][kHeadDim / 32];  // A operands of S^T: key 16*blk + c, d-slots 32*st + 8*g ..
+  v8_t<T> v[8];                 // V rows 8*g + i, d-chunk c
+  f32x4 rl[2];                  // bias of keys 16*blk + 4*g .. +3 (log2 units)
+};
+
+// Per-workgroup reduction of the four waves' partial states (reuses the V tiles' LDS).
+struct DecReduce {
+  float m[kDecWaves][16];
+  float l[kDecWaves][16];
+  float o[kDecWaves][16][kHeadDim];
+};
+
+template <typename T>
+__global__ __launch_bounds__(kDecWaves * 64, sizeof(T) == 2 ? 2 : 1) void decode_split_kernel(DecodeArgs p) {
+  using VS = DecV<T>;
   constexpr int D = kHeadDim;
-  __shared__ __attribute__((aligned(16))) unsigned char smem[kDecWaves * C::LDS_WAVE];
+  constexpr size_t SMEM = kDecWaves * VS::BYTES > sizeof(DecReduce) ? kDecWaves * VS::BYTES : sizeof(DecReduce);
+  __shared__ __attribute__((aligned(16))) unsigned char smem[SMEM];
 
   const int tid = threadIdx.x;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lane = tid & 63;
-  const int g = lane >> 4;   // lane group: k-slots 8g..8g+7, accumulator rows 4g..4g+3
-  const int c = lane & 15;   // query head column / A-operand row
+  const int g = lane >> 4;  // lane group: k-slots 8g..8g+7, accumulator rows 4g..4g+3
+  const int c = lane & 15;  // query head column / A-operand row
 
   const int L = p.L, Hq = p.Hq, Hkv = p.Hkv, G = Hq / Hkv;
-  const int d_r = p.d_r, E = p.E, W = p.W;
 
-  // wave -> (batch, kv head, head group, split)
-  const long long wid = (long long)blockIdx.x * kDecWaves + w;
-  const long long n_waves = (long long)p.B * Hkv * p.n_hg * p.n_split;
-  if (wid >= n_waves) return;
-  const int split = (int)(wid % p.n_split);
-  long long rest = wid / p.n_split;
-  const int hg = (int)(rest % p.n_hg);
-  rest /= p.n_hg;
+  // workgroup -> (batch, split, kv head, head group).  Its four waves take
+  // interleaved 32-key steps of the split, so the workgroup streams one
+  // contiguous window of the cache; neighbouring workgroups take the kv heads
+  // of the same key range ([L, Hkv, D] interleaves the heads of a position).
+  const long long wg = blockIdx.x;
+  const int hg = (int)(wg % p.n_hg);
+  long long rest = wg / p.n_hg;
   const int kvh = (int)(rest % Hkv);
-  const int b = (int)(rest / Hkv);
+  rest /= Hkv;
+  const int split = (int)(rest % p.n_split);
+  const int b = (int)(rest / p.n_split);
 
   const int ks = p.kv_lo + split * p.chunk;
   const int ke = min(ks + p.chunk, L);
@@ -96,185 +149,191 @@ __global__ __launch_bounds__(kDecWaves * 64) void decode_split_kernel(DecodeArgs
   const T* qg = static_cast<const T*>(p.q);
   const T* kg = static_cast<const T*>(p.k);
   const T* vg = static_cast<const T*>(p.v);
-  const T* rg = static_cast<const T*>(p.r);
-  const T* pcg = static_cast<const T*>(p.pc);
-
   // query (B operand of S^T = K Q^T): k-slot 8g+t of step st is d = 32*st + 8*g + t
   v8_t<T> qreg[D / 32];
 #pragma unroll
   for (int st = 0; st < D / 32; ++st)
     qreg[st] = ld8_or_zero<T>(qg + (size_t(b) * Hq + h) * D + 32 * st + 8 * g, hvalid);
-  v8_t<T> rreg[kMaxDr / 32];
-#pragma unroll
-  for (int st = 0; st < kMaxDr / 32; ++st) {
-    const int c0 = 32 * st + 8 * g;
-    rreg[st] = ld8_or_zero<T>(rg + (size_t(b) * Hq + h) * d_r + (c0 < d_r ? c0 : 0), E > 0 && hvalid && c0 < d_r);
-  }
-  const int nsr = (d_r + 31) / 32;
+  // bias rows (log2-scaled s * r.P, reversed): key j reads entry j - L + rl_base
+  const float* rlrow = p.rl + (size_t(b) * Hq + h) * p.rl_stride;
 
   f32x4 o[D / 16];
 #pragma unroll
   for (int i = 0; i < D / 16; ++i) o[i] = zero4();
-  float m_run = -INFINITY, l_run = 0.0f;
+  // Running max in log2 units.  It starts finite so exp2(x - m_run) of a masked
+  // score is exactly 0 and never NaN.
+  float m_run = -1e30f, l_run = 0.0f;
 
-  T* vt = reinterpret_cast<T*>(smem + w * C::LDS_WAVE);
+  T* vbuf = reinterpret_cast<T*>(smem + w * VS::BYTES);
   const size_t row_stride = size_t(Hkv) * D;
   const T* kbase = kg + (size_t(b) * L * Hkv + kvh) * D;
   const T* vbase = vg + (size_t(b) * L * Hkv + kvh) * D;
 
-  v8_t<T> kc[2][D / 32], vc[8];
-  auto fetch = [&](int j0, v8_t<T> (&kd)[2][D / 32], v8_t<T> (&vd)[8]) {
+  // Every load of a step is unconditional, so the compiler's wait before a
+  // step covers only that step's loads and later steps' stay in flight: rows
+  // past the split end are clamped to its last key (masked later, weight
+  // exactly 0 against finite data).
+  auto fetch = [&](int j0, Chunk<T>& ch) {
 #pragma unroll
     for (int blk = 0; blk < 2; ++blk) {
-      const int j = j0 + 16 * blk + c;
-      const bool ok = j < ke;
-      const T* src = kbase + size_t(ok ? j : ks) * row_stride + 8 * g;
+      const int j = min(j0 + 16 * blk + c, ke - 1);
+      const T* src = kbase + size_t(j) * row_stride + 8 * g;
 #pragma unroll
-      for (int st = 0; st < D / 32; ++st) kd[blk][st] = ld8_or_zero<T>(src + 32 * st, ok);
+      for (int st = 0; st < D / 32; ++st) ch.k[blk][st] = ld8<T>(src + 32 * st);
     }
-    // V: lane (g, c) loads d-chunk c (8 values) of keys 8g .. 8g+7
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-      const int j = j0 + 8 * g + i;
-      const bool ok = j < ke;
-      vd[i] = ld8_or_zero<T>(vbase + size_t(ok ? j : ks) * row_stride + 8 * c, ok);
+      const int j = min(j0 + 8 * g + i, ke - 1);
+      ch.v[i] = ld8<T>(vbase + size_t(j) * row_stride + 8 * c);
+    }
+    // Bias of keys j0+16*blk+4g .. +3: entries j - L + rl_base.  Clamping keeps
+    // the read inside the row; a clamped key is at distance >= E, whose entry
+    // (like every entry beyond the extent) holds exactly 0.
+#pragma unroll
+    for (int blk = 0; blk < 2; ++blk) {
+      const int idx = min(max(j0 + 16 * blk + 4 * g - L + p.rl_base, 0), p.rl_stride - 4);
+      ch.rl[blk] = *reinterpret_cast<const f32x4*>(rlrow + idx);
     }
   };
 
-  if (ks < ke) fetch(ks, kc, vc);
-  for (int j0 = ks; j0 < ke; j0 += kDecKeys) {
-    v8_t<T> kn[2][D / 32], vn[8];
-    const bool more = j0 + kDecKeys < ke;
-    if (more) fetch(j0 + kDecKeys, kn, vn);
+  auto process = [&](int j0, Chunk<T>& ch) {
+    VS::stage(vbuf, ch.v, g, c);
 
-    // scores: accumulator (blk, v) of lane (g, c) = key j0 + 16*blk + 4*g + v, head c
-    f32x4 sc[2];
+    // scores in log2 units: accumulator (blk, v) of lane (g, c) = key j0 + 16*blk + 4*g + v, head c
+    f32x4 x[2];
 #pragma unroll
     for (int blk = 0; blk < 2; ++blk) {
-      sc[blk] = zero4();
+      x[blk] = zero4();
 #pragma unroll
-      for (int st = 0; st < D / 32; ++st) mma16(kc[blk][st], qreg[st], sc[blk]);
-#pragma unroll
-      for (int v = 0; v < 4; ++v) sc[blk][v] *= p.c1;
+      for (int st = 0; st < D / 32; ++st) mma16(ch.k[blk][st], qreg[st], x[blk]);
     }
-
-    // relative bias on keys with distance L-1-j < E
-    if (E > 0 && (L - 1) - min(j0 + kDecKeys - 1, ke - 1) < E) {
 #pragma unroll
-      for (int blk = 0; blk < 2; ++blk) {
-        const int j = j0 + 16 * blk + c;          // A-operand row of this lane
-        const int dist = L - 1 - j;
-        const bool ok = j < ke && dist >= 0 && dist < E;
-        const T* prow = pcg + size_t(ok ? dist : 0) * d_r + 8 * g;
-        f32x4 racc = zero4();
+    for (int blk = 0; blk < 2; ++blk)
 #pragma unroll
-        for (int st = 0; st < kMaxDr / 32; ++st) {
-          if (st < nsr) {
-            const bool okc = ok && (32 * st + 8 * g) < d_r;
-            mma16(ld8_or_zero<T>(prow + 32 * st, okc), rreg[st], racc);
-          }
-        }
-#pragma unroll
-        for (int v = 0; v < 4; ++v) sc[blk][v] += racc[v] * p.c2;
-      }
-    }
-
-    // mask: past the split end, or outside the window
-    const bool need_mask = (j0 + kDecKeys > ke) || (W > 0 && (L - 1) - j0 >= W);
-    if (need_mask) {
+      for (int v = 0; v < 4; ++v) x[blk][v] = fmaf(x[blk][v], p.c1, ch.rl[blk][v]);
+    if (j0 + kDecKeys > ke) {  // ragged end of the split
 #pragma unroll
       for (int blk = 0; blk < 2; ++blk)
 #pragma unroll
-        for (int v = 0; v < 4; ++v) {
-          const int j = j0 + 16 * blk + 4 * g + v;
-          if (j >= ke || (W > 0 && (L - 1) - j >= W)) sc[blk][v] = -INFINITY;
-        }
+        for (int v = 0; v < 4; ++v)
+          if (j0 + 16 * blk + 4 * g + v >= ke) x[blk][v] = -INFINITY;
     }
 
-    // online softmax per head (lanes c, c+16, c+32, c+48)
-    float mx = fmaxf(fmaxf(fmaxf(sc[0][0], sc[0][1]), fmaxf(sc[0][2], sc[0][3])),
-                     fmaxf(fmaxf(sc[1][0], sc[1][1]), fmaxf(sc[1][2], sc[1][3])));
+    // online softmax per head (lanes c, c+16, c+32, c+48); O is rescaled only
+    // when some row max grows by more than 2^kLazyRescale
+    float mx = fmaxf(fmaxf(fmaxf(x[0][0], x[0][1]), fmaxf(x[0][2], x[0][3])),
+                     fmaxf(fmaxf(x[1][0], x[1][1]), fmaxf(x[1][2], x[1][3])));
     mx = fmaxf(mx, xor_lane(mx, 16));
     mx = fmaxf(mx, xor_lane(mx, 32));
-    const float m_new = fmaxf(m_run, mx);
-    const float m_use = (m_new == -INFINITY) ? 0.0f : m_new;
-    const float corr = fast_exp2(m_run - m_use);
-    m_run = m_new;
+    if (__builtin_amdgcn_ballot_w64(mx > m_run + kLazyRescale) != 0) {
+      const float m_new = fmaxf(m_run, mx);
+      const float corr = fast_exp2(m_run - m_new);
+      m_run = m_new;
+      l_run *= corr;
+#pragma unroll
+      for (int i = 0; i < D / 16; ++i)
+#pragma unroll
+        for (int v = 0; v < 4; ++v) o[i][v] *= corr;
+    }
     float psum = 0.0f;
     v8_t<T> pb;
 #pragma unroll
     for (int blk = 0; blk < 2; ++blk)
 #pragma unroll
       for (int v = 0; v < 4; ++v) {
-        const float e = fast_exp2(sc[blk][v] - m_use);
+        const float e = fast_exp2(x[blk][v] - m_run);
         psum += e;
         pb[4 * blk + v] = T(e);
       }
-    l_run = l_run * corr + psum;
-#pragma unroll
-    for (int i = 0; i < D / 16; ++i)
-#pragma unroll
-      for (int v = 0; v < 4; ++v) o[i][v] *= corr;
+    l_run += psum;
 
-    // V^T into LDS: V^T[d][slot] for d = 8c + e, keys 8g..8g+3 and 8g+4..8g+7
-    {
-      const int pos0 = dec_vt_pos(8 * g);
-      const int pos1 = dec_vt_pos(8 * g + 4);
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        T* row = vt + (8 * c + e) * C::VS;
-        put4(row + pos0, vc, 0, e);
-        put4(row + pos1, vc, 4, e);
-      }
-    }
     wave_lds_fence();
 #pragma unroll
-    for (int db = 0; db < D / 16; ++db) mma16(ld8<T>(vt + (16 * db + c) * C::VS + 8 * g), pb, o[db]);
+    for (int db = 0; db < D / 16; ++db) mma16(VS::frag(vbuf, db, g, c), pb, o[db]);
     wave_lds_fence();
+  };
 
-    if (more) {
+  // Wave w takes steps w, w+4, w+8, ... of the split through a ring of
+  // kDecDepth buffers: a step is consumed while the next kDecDepth-1 are in
+  // flight.  Splits hold a multiple of kDecSplitQuantum keys (the last split
+  // may end early: its missing keys are masked), so every fetch and every
+  // process below is unconditional and the waits stay partial.
+  constexpr int NB = kDecDepth;
+  constexpr int STRIDE = kDecWaves * kDecKeys;
+  Chunk<T> ring[NB];
 #pragma unroll
-      for (int blk = 0; blk < 2; ++blk)
+  for (int bfi = 0; bfi < NB - 1; ++bfi) fetch(ks + w * kDecKeys + bfi * STRIDE, ring[bfi]);
+  for (int j0 = ks + w * kDecKeys; j0 < ks + p.chunk; j0 += NB * STRIDE) {
 #pragma unroll
-        for (int st = 0; st < D / 32; ++st) kc[blk][st] = kn[blk][st];
-#pragma unroll
-      for (int i = 0; i < 8; ++i) vc[i] = vn[i];
+    for (int bfi = 0; bfi < NB; ++bfi) {
+      fetch(j0 + (bfi + NB - 1) * STRIDE, ring[(bfi + NB - 1) % NB]);
+      process(j0 + bfi * STRIDE, ring[bfi]);
     }
   }
 
-  // partial state: sum l over the 4 lane groups; o rows d = 16*db + 4*g + v
+  // workgroup reduction of the four waves' (o, m, l) by log-sum-exp
   float l_tot = l_run + xor_lane(l_run, 16);
   l_tot += xor_lane(l_tot, 32);
-  if (!hvalid) return;
+  __syncthreads();  // every wave is done with its V tile: the LDS is reused
+  DecReduce* red = reinterpret_cast<DecReduce*>(smem);
+#pragma unroll
+  for (int db = 0; db < D / 16; ++db) *reinterpret_cast<f32x4*>(&red->o[w][c][16 * db + 4 * g]) = o[db];
+  if (g == 0) {
+    red->m[w][c] = m_run;
+    red->l[w][c] = l_tot;
+  }
+  __syncthreads();
+  // thread t: head t/16, output columns 8*(t%16) .. +7
+  const int hc = tid >> 4;
+  const int d0 = 8 * (tid & 15);
+  const int hin2 = hg * 16 + hc;
+  if (hin2 >= G) return;
+  float M = red->m[0][hc];
+#pragma unroll
+  for (int i = 1; i < kDecWaves; ++i) M = fmaxf(M, red->m[i][hc]);
+  float wsum_l = 0.0f;
+  f32x8 acc;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) acc[e] = 0.0f;
+#pragma unroll
+  for (int i = 0; i < kDecWaves; ++i) {
+    const float wt = fast_exp2(red->m[i][hc] - M);
+    wsum_l += wt * red->l[i][hc];
+    const f32x8 oi = *reinterpret_cast<const f32x8*>(&red->o[i][hc][d0]);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc[e] += wt * oi[e];
+  }
   const size_t n_bh = size_t(p.B) * Hq;
-  const size_t bh = size_t(b) * Hq + h;
+  const size_t bh = size_t(b) * Hq + kvh * G + hin2;
   float* ws_o = p.ws + (size_t(split) * n_bh + bh) * D;
   float* ws_m = p.ws + size_t(p.n_split) * n_bh * D;
   float* ws_l = ws_m + size_t(p.n_split) * n_bh;
-#pragma unroll
-  for (int db = 0; db < D / 16; ++db) *reinterpret_cast<f32x4*>(ws_o + 16 * db + 4 * g) = o[db];
-  if (g == 0) {
-    ws_m[size_t(split) * n_bh + bh] = m_run;
-    ws_l[size_t(split) * n_bh + bh] = l_tot;
+  *reinterpret_cast<f32x8*>(ws_o + d0) = acc;
+  if (d0 == 0) {
+    ws_m[size_t(split) * n_bh + bh] = M;
+    ws_l[size_t(split) * n_bh + bh] = wsum_l;
   }
 }
 
-// Log-sum-exp merge of the split partials: one workgroup per (batch, head),
-// thread (sg, d4) covers splits sg, sg+8, ... and output columns 4*d4..4*d4+3.
+// Log-sum-exp merge of the split partials.  Workgroup (bh, quarter) merges
+// output columns 32*quarter .. +31 of one (batch, head): thread (sg, d4)
+// covers splits sg, sg+NSG, ... and columns 4*d4 .. 4*d4+3 of the quarter.
 constexpr int kMergeThreads = 256;
+constexpr int kMergeCols = 32;
 
 template <typename T>
 __global__ __launch_bounds__(kMergeThreads) void decode_merge_kernel(DecodeArgs p) {
   constexpr int D = kHeadDim;
-  constexpr int NSG = kMergeThreads / (D / 4);  // split groups (8)
+  constexpr int NSG = kMergeThreads / (kMergeCols / 4);  // split groups (32)
   __shared__ float red_m[NSG];
-  __shared__ float red_l[NSG][D / 4];
-  __shared__ f32x4 red_o[NSG][D / 4];
+  __shared__ float red_l[NSG];
+  __shared__ f32x4 red_o[NSG][kMergeCols / 4];
 
-  const int bh = blockIdx.x;
+  const int bh = blockIdx.x / (D / kMergeCols);
+  const int col0 = (blockIdx.x % (D / kMergeCols)) * kMergeCols;
   const int tid = threadIdx.x;
-  const int d4 = tid % (D / 4);
-  const int sg = tid / (D / 4);
+  const int d4 = tid % (kMergeCols / 4);
+  const int sg = tid / (kMergeCols / 4);
   const size_t n_bh = size_t(p.B) * p.Hq;
   const float* ws_o = p.ws;
   const float* ws_m = p.ws + size_t(p.n_split) * n_bh * D;
@@ -287,76 +346,105 @@ __global__ __launch_bounds__(kMergeThreads) void decode_merge_kernel(DecodeArgs 
   float M = red_m[0];
 #pragma unroll
   for (int i = 1; i < NSG; ++i) M = fmaxf(M, red_m[i]);
-  const float Muse = (M == -INFINITY) ? 0.0f : M;
 
   f32x4 acc = zero4();
   float den = 0.0f;
+#pragma unroll 4
   for (int s = sg; s < p.n_split; s += NSG) {
-    const float wgt = fast_exp2(ws_m[size_t(s) * n_bh + bh] - Muse);
-    const f32x4 os = *reinterpret_cast<const f32x4*>(ws_o + (size_t(s) * n_bh + bh) * D + 4 * d4);
+    const float wgt = fast_exp2(ws_m[size_t(s) * n_bh + bh] - M);
+    const f32x4 os = *reinterpret_cast<const f32x4*>(ws_o + (size_t(s) * n_bh + bh) * D + col0 + 4 * d4);
     den += wgt * ws_l[size_t(s) * n_bh + bh];
 #pragma unroll
     for (int v = 0; v < 4; ++v) acc[v] += wgt * os[v];
   }
   red_o[sg][d4] = acc;
-  red_l[sg][d4] = den;
+  if (d4 == 0) red_l[sg] = den;
   __syncthreads();
   if (sg != 0) return;
+  den = red_l[0];
 #pragma unroll
   for (int i = 1; i < NSG; ++i) {
-    const f32x4 x = red_o[i][d4];
+    const f32x4 y = red_o[i][d4];
 #pragma unroll
-    for (int v = 0; v < 4; ++v) acc[v] += x[v];
-    den += red_l[i][d4];
+    for (int v = 0; v < 4; ++v) acc[v] += y[v];
+    den += red_l[i];
   }
   const float inv = 1.0f / den;
-  st4_f32<T>(static_cast<T*>(p.out) + size_t(bh) * D + 4 * d4, acc[0] * inv, acc[1] * inv, acc[2] * inv,
-             acc[3] * inv);
-  if (p.lse != nullptr && d4 == 0) p.lse[bh] = (Muse + log2f(den)) * kLn2;
+  st4_f32<T>(static_cast<T*>(p.out) + size_t(bh) * D + col0 + 4 * d4, acc[0] * inv, acc[1] * inv,
+             acc[2] * inv, acc[3] * inv);
+  if (p.lse != nullptr && col0 == 0 && d4 == 0) p.lse[bh] = (M + log2f(den)) * kLn2;
 }
 
 template <typename T>
 hipError_t launch_decode_t(const DecodeArgs& a, hipStream_t stream) {
-  const long long n_waves = (long long)a.B * a.Hkv * a.n_hg * a.n_split;
-  const long long grid = (n_waves + kDecWaves - 1) / kDecWaves;
+  {
+    // bias rows of every (sequence, head): s * log2(e) * r.P[:, d], stored
+    // reversed so that key j finds its distance L-1-j at entry j - L + rl_base
+    // (all zeros when E == 0)
+    RelLogitsArgs ra;
+    ra.r = a.r;
+    ra.pc = a.pc;
+    ra.out = const_cast<float*>(a.rl);
+    ra.n_rows = (long long)a.B * a.Hq;
+    ra.d_r = a.d_r;
+    ra.E = a.E;
+    ra.s = a.c2;
+    ra.out_cols = a.rl_stride;
+    ra.out_stride = a.rl_stride;
+    ra.rev_base = a.rl_base;
+    hipError_t e = launch_rel_logits(sizeof(T) == 2 ? 1 : 2, ra, stream);
+    if (e != hipSuccess) return e;
+  }
+  const long long grid = (long long)a.B * a.Hkv * a.n_hg * a.n_split;
   if (grid > 0x7fffffffLL) return hipErrorInvalidConfiguration;
   hipLaunchKernelGGL(decode_split_kernel<T>, dim3((unsigned)grid), dim3(kDecWaves * 64), 0, stream, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(decode_merge_kernel<T>, dim3((unsigned)(a.B * a.Hq)), dim3(kMergeThreads), 0, stream, a);
+  hipLaunchKernelGGL(decode_merge_kernel<T>, dim3((unsigned)(a.B * a.Hq * (kHeadDim / kMergeCols))),
+                     dim3(kMergeThreads), 0, stream, a);
   return hipGetLastError();
 }
 
 }  // namespace
 
-DecodePlan plan_decode(int B, int L, int Hq, int Hkv, int num_splits_req, int window) {
+DecodePlan plan_decode(int B, int L, int Hq, int Hkv, int num_splits_req, int window, int rel_extent) {
   DecodePlan pl;
   const int G = Hq / Hkv;
   pl.n_hg = (G + 15) / 16;
   pl.kv_lo = (window > 0 && L > window) ? L - window : 0;
   const int vis = L - pl.kv_lo;
-  const int max_split = (vis + kDecKeys - 1) / kDecKeys;  // at least one 32-key step per split
+  const int max_split = (vis + kDecSplitQuantum - 1) / kDecSplitQuantum;  // >= one quantum per split
   int ns;
   if (num_splits_req > 0) {
     ns = num_splits_req;
   } else {
-    // Aim for ~1024 waves (4 per CU of a 256-CU part) and at least 256 keys per split.
-    const long long waves_per_split = (long long)B * Hkv * pl.n_hg;
-    long long want = (1024 + waves_per_split - 1) / waves_per_split;
-    const long long cap = (vis + 255) / 256;
+    // Aim for ~512 workgroups (two per CU of a 256-CU part), each streaming
+    // at least two quanta so its prologue latency is amortised.
+    const long long wgs_per_split = (long long)B * Hkv * pl.n_hg;
+    long long want = (512 + wgs_per_split - 1) / wgs_per_split;
+    const long long cap = (vis + 2 * kDecSplitQuantum - 1) / (2 * kDecSplitQuantum);
     if (want > cap) want = cap;
     ns = (int)(want < 1 ? 1 : want);
   }
   if (ns > max_split) ns = max_split;
   if (ns < 1) ns = 1;
   int chunk = (vis + ns - 1) / ns;
-  chunk = (chunk + kDecKeys - 1) / kDecKeys * kDecKeys;
+  chunk = (chunk + kDecSplitQuantum - 1) / kDecSplitQuantum * kDecSplitQuantum;
   ns = (vis + chunk - 1) / chunk;  // drop splits that would be empty
   if (ns < 1) ns = 1;
   pl.n_split = ns;
-  pl.chunk = chunk < kDecKeys ? kDecKeys : chunk;
+  pl.chunk = chunk;
   const size_t n_bh = size_t(B) * Hq;
-  pl.ws_bytes = size_t(ns) * n_bh * (kHeadDim + 2) * sizeof(float);
+  pl.ws_partial_bytes = (size_t(ns) * n_bh * (kHeadDim + 2) * sizeof(float) + 255) / 256 * 256;
+  // Entry index of key j is j - L + rl_base (clamped to the row).
+  // rl_base >= E + 31 keeps every key of a step that has bias at an index
+  // >= 0, (rl_base - L + kv_lo) % 4 == 0 makes the 4-key groups 16-byte
+  // aligned (steps start at kv_lo + 32n), and the row reaches rl_base + 31 so
+  // a ragged last step stays inside it.
+  const int base0 = rel_extent + 31;
+  pl.rl_base = base0 + (((L - pl.kv_lo - base0) % 4) + 4) % 4;
+  pl.rl_stride = (pl.rl_base + 31 + 3) / 4 * 4;
+  pl.ws_bytes = pl.ws_partial_bytes + n_bh * size_t(pl.rl_stride) * sizeof(float);
   return pl;
 }
 

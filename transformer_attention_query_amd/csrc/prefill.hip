@@ -5,8 +5,8 @@
 // Positional Embedding", eqs. for rel_logits and l(i,j,h)):
 //   l(i,j) = s*alpha*q_i.k_j + [0 <= i-j < E] * s * r_i.P[:, i-j]
 // under the causal / sliding-window mask, then the softmax over j and the
-// weighted sum of v_j, in one pass (online softmax, the bias added before the
-// running max as the FA4 fork does -- section "Relative Logits
+// weighted sum of v_j, in one pass (online softmax with the bias added before
+// the running max, as the FA4 fork does -- section "Relative Logits
 // Optimization", Figure 3).
 //
 // Work decomposition
@@ -16,70 +16,127 @@
 //     window are never touched).
 //   * Scores are computed transposed, S^T = K Q^T, so lane l of a wave owns
 //     query l%32 and the 32x32 MFMA accumulators run over keys: the row max
-//     and row sum are in-lane reductions plus one exchange with lane l^32,
-//     and the output accumulator O^T = V^T P^T needs no cross-lane traffic
-//     for its rescaling.
-//   * K tiles are staged in LDS row-major, V tiles transposed (d-major, with
-//     the keys of each 16-key chunk permuted so that one 16-byte LDS read
-//     yields the 8 keys a lane feeds to the PV MFMA).
+//     and row sum are in-lane reductions plus one exchange with lane l^32, and
+//     the output accumulator O^T = V^T P^T needs no cross-lane traffic.
+//   * K tiles are staged in LDS row-major.  bf16 V tiles are staged row-major
+//     too and read as MFMA fragments with the gfx950 transpose read
+//     (ds_read_b64_tr_b16); fp32 V tiles are stored transposed.
 //   * Relative bias ("sheared bias" of section "Relative Logits
-//     Optimization": bias(i,j) = rel_logits(i, i-j)) is formed per wave in
-//     LDS: the wave's tile needs distances in [i0w - j0 - N + 1, i0w - j0 + 31];
-//     it computes R^T = P_rows r^T for those N+32 distances with MFMA (P rows
-//     staged in LDS for the whole workgroup), writes R into a wave-private LDS
-//     buffer indexed [query][distance], and reads it back along the shear
-//     (row a, column a - b + N for key b) -- a lane only ever reads its own
-//     query's row.  Distances outside [0, E) read zero rows of P, so the
-//     rel_extent cut and the causal edge need no per-score test.
-//   * K/V for the next tile are fetched into registers while the current
-//     tile computes.
+//     Optimization": bias(i,j) = rel_logits(i, i-j)) is formed per wave: the
+//     wave's (32 queries x N keys) tile needs distances [Dw - N + 1, Dw + 31]
+//     (Dw = its first query minus the tile's first key); it computes
+//     R^T = P_rows r^T for the N+32 distances [Dw - N, Dw + 32) with MFMA,
+//     writes R to a wave-private LDS buffer indexed [query][distance] and reads
+//     it back along the shear (row a, column a - b + N for key b): a lane only
+//     reads its own query's row.  Distances outside [0, E) read zero P rows,
+//     so the rel_extent cut needs no per-score test.
+//   * P rows live in a ring of N-row chunks in LDS.  A tile's window of
+//     distances [D0 - N, D0 + M) is M/N + 1 consecutive chunks (D0 = first
+//     query minus first key); moving one tile right slides the window down by
+//     one chunk, so each tile fetches a single new chunk, into a slot the
+//     current window does not use.
+//   * The next tile's K, V and P chunk are fetched into registers while the
+//     current tile computes and are written to LDS between two barriers.
+//   * Softmax works in units of c2 = s*log2(e): y = S*(c1/c2) + R, so the bias
+//     rows need no scaling, and p = exp2(c2*y - c2*m).  O is rescaled only
+//     when a row maximum grows by more than 2^8 (exact either way: O and l
+//     share the stale maximum).
 #include "device_common.hpp"
 #include "relattn_internal.hpp"
 
 namespace relattn {
 namespace {
 
-template <typename T, int WAVES, int N>
-struct PrefillCfg {
-  static constexpr int M = 32 * WAVES;       // queries per workgroup
-  static constexpr int NB = N / 32;          // 32-key blocks per tile
-  static constexpr int PAD = 16 / sizeof(T); // 16 bytes of padding per LDS row
-  static constexpr int KS = kHeadDim + PAD;  // K tile row stride (elements)
-  static constexpr int VS = N + PAD;         // V^T tile row stride
-  static constexpr int PSMAX = kMaxDr + PAD; // P slice row stride (max)
-  static constexpr int NR = M + N;           // P slice rows (distances)
-  static constexpr int LS = N + 36;          // R buffer row stride (floats)
-  static constexpr int THREADS = WAVES * 64;
-  static constexpr int KV_VECS = N * (kHeadDim / 8) / THREADS;  // 8-element vectors per thread per tile
-  static constexpr size_t LDS_K = size_t(N) * KS * sizeof(T);
-  static constexpr size_t LDS_V = size_t(kHeadDim) * VS * sizeof(T);
-  static constexpr size_t LDS_P = size_t(NR) * PSMAX * sizeof(T);
-  static constexpr size_t LDS_R = size_t(WAVES) * 32 * LS * sizeof(float);
-  static constexpr size_t LDS_TOTAL = LDS_K + LDS_V + LDS_P + LDS_R;
-  static_assert(KV_VECS * THREADS == N * (kHeadDim / 8), "tile must split evenly over threads");
-  static_assert(LDS_TOTAL <= 160 * 1024, "LDS budget of one gfx950 workgroup");
+constexpr float kLazyRescaleLog2 = 8.0f;
+
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef short s16x8 __attribute__((ext_vector_type(8)));
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+
+__device__ __forceinline__ s16x4 lds_read_tr(const __bf16* p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (lds_s16x4*)((__attribute__((address_space(3))) char*)((__attribute__((address_space(3))) void*)p)));
+}
+
+// V tile staging and PV A-operand fragments.  The PV MFMA's k-slot 8*h + t
+// (h = lane/32) holds key 16*c16 + 8*(t/4) + 4*h + t%4 of 16-key chunk c16:
+// the key the S^T accumulator register 8*(c16%2) + t of that lane holds.
+template <typename T, int N> struct PreV;
+
+template <int N> struct PreV<__bf16, N> {
+  // Row-major [N keys][160]: 320-byte rows put the 4 rows x 64 bytes a
+  // half-wave transpose read touches in distinct bank groups.
+  static constexpr int ROW = 160;
+  static constexpr size_t BYTES = size_t(N) * ROW * sizeof(__bf16);
+  __device__ static void store(__bf16* vs, int row, int c8, const bf16x8& x) { st8<__bf16>(vs + row * ROW + c8 * 8, x); }
+  // Within each 16-lane group G, result lane 4i+e element k is element e of
+  // the 8 bytes addressed by lane i+4k: lane (G, s) addresses key row
+  // 16*c16 + 4*h + s/4 (then +8) at columns 32*db + 16*(G%2) + 4*(s%4).
+  __device__ static bf16x8 frag(const __bf16* vs, int c16, int db, int lane) {
+    const int G = lane >> 4, s = lane & 15, h = G >> 1;
+    const __bf16* p0 = vs + (16 * c16 + 4 * h + (s >> 2)) * ROW + 32 * db + 16 * (G & 1) + 4 * (s & 3);
+    const s16x4 a = lds_read_tr(p0);
+    const s16x4 b = lds_read_tr(p0 + 8 * ROW);
+    return __builtin_bit_cast(bf16x8, __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7));
+  }
 };
 
-// Position of key `row` (0..N-1) inside a V^T row: within each 16-key chunk
-// the middle two groups of four are swapped, so that k-slot 8*h + t of the
-// PV MFMA (h = lane/32) holds key 8*(t/4) + 4*h + t%4, which is the key the
-// S^T accumulator register 8*(chunk%2) + t of that lane holds.
-__device__ __forceinline__ int vt_pos(int row) {
-  int k16 = row & 15;
-  int p16 = ((k16 >> 2) & 1) * 8 + (k16 >> 3) * 4 + (k16 & 3);
-  return (row & ~15) + p16;
-}
+template <int N> struct PreV<float, N> {
+  // Transposed [128 d][N + 4]; key `row` sits at the slot where the middle two
+  // groups of four of its 16-key chunk are swapped.
+  static constexpr int VS = N + 4;
+  static constexpr size_t BYTES = size_t(kHeadDim) * VS * sizeof(float);
+  __device__ static int pos(int row) {
+    const int k16 = row & 15;
+    return (row & ~15) + ((k16 >> 2) & 1) * 8 + (k16 >> 3) * 4 + (k16 & 3);
+  }
+  __device__ static void store(float* vs, int row, int c8, const f32x8& x) {
+    const int p = pos(row);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) vs[(c8 * 8 + e) * VS + p] = x[e];
+  }
+  __device__ static f32x8 frag(const float* vs, int c16, int db, int lane) {
+    const int a = lane & 31, h = lane >> 5;
+    return ld8<float>(vs + (32 * db + a) * VS + 16 * c16 + 8 * h);
+  }
+};
+
+template <typename T, int WAVES, int N>
+struct PrefillCfg {
+  static constexpr int M = 32 * WAVES;        // queries per workgroup
+  static constexpr int NB = N / 32;           // 32-key blocks per tile
+  static constexpr int PAD = 16 / sizeof(T);  // 16 bytes of padding per K / P row
+  static constexpr int KS = kHeadDim + PAD;   // K tile row stride (elements)
+  static constexpr int PS = kMaxDr + PAD;     // P ring row stride (elements)
+  static constexpr int WIN = M / N + 1;       // P chunks in a tile's window
+  static constexpr int RING = WIN < 4 ? 4 : 8;  // P chunk slots: a power of two > WIN
+  static constexpr int LS = N + 36;           // R buffer row stride (floats)
+  static constexpr int THREADS = WAVES * 64;
+  static constexpr int KV_VECS = N * (kHeadDim / 8) / THREADS;  // 8-element vectors per thread per tile
+  static constexpr int P_VECS = N * (kMaxDr / 8) / THREADS;     // per thread per P chunk (d_r = 128)
+  static constexpr size_t LDS_K = size_t(N) * KS * sizeof(T);
+  static constexpr size_t LDS_V = PreV<T, N>::BYTES;
+  static constexpr size_t LDS_P = size_t(RING) * N * PS * sizeof(T);
+  static constexpr size_t LDS_R = size_t(WAVES) * 32 * LS * sizeof(float);
+  static constexpr size_t LDS_TOTAL = LDS_K + LDS_V + LDS_P + LDS_R;
+  static_assert(M % N == 0 && N % 32 == 0, "the P window must be whole chunks of whole blocks");
+  static_assert(WIN < RING && WIN <= 8, "the ring holds the window plus the chunk being filled");
+  static_assert(KV_VECS * THREADS == N * (kHeadDim / 8), "tile must split evenly over threads");
+  static_assert(P_VECS * THREADS == N * (kMaxDr / 8), "chunk must split evenly over threads");
+  static_assert(LDS_TOTAL <= 160 * 1024, "LDS budget of one gfx950 workgroup");
+};
 
 template <typename T, int WAVES, int N>
 __global__ __launch_bounds__(WAVES * 64, 1) void prefill_kernel(PrefillArgs p, int n_qt, int n_groups) {
   using C = PrefillCfg<T, WAVES, N>;
+  using VS = PreV<T, N>;
   constexpr int M = C::M, NB = C::NB;
   constexpr int D = kHeadDim;
 
   __shared__ __attribute__((aligned(16))) unsigned char smem[C::LDS_TOTAL];
   T* Ks = reinterpret_cast<T*>(smem);
-  T* Vt = reinterpret_cast<T*>(smem + C::LDS_K);
-  T* Pt = reinterpret_cast<T*>(smem + C::LDS_K + C::LDS_V);
+  T* Vs = reinterpret_cast<T*>(smem + C::LDS_K);
+  T* Pr = reinterpret_cast<T*>(smem + C::LDS_K + C::LDS_V);
   float* Rs = reinterpret_cast<float*>(smem + C::LDS_K + C::LDS_V + C::LDS_P);
 
   const int T_ = p.T, Hq = p.Hq, Hkv = p.Hkv, G = Hq / Hkv;
@@ -120,6 +177,10 @@ __global__ __launch_bounds__(WAVES * 64, 1) void prefill_kernel(PrefillArgs p, i
   const T* rg = static_cast<const T*>(p.r);
   const T* pcg = static_cast<const T*>(p.pc);
 
+  // softmax constants in units of c2 (c2 = s*log2(e) > 0)
+  const float qk_scale = p.c1 / p.c2;
+  const float lazy = kLazyRescaleLog2 / p.c2;
+
   // ---- this lane's query and relative feature, as MFMA B operands
   v8_t<T> qreg[D / 16];
   {
@@ -129,19 +190,17 @@ __global__ __launch_bounds__(WAVES * 64, 1) void prefill_kernel(PrefillArgs p, i
   }
   v8_t<T> rreg[kMaxDr / 16];
   const int nkr = d_r / 16;
-  if (E > 0) {
+  {
     const T* rrow = rg + ((size_t(b) * T_ + (qvalid ? qa : 0)) * Hq + h) * d_r + 8 * h2;
 #pragma unroll
-    for (int kk = 0; kk < kMaxDr / 16; ++kk) rreg[kk] = ld8_or_zero<T>(rrow + kk * 16, qvalid && kk < nkr);
-  } else {
-#pragma unroll
-    for (int kk = 0; kk < kMaxDr / 16; ++kk) rreg[kk] = zero8<T>();
+    for (int kk = 0; kk < kMaxDr / 16; ++kk) rreg[kk] = ld8_or_zero<T>(rrow + kk * 16, E > 0 && qvalid && kk < nkr);
   }
 
   f32x16 o[D / 32];
 #pragma unroll
   for (int i = 0; i < D / 32; ++i) o[i] = zero16();
-  float m_run = -INFINITY;
+  // running max (units of c2), finite so exp2 of a masked score is exactly 0
+  float m_run = -1e30f;
   float l_run = 0.0f;
 
   // ---- visible key tiles of this q-tile
@@ -150,160 +209,206 @@ __global__ __launch_bounds__(WAVES * 64, 1) void prefill_kernel(PrefillArgs p, i
   if (W > 0) kt_lo = max(0, i0 - W + 1) / N;
   const int kt_hi = i_last / N;
 
-  // ---- register prefetch of one K/V tile
-  v8_t<T> kpre[C::KV_VECS], vpre[C::KV_VECS];
+  // ---- K/V tile and P chunk prefetch through registers
   const size_t kv_row_stride = size_t(Hkv) * D;
   const T* kbase = kg + (size_t(b) * T_ * Hkv + kvh) * D;
   const T* vbase = vg + (size_t(b) * T_ * Hkv + kvh) * D;
+  v8_t<T> kpre[C::KV_VECS], vpre[C::KV_VECS];
   auto fetch_kv = [&](int kt) {
     const int j0 = kt * N;
 #pragma unroll
     for (int i = 0; i < C::KV_VECS; ++i) {
       const int vid = tid + i * C::THREADS;
-      const int row = vid >> 4, c8 = vid & 15;
-      const int j = j0 + row;
-      const bool ok = j < T_;
-      const size_t off = size_t(ok ? j : 0) * kv_row_stride + c8 * 8;
-      kpre[i] = ld8_or_zero<T>(kbase + off, ok);
-      vpre[i] = ld8_or_zero<T>(vbase + off, ok);
+      const int j = min(j0 + (vid >> 4), T_ - 1);  // rows past T: clamped, masked later
+      const size_t off = size_t(j) * kv_row_stride + (vid & 15) * 8;
+      kpre[i] = ld8<T>(kbase + off);
+      vpre[i] = ld8<T>(vbase + off);
     }
   };
-
-  fetch_kv(kt_lo);
-
-  const int PS = d_r + C::PAD;
-  float* rs = Rs + w * 32 * C::LS;
-
-  for (int kt = kt_lo; kt <= kt_hi; ++kt) {
-    const int j0 = kt * N;
-    const int D0 = i0 - j0;  // distance between the first query and the first key of the tile
-    const bool wg_band = E > 0 && max(0, D0 - (N - 1)) < E;
-
-    __syncthreads();  // every wave is done reading the previous tile
-    // K row-major, V transposed with the PV key permutation
+  auto store_kv = [&]() {
 #pragma unroll
     for (int i = 0; i < C::KV_VECS; ++i) {
       const int vid = tid + i * C::THREADS;
       const int row = vid >> 4, c8 = vid & 15;
       st8<T>(Ks + row * C::KS + c8 * 8, kpre[i]);
-      const int pos = vt_pos(row);
-#pragma unroll
-      for (int e = 0; e < 8; ++e) Vt[(c8 * 8 + e) * C::VS + pos] = vpre[i][e];
+      VS::store(Vs, row, c8, vpre[i]);
     }
-    if (wg_band) {
-      // P rows for distances D0 - N .. D0 + M - 1 (zero outside [0, E))
-      const int vec_per_row = d_r / 8;
-      const int nvec = C::NR * vec_per_row;
-      for (int vid = tid; vid < nvec; vid += C::THREADS) {
-        const int rho = vid / vec_per_row, c8 = vid - rho * vec_per_row;
-        const int d = D0 - N + rho;
-        const bool ok = d >= 0 && d < E;
-        st8<T>(Pt + rho * PS + c8 * 8, ld8_or_zero<T>(pcg + size_t(ok ? d : 0) * d_r + c8 * 8, ok));
-      }
-    }
-    __syncthreads();
+  };
 
-    if (kt < kt_hi) fetch_kv(kt + 1);
+  // P chunk k holds distances [k*N, k*N + N) in ring slot k mod RING.  Vector
+  // i of this thread covers chunk row vid/16, columns 8*(vid%16) .. +7 (used
+  // when 8*(vid%16) < d_r).
+  const int vec_per_row = d_r / 8;
+  v8_t<T> ppre[C::P_VECS];
+  // Classify chunk k: 0 = not needed (no window that uses it has bias),
+  // 1 = zeros (all its distances are >= E but a window with bias may use it),
+  // 2 = load from P_cols.  Distances < 0 only meet causally masked keys.
+  auto chunk_kind = [&](int k) {
+    const int lo = k * N;
+    if (E == 0 || lo + N <= 0 || lo >= E + 2 * N) return 0;
+    return lo >= E ? 1 : 2;
+  };
+  auto fetch_p = [&](int k) {
+#pragma unroll
+    for (int i = 0; i < C::P_VECS; ++i) {
+      const int vid = tid + i * C::THREADS;
+      const int d = k * N + (vid >> 4);
+      const int c8 = vid & 15;
+      const bool ok = d >= 0 && d < E && c8 < vec_per_row;
+      const v8_t<T> x = ld8<T>(pcg + size_t(min(max(d, 0), E - 1)) * d_r + 8 * min(c8, vec_per_row - 1));
+      ppre[i] = ok ? x : zero8<T>();
+    }
+  };
+  auto store_p = [&](int k, bool zeros) {
+    T* base = Pr + size_t(k & (C::RING - 1)) * N * C::PS;
+#pragma unroll
+    for (int i = 0; i < C::P_VECS; ++i) {
+      const int vid = tid + i * C::THREADS;
+      if ((vid & 15) < vec_per_row) st8<T>(base + (vid >> 4) * C::PS + (vid & 15) * 8, zeros ? zero8<T>() : ppre[i]);
+    }
+  };
+
+  // ---- prologue: first tile and its P window
+  {
+    fetch_kv(kt_lo);
+    const int kc = (i0 - kt_lo * N) / N;  // D0 / N
+    for (int k = kc - 1; k < kc - 1 + C::WIN; ++k) {
+      const int kind = chunk_kind(k);
+      if (kind == 2) fetch_p(k);
+      if (kind != 0) store_p(k, kind == 1);
+    }
+    store_kv();
+  }
+
+  const int ring_base_stride = N * C::PS;
+  float* rs = Rs + w * 32 * C::LS;
+
+  for (int kt = kt_lo; kt <= kt_hi; ++kt) {
+    const int j0 = kt * N;
+    const int D0 = i0 - j0;  // distance between the first query and the first key of the tile
+    __syncthreads();          // tile kt (K, V, P window) is in LDS
+
+    // prefetch tile kt+1 and the one new P chunk its window needs
+    const bool more = kt < kt_hi;
+    const int knew = D0 / N - 2;  // lowest chunk of the next window
+    const int kind_new = more ? chunk_kind(knew) : 0;
+    if (more) {
+      fetch_kv(kt + 1);
+      if (kind_new == 2) fetch_p(knew);
+    }
 
     // ---- per-wave work on the (32 queries) x (N keys) sub-tile
     const bool wdead = qw0 >= T_ || j0 > qw0 + 31 || (W > 0 && qw0 - (j0 + N - 1) >= W);
-    if (wdead) continue;
-    const bool wband = E > 0 && max(0, qw0 - (j0 + N - 1)) < E;
-    const bool wmask = (j0 + N - 1 > qw0) || (W > 0 && qw0 + 31 - j0 >= W);
+    if (!wdead) {
+      const bool wband = E > 0 && max(0, qw0 - (j0 + N - 1)) < E;
+      const bool wmask = (j0 + N - 1 > qw0) || (W > 0 && qw0 + 31 - j0 >= W);
 
-    // S^T = K Q^T
-    f32x16 s[NB];
+      if (wband) {
+        // R^T for this wave's distances [Dw - N, Dw + 32): window rows
+        // 32*w + 32*rb + (0..31), window row rho = chunk (D0/N - 1 + rho/N), row rho%N
 #pragma unroll
-    for (int nb = 0; nb < NB; ++nb) {
-      s[nb] = zero16();
-      const T* krow = Ks + (nb * 32 + a) * C::KS + 8 * h2;
+        for (int rb = 0; rb <= NB; ++rb) {
+          const int rho0 = 32 * w + 32 * rb;
+          const int k = D0 / N - 1 + rho0 / N;
+          const T* prow_l = Pr + (k & (C::RING - 1)) * ring_base_stride + (rho0 % N + a) * C::PS + 8 * h2;
+          f32x16 racc = zero16();
 #pragma unroll
-      for (int kk = 0; kk < D / 16; ++kk) mma32(ld8<T>(krow + kk * 16), qreg[kk], s[nb]);
-    }
-
-    // logits in base 2: t = c1 * q.k (+ c2 * r.P on the sheared distance)
+          for (int kk = 0; kk < kMaxDr / 16; ++kk)
+            if (kk < nkr) mma32(ld8<T>(prow_l + kk * 16), rreg[kk], racc);
+          float* dst = rs + a * C::LS + rb * 32 + 4 * h2;
 #pragma unroll
-    for (int nb = 0; nb < NB; ++nb)
-#pragma unroll
-      for (int v = 0; v < 16; ++v) s[nb][v] *= p.c1;
-
-    if (wband) {
-      // R^T for this wave's N+32 distances: rows 32*w + rb*32 + (0..31) of the P slice
-#pragma unroll
-      for (int rb = 0; rb <= NB; ++rb) {
-        f32x16 racc = zero16();
-        const T* prow = Pt + (32 * w + rb * 32 + a) * PS + 8 * h2;
-#pragma unroll
-        for (int kk = 0; kk < kMaxDr / 16; ++kk)
-          if (kk < nkr) mma32(ld8<T>(prow + kk * 16), rreg[kk], racc);
-        float* dst = rs + a * C::LS + rb * 32 + 4 * h2;
-#pragma unroll
-        for (int g4 = 0; g4 < 4; ++g4) {
-          f32x4 x;
-          x[0] = racc[4 * g4 + 0] * p.c2;
-          x[1] = racc[4 * g4 + 1] * p.c2;
-          x[2] = racc[4 * g4 + 2] * p.c2;
-          x[3] = racc[4 * g4 + 3] * p.c2;
-          *reinterpret_cast<f32x4*>(dst + g4 * 8) = x;
+          for (int g4 = 0; g4 < 4; ++g4) {
+            f32x4 x;
+            x[0] = racc[4 * g4 + 0];
+            x[1] = racc[4 * g4 + 1];
+            x[2] = racc[4 * g4 + 2];
+            x[3] = racc[4 * g4 + 3];
+            *reinterpret_cast<f32x4*>(dst + g4 * 8) = x;
+          }
         }
+        wave_lds_fence();
       }
-      wave_lds_fence();
-      // key b of accumulator (nb, v): nb*32 + 8*(v/4) + 4*h2 + v%4; its distance column is a - b + N
-      const float* src = rs + a * C::LS + a + N - 4 * h2;
+
+      // S^T = K Q^T
+      f32x16 s[NB];
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) {
+        s[nb] = zero16();
+        const T* krow = Ks + (nb * 32 + a) * C::KS + 8 * h2;
+#pragma unroll
+        for (int kk = 0; kk < D / 16; ++kk) mma32(ld8<T>(krow + kk * 16), qreg[kk], s[nb]);
+      }
+
+      // y = S*(c1/c2) (+ R on the sheared distance): key b of accumulator
+      // (nb, v) is nb*32 + 8*(v/4) + 4*h2 + v%4, its distance column a - b + N
+      if (wband) {
+        const float* src = rs + a * C::LS + a + N - 4 * h2;
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+          for (int v = 0; v < 16; ++v) s[nb][v] = fmaf(s[nb][v], qk_scale, src[-(nb * 32 + 8 * (v >> 2) + (v & 3))]);
+        wave_lds_fence();
+      } else {
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+          for (int v = 0; v < 16; ++v) s[nb][v] *= qk_scale;
+      }
+
+      if (wmask) {
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+          for (int v = 0; v < 16; ++v) {
+            const int dd = qa - (j0 + nb * 32 + 8 * (v >> 2) + 4 * h2 + (v & 3));
+            if (dd < 0 || (W > 0 && dd >= W)) s[nb][v] = -INFINITY;
+          }
+      }
+
+      // online softmax (per query = per lane pair l, l^32)
+      float mx = -INFINITY;
 #pragma unroll
       for (int nb = 0; nb < NB; ++nb)
 #pragma unroll
-        for (int v = 0; v < 16; ++v) s[nb][v] += src[-(nb * 32 + 8 * (v >> 2) + (v & 3))];
-      wave_lds_fence();
-    }
-
-    if (wmask) {
+        for (int v = 0; v < 16; ++v) mx = fmaxf(mx, s[nb][v]);
+      mx = fmaxf(mx, xor_lane(mx, 32));
+      if (__builtin_amdgcn_ballot_w64(mx > m_run + lazy) != 0) {
+        const float m_new = fmaxf(m_run, mx);
+        const float corr = fast_exp2(p.c2 * (m_run - m_new));
+        m_run = m_new;
+        l_run *= corr;
+#pragma unroll
+        for (int i = 0; i < D / 32; ++i)
+#pragma unroll
+          for (int v = 0; v < 16; ++v) o[i][v] *= corr;
+      }
+      const float nm = -p.c2 * m_run;
+      float psum = 0.0f;
 #pragma unroll
       for (int nb = 0; nb < NB; ++nb)
 #pragma unroll
         for (int v = 0; v < 16; ++v) {
-          const int j = j0 + nb * 32 + 8 * (v >> 2) + 4 * h2 + (v & 3);
-          const int dd = qa - j;
-          const bool vis = dd >= 0 && (W == 0 || dd < W);
-          if (!vis) s[nb][v] = -INFINITY;
+          const float e = fast_exp2(fmaf(s[nb][v], p.c2, nm));
+          s[nb][v] = e;
+          psum += e;
         }
+      l_run += psum;
+
+      // O^T += V^T P^T
+#pragma unroll
+      for (int c16 = 0; c16 < N / 16; ++c16) {
+        v8_t<T> pb;
+#pragma unroll
+        for (int t = 0; t < 8; ++t) pb[t] = T(s[c16 >> 1][8 * (c16 & 1) + t]);
+#pragma unroll
+        for (int db = 0; db < D / 32; ++db) mma32(VS::frag(Vs, c16, db, lane), pb, o[db]);
+      }
     }
 
-    // online softmax (per query = per lane pair l, l^32)
-    float mx = -INFINITY;
-#pragma unroll
-    for (int nb = 0; nb < NB; ++nb)
-#pragma unroll
-      for (int v = 0; v < 16; ++v) mx = fmaxf(mx, s[nb][v]);
-    mx = fmaxf(mx, xor_lane(mx, 32));
-    const float m_new = fmaxf(m_run, mx);
-    const float m_use = (m_new == -INFINITY) ? 0.0f : m_new;
-    const float corr = fast_exp2(m_run - m_use);
-    m_run = m_new;
-    float psum = 0.0f;
-#pragma unroll
-    for (int nb = 0; nb < NB; ++nb)
-#pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        const float e = fast_exp2(s[nb][v] - m_use);
-        s[nb][v] = e;
-        psum += e;
-      }
-    l_run = l_run * corr + psum;
-#pragma unroll
-    for (int i = 0; i < D / 32; ++i)
-#pragma unroll
-      for (int v = 0; v < 16; ++v) o[i][v] *= corr;
-
-    // O^T += V^T P^T
-#pragma unroll
-    for (int c16 = 0; c16 < N / 16; ++c16) {
-      v8_t<T> pb;
-#pragma unroll
-      for (int t = 0; t < 8; ++t) pb[t] = T(s[c16 >> 1][8 * (c16 & 1) + t]);
-#pragma unroll
-      for (int db = 0; db < D / 32; ++db)
-        mma32(ld8<T>(Vt + (db * 32 + a) * C::VS + c16 * 16 + 8 * h2), pb, o[db]);
+    __syncthreads();  // every wave is done with tile kt's K and V
+    if (more) {
+      store_kv();
+      if (kind_new != 0) store_p(knew, kind_new == 1);
     }
   }
 
@@ -318,7 +423,7 @@ __global__ __launch_bounds__(WAVES * 64, 1) void prefill_kernel(PrefillArgs p, i
     for (int g4 = 0; g4 < 4; ++g4)
       st4_f32<T>(orow + db * 32 + g4 * 8 + 4 * h2, o[db][4 * g4] * inv, o[db][4 * g4 + 1] * inv,
                  o[db][4 * g4 + 2] * inv, o[db][4 * g4 + 3] * inv);
-  if (p.lse != nullptr && h2 == 0) p.lse[(size_t(b) * Hq + h) * T_ + qa] = (m_run + log2f(l_tot)) * kLn2;
+  if (p.lse != nullptr && h2 == 0) p.lse[(size_t(b) * Hq + h) * T_ + qa] = (p.c2 * m_run + log2f(l_tot)) * kLn2;
 }
 
 template <typename T, int WAVES, int N>
@@ -337,7 +442,7 @@ hipError_t launch_prefill_t(const PrefillArgs& a, hipStream_t stream) {
 }  // namespace
 
 hipError_t launch_prefill(int dtype, const PrefillArgs& a, hipStream_t stream) {
-  if (dtype == 1) return launch_prefill_t<__bf16, 4, 64>(a, stream);
+  if (dtype == 1) return launch_prefill_t<__bf16, 4, 32>(a, stream);
   return launch_prefill_t<float, 2, 32>(a, stream);
 }
 

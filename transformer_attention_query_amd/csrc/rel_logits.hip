@@ -14,8 +14,8 @@ namespace relattn {
 namespace {
 
 constexpr int kRlWaves = 4;
-constexpr int kRlRows = 32 * kRlWaves;  // rows per workgroup
-constexpr int kRlCols = 128;            // distances per workgroup
+constexpr int kRlRows = 32;             // rows per workgroup
+constexpr int kRlCols = 32 * kRlWaves;  // output columns per workgroup (32 per wave)
 
 template <typename T>
 __global__ __launch_bounds__(kRlWaves * 64) void rel_logits_kernel(RelLogitsArgs p) {
@@ -27,34 +27,27 @@ __global__ __launch_bounds__(kRlWaves * 64) void rel_logits_kernel(RelLogitsArgs
   const int d_r = p.d_r, E = p.E;
   const int nk = d_r / 16;
 
-  const long long row0 = (long long)blockIdx.x * kRlRows + 32 * w;
-  const int col0 = blockIdx.y * kRlCols;
+  const long long row0 = (long long)blockIdx.x * kRlRows;
+  const int col = blockIdx.y * kRlCols + 32 * w + a;  // this lane's output column (B-operand column)
   const T* rg = static_cast<const T*>(p.r);
   const T* pcg = static_cast<const T*>(p.pc);
 
   const long long arow = row0 + a;
-  const bool aok = arow < p.n_rows;
-  v8_t<T> areg[kMaxDr / 16];
+  const bool aok = arow < p.n_rows && E > 0;
+  const int d = p.rev_base > 0 ? p.rev_base - 1 - col : col;
+  const bool bok = d >= 0 && d < E;
+  const T* arow_p = rg + (aok ? arow : 0) * d_r + 8 * h2;
+  const T* prow = pcg + size_t(bok ? d : 0) * d_r + 8 * h2;
+  f32x16 acc = zero16();
 #pragma unroll
   for (int kk = 0; kk < kMaxDr / 16; ++kk)
-    areg[kk] = ld8_or_zero<T>(rg + (aok ? arow : 0) * d_r + kk * 16 + 8 * h2, aok && kk < nk);
-
+    if (kk < nk) mma32(ld8_or_zero<T>(arow_p + kk * 16, aok), ld8_or_zero<T>(prow + kk * 16, bok), acc);
+  // accumulator v of lane (h2, a): row 8*(v/4) + 4*h2 + v%4, column a
+  if (col < p.out_cols) {
 #pragma unroll
-  for (int cb = 0; cb < kRlCols / 32; ++cb) {
-    const int col = col0 + cb * 32 + a;
-    const bool bok = col < E;
-    const T* prow = pcg + size_t(bok ? col : 0) * d_r + 8 * h2;
-    f32x16 acc = zero16();
-#pragma unroll
-    for (int kk = 0; kk < kMaxDr / 16; ++kk)
-      if (kk < nk) mma32(areg[kk], ld8_or_zero<T>(prow + kk * 16, bok), acc);
-    // accumulator v of lane (h2, a): row 8*(v/4) + 4*h2 + v%4, column a
-    if (bok) {
-#pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        const long long row = row0 + 8 * (v >> 2) + 4 * h2 + (v & 3);
-        if (row < p.n_rows) p.out[row * E + col] = acc[v] * p.s;
-      }
+    for (int v = 0; v < 16; ++v) {
+      const long long row = row0 + 8 * (v >> 2) + 4 * h2 + (v & 3);
+      if (row < p.n_rows) p.out[row * p.out_stride + col] = acc[v] * p.s;
     }
   }
 }
@@ -62,7 +55,7 @@ __global__ __launch_bounds__(kRlWaves * 64) void rel_logits_kernel(RelLogitsArgs
 template <typename T>
 hipError_t launch_rel_logits_t(const RelLogitsArgs& a, hipStream_t stream) {
   const long long gx = (a.n_rows + kRlRows - 1) / kRlRows;
-  const int gy = (a.E + kRlCols - 1) / kRlCols;
+  const int gy = (a.out_cols + kRlCols - 1) / kRlCols;
   if (gx > 0x7fffffffLL || gy > 65535) return hipErrorInvalidConfiguration;
   hipLaunchKernelGGL(rel_logits_kernel<T>, dim3((unsigned)gx, (unsigned)gy), dim3(kRlWaves * 64), 0, stream, a);
   return hipGetLastError();

@@ -35,15 +35,21 @@ struct DecodeArgs {
   const void* pc;
   void* out;
   float* lse;       // may be null
-  float* ws;        // workspace base (float)
+  float* ws;        // workspace base (float): split partials, then bias rows
+  const float* rl;  // bias rows inside the workspace (any valid address when E == 0)
   int B, L, Hq, Hkv, d_r, E, W;
   float c1, c2;
   int n_split;      // splits of the visible key range
   int chunk;        // keys per split (multiple of 32)
   int kv_lo;        // first visible key (L - W for a window, else 0)
   int n_hg;         // groups of 16 query heads per kv head
+  int rl_base;      // key j reads bias row entry j - L + rl_base
+  int rl_stride;    // floats per bias row
 };
 
+// out[row * out_stride + oc] = s * r[row] . P_cols[d(oc)] for oc < out_cols,
+// with d(oc) = oc, or d(oc) = rev_base - 1 - oc when rev_base > 0; entries
+// whose d falls outside [0, E) are written as 0.
 struct RelLogitsArgs {
   const void* r;
   const void* pc;
@@ -51,6 +57,7 @@ struct RelLogitsArgs {
   long long n_rows;  // n_tok * H
   int d_r, E;
   float s;
+  int out_cols, out_stride, rev_base;
 };
 
 // Decode planning shared by rel_attn_decode_plan and rel_attn_decode.
@@ -59,9 +66,12 @@ struct DecodePlan {
   int chunk;
   int kv_lo;
   int n_hg;
-  size_t ws_bytes;
+  int rl_base;
+  int rl_stride;
+  size_t ws_partial_bytes;  // split partials (o, m, l)
+  size_t ws_bytes;          // total, bias rows included
 };
-DecodePlan plan_decode(int B, int L, int Hq, int Hkv, int num_splits_req, int window);
+DecodePlan plan_decode(int B, int L, int Hq, int Hkv, int num_splits_req, int window, int rel_extent);
 
 // Launchers: return hipSuccess or the launch error.  dtype: 1 = bf16, 2 = fp32.
 hipError_t launch_prefill(int dtype, const PrefillArgs& a, hipStream_t stream);
