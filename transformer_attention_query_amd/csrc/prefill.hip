@@ -22,14 +22,16 @@
 //     too and read as MFMA fragments with the gfx950 transpose read
 //     (ds_read_b64_tr_b16); fp32 V tiles are stored transposed.
 //   * Relative bias ("sheared bias" of section "Relative Logits
-//     Optimization": bias(i,j) = rel_logits(i, i-j)) is formed per wave: the
-//     wave's (32 queries x N keys) tile needs distances [Dw - N + 1, Dw + 31]
-//     (Dw = its first query minus the tile's first key); it computes
-//     R^T = P_rows r^T for the N+32 distances [Dw - N, Dw + 32) with MFMA,
-//     writes R to a wave-private LDS buffer indexed [query][distance] and reads
-//     it back along the shear (row a, column a - b + N for key b): a lane only
-//     reads its own query's row.  Distances outside [0, E) read zero P rows,
-//     so the rel_extent cut needs no per-score test.
+//     Optimization": bias(i,j) = rel_logits(i, i-j)) is formed per wave.  The
+//     wave's queries start Dw = 32c keys after the tile's first key, so query
+//     a and key b are 32c + a - b apart: distance chunks c-1 (a < b) and c
+//     (a >= b), 32 distances each.  Chunk c was made on the previous key tile;
+//     only chunk c-1 is new: R^T = P_rows r^T over its 32 distances, one MFMA
+//     chain the length of the QK chain.  R goes to a wave-private LDS buffer
+//     [query][distance] (two chunk slots, even chunks also in a third so the
+//     pair is always contiguous) and is read back along the shear: a lane
+//     only reads its own query's row.  Distances outside [0, E) read zero P
+//     rows, so the rel_extent cut needs no per-score test.
 //   * P rows live in a ring of N-row chunks in LDS.  A tile's window of
 //     distances [D0 - N, D0 + M) is M/N + 1 consecutive chunks (D0 = first
 //     query minus first key); moving one tile right slides the window down by
@@ -41,6 +43,8 @@
 //     rows need no scaling, and p = exp2(c2*y - c2*m).  O is rescaled only
 //     when a row maximum grows by more than 2^8 (exact either way: O and l
 //     share the stale maximum).
+#include <climits>
+
 #include "device_common.hpp"
 #include "relattn_internal.hpp"
 
@@ -110,7 +114,7 @@ struct PrefillCfg {
   static constexpr int PS = kMaxDr + PAD;     // P ring row stride (elements)
   static constexpr int WIN = M / N + 1;       // P chunks in a tile's window
   static constexpr int RING = WIN < 4 ? 4 : 8;  // P chunk slots: a power of two > WIN
-  static constexpr int LS = N + 36;           // R buffer row stride (floats)
+  static constexpr int LS = 100;              // R buffer row stride (floats): 96 columns + 4
   static constexpr int THREADS = WAVES * 64;
   static constexpr int KV_VECS = N * (kHeadDim / 8) / THREADS;  // 8-element vectors per thread per tile
   static constexpr int P_VECS = N * (kMaxDr / 8) / THREADS;     // per thread per P chunk (d_r = 128)
@@ -132,6 +136,7 @@ __global__ __launch_bounds__(WAVES * 64, 1) void prefill_kernel(PrefillArgs p, i
   using VS = PreV<T, N>;
   constexpr int M = C::M, NB = C::NB;
   constexpr int D = kHeadDim;
+  static_assert(N == 32, "one 32-distance chunk of relative logits per key tile");
 
   __shared__ __attribute__((aligned(16))) unsigned char smem[C::LDS_TOTAL];
   T* Ks = reinterpret_cast<T*>(smem);
@@ -175,7 +180,8 @@ __global__ __launch_bounds__(WAVES * 64, 1) void prefill_kernel(PrefillArgs p, i
   const T* kg = static_cast<const T*>(p.k);
   const T* vg = static_cast<const T*>(p.v);
   const T* rg = static_cast<const T*>(p.r);
-  const T* pcg = static_cast<const T*>(p.pc);
+  // P_cols, or any valid address when there is no bias (its loads are then discarded)
+  const T* pcg = E > 0 ? static_cast<const T*>(p.pc) : kg;
 
   // softmax constants in units of c2 (c2 = s*log2(e) > 0)
   const float qk_scale = p.c1 / p.c2;
@@ -240,6 +246,7 @@ __global__ __launch_bounds__(WAVES * 64, 1) void prefill_kernel(PrefillArgs p, i
   // when 8*(vid%16) < d_r).
   const int vec_per_row = d_r / 8;
   v8_t<T> ppre[C::P_VECS];
+  unsigned pok = 0;  // bit i: vector i of the pending chunk holds P values (else zeros)
   // Classify chunk k: 0 = not needed (no window that uses it has bias),
   // 1 = zeros (all its distances are >= E but a window with bias may use it),
   // 2 = load from P_cols.  Distances < 0 only meet causally masked keys.
@@ -248,23 +255,29 @@ __global__ __launch_bounds__(WAVES * 64, 1) void prefill_kernel(PrefillArgs p, i
     if (E == 0 || lo + N <= 0 || lo >= E + 2 * N) return 0;
     return lo >= E ? 1 : 2;
   };
+  // Loads are issued unconditionally from clamped addresses and the zero fill
+  // is applied when the chunk is stored, so the loads stay in flight until
+  // then (a select at the load would wait for it there).
   auto fetch_p = [&](int k) {
+    pok = 0;
 #pragma unroll
     for (int i = 0; i < C::P_VECS; ++i) {
       const int vid = tid + i * C::THREADS;
       const int d = k * N + (vid >> 4);
       const int c8 = vid & 15;
-      const bool ok = d >= 0 && d < E && c8 < vec_per_row;
-      const v8_t<T> x = ld8<T>(pcg + size_t(min(max(d, 0), E - 1)) * d_r + 8 * min(c8, vec_per_row - 1));
-      ppre[i] = ok ? x : zero8<T>();
+      pok |= unsigned(d >= 0 && d < E && c8 < vec_per_row) << i;
+      ppre[i] = ld8<T>(pcg + size_t(min(max(d, 0), max(E - 1, 0))) * d_r + 8 * min(c8, vec_per_row - 1));
     }
   };
+  // every column of the slot is written, zeros past d_r, so the R^T MFMAs can
+  // always run all kMaxDr/16 k-steps
   auto store_p = [&](int k, bool zeros) {
     T* base = Pr + size_t(k & (C::RING - 1)) * N * C::PS;
 #pragma unroll
     for (int i = 0; i < C::P_VECS; ++i) {
       const int vid = tid + i * C::THREADS;
-      if ((vid & 15) < vec_per_row) st8<T>(base + (vid >> 4) * C::PS + (vid & 15) * 8, zeros ? zero8<T>() : ppre[i]);
+      const bool ok = !zeros && ((pok >> i) & 1u);
+      st8<T>(base + (vid >> 4) * C::PS + (vid & 15) * 8, ok ? ppre[i] : zero8<T>());
     }
   };
 
@@ -274,14 +287,19 @@ __global__ __launch_bounds__(WAVES * 64, 1) void prefill_kernel(PrefillArgs p, i
     const int kc = (i0 - kt_lo * N) / N;  // D0 / N
     for (int k = kc - 1; k < kc - 1 + C::WIN; ++k) {
       const int kind = chunk_kind(k);
-      if (kind == 2) fetch_p(k);
+      fetch_p(k);
       if (kind != 0) store_p(k, kind == 1);
     }
     store_kv();
   }
 
   const int ring_base_stride = N * C::PS;
+  // Per-wave buffer of relative logits R(a, d) of this wave's queries, by
+  // distance chunk: chunk k (distances 32k .. 32k+31) at columns 32*(k&1),
+  // even chunks also at 64..95, so that chunks k-1 and k are always 64
+  // contiguous columns.
   float* rs = Rs + w * 32 * C::LS;
+  int rlast = INT_MIN;  // the newest chunk in the buffer (the one before it is there too)
 
   for (int kt = kt_lo; kt <= kt_hi; ++kt) {
     const int j0 = kt * N;
@@ -292,10 +310,8 @@ __global__ __launch_bounds__(WAVES * 64, 1) void prefill_kernel(PrefillArgs p, i
     const bool more = kt < kt_hi;
     const int knew = D0 / N - 2;  // lowest chunk of the next window
     const int kind_new = more ? chunk_kind(knew) : 0;
-    if (more) {
-      fetch_kv(kt + 1);
-      if (kind_new == 2) fetch_p(knew);
-    }
+    fetch_kv(more ? kt + 1 : kt);
+    fetch_p(knew);
 
     // ---- per-wave work on the (32 queries) x (N keys) sub-tile
     const bool wdead = qw0 >= T_ || j0 > qw0 + 31 || (W > 0 && qw0 - (j0 + N - 1) >= W);
@@ -303,56 +319,76 @@ __global__ __launch_bounds__(WAVES * 64, 1) void prefill_kernel(PrefillArgs p, i
       const bool wband = E > 0 && max(0, qw0 - (j0 + N - 1)) < E;
       const bool wmask = (j0 + N - 1 > qw0) || (W > 0 && qw0 + 31 - j0 >= W);
 
-      if (wband) {
-        // R^T for this wave's distances [Dw - N, Dw + 32): window rows
-        // 32*w + 32*rb + (0..31), window row rho = chunk (D0/N - 1 + rho/N), row rho%N
-#pragma unroll
-        for (int rb = 0; rb <= NB; ++rb) {
-          const int rho0 = 32 * w + 32 * rb;
-          const int k = D0 / N - 1 + rho0 / N;
-          const T* prow_l = Pr + (k & (C::RING - 1)) * ring_base_stride + (rho0 % N + a) * C::PS + 8 * h2;
-          f32x16 racc = zero16();
-#pragma unroll
-          for (int kk = 0; kk < kMaxDr / 16; ++kk)
-            if (kk < nkr) mma32(ld8<T>(prow_l + kk * 16), rreg[kk], racc);
-          float* dst = rs + a * C::LS + rb * 32 + 4 * h2;
-#pragma unroll
-          for (int g4 = 0; g4 < 4; ++g4) {
-            f32x4 x;
-            x[0] = racc[4 * g4 + 0];
-            x[1] = racc[4 * g4 + 1];
-            x[2] = racc[4 * g4 + 2];
-            x[3] = racc[4 * g4 + 3];
-            *reinterpret_cast<f32x4*>(dst + g4 * 8) = x;
-          }
-        }
-        wave_lds_fence();
-      }
-
-      // S^T = K Q^T
-      f32x16 s[NB];
+      // Scores S^T = K Q^T as two interleaved accumulators (even / odd
+      // k-steps) and, on tiles with bias, the R^T blocks = P_rows r^T for
+      // this wave's distances [Dw - N, Dw + 32): window rows 32*w + 32*rb +
+      // (0..31); window row rho lives in chunk D0/N - 1 + rho/N, row rho%N.
+      // Independent chains keep the matrix cores busy with one wave per SIMD.
+      f32x16 s[NB], s_odd[NB];
 #pragma unroll
       for (int nb = 0; nb < NB; ++nb) {
         s[nb] = zero16();
-        const T* krow = Ks + (nb * 32 + a) * C::KS + 8 * h2;
-#pragma unroll
-        for (int kk = 0; kk < D / 16; ++kk) mma32(ld8<T>(krow + kk * 16), qreg[kk], s[nb]);
+        s_odd[nb] = zero16();
       }
-
-      // y = S*(c1/c2) (+ R on the sheared distance): key b of accumulator
-      // (nb, v) is nb*32 + 8*(v/4) + 4*h2 + v%4, its distance column a - b + N
+      auto qk_step = [&](int kk) {
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb) {
+          const v8_t<T> kf = ld8<T>(Ks + (nb * 32 + a) * C::KS + 8 * h2 + kk * 16);
+          if (kk & 1) mma32(kf, qreg[kk], s_odd[nb]);
+          else mma32(kf, qreg[kk], s[nb]);
+        }
+      };
       if (wband) {
-        const float* src = rs + a * C::LS + a + N - 4 * h2;
+        // Keys b of this tile sit at distance 32c + a - b from query a, in
+        // chunks c-1 (a < b) and c (a >= b).  Chunk c was made on the previous
+        // tile; chunk c-1 is new: R^T = P_rows r^T over its 32 distances.
+        const int c = D0 / N + w;
+        auto prow = [&](int k) { return Pr + (k & (C::RING - 1)) * ring_base_stride + a * C::PS + 8 * h2; };
+        auto write_chunk = [&](int k, const f32x16& acc) {
+          float* dst = rs + a * C::LS + 32 * (k & 1) + 4 * h2;
 #pragma unroll
-        for (int nb = 0; nb < NB; ++nb)
+          for (int g4 = 0; g4 < 4; ++g4) {
+            f32x4 x;
+            x[0] = acc[4 * g4 + 0];
+            x[1] = acc[4 * g4 + 1];
+            x[2] = acc[4 * g4 + 2];
+            x[3] = acc[4 * g4 + 3];
+            *reinterpret_cast<f32x4*>(dst + g4 * 8) = x;
+            if ((k & 1) == 0) *reinterpret_cast<f32x4*>(dst + 64 + g4 * 8) = x;
+          }
+        };
+        if (rlast != c) {  // first tile with bias for this wave
+          f32x16 rc = zero16();
+          const T* pr = prow(c);
 #pragma unroll
-          for (int v = 0; v < 16; ++v) s[nb][v] = fmaf(s[nb][v], qk_scale, src[-(nb * 32 + 8 * (v >> 2) + (v & 3))]);
+          for (int kk = 0; kk < kMaxDr / 16; ++kk) mma32(ld8<T>(pr + kk * 16), rreg[kk], rc);
+          write_chunk(c, rc);
+        }
+        f32x16 racc = zero16();
+        {
+          const T* pr = prow(c - 1);
+#pragma unroll
+          for (int kk = 0; kk < kMaxDr / 16; ++kk) {
+            mma32(ld8<T>(Ks + a * C::KS + 8 * h2 + kk * 16), qreg[kk], s[0]);
+            mma32(ld8<T>(pr + kk * 16), rreg[kk], racc);
+          }
+        }
+        write_chunk(c - 1, racc);
+        rlast = c - 1;
+        wave_lds_fence();
+        // y = S*(c1/c2) + R(a, 32c + a - b): key b of accumulator v is
+        // 8*(v/4) + 4*h2 + v%4, at column 32*((c-1)&1) + 32 + a - b
+        const float* src = rs + a * C::LS + 32 * ((c - 1) & 1) + 32 + a - 4 * h2;
+#pragma unroll
+        for (int v = 0; v < 16; ++v) s[0][v] = fmaf(s[0][v], qk_scale, src[-(8 * (v >> 2) + (v & 3))]);
         wave_lds_fence();
       } else {
 #pragma unroll
+        for (int kk = 0; kk < D / 16; ++kk) qk_step(kk);
+#pragma unroll
         for (int nb = 0; nb < NB; ++nb)
 #pragma unroll
-          for (int v = 0; v < 16; ++v) s[nb][v] *= qk_scale;
+          for (int v = 0; v < 16; ++v) s[nb][v] = (s[nb][v] + s_odd[nb][v]) * qk_scale;
       }
 
       if (wmask) {
@@ -365,12 +401,22 @@ __global__ __launch_bounds__(WAVES * 64, 1) void prefill_kernel(PrefillArgs p, i
           }
       }
 
-      // online softmax (per query = per lane pair l, l^32)
+      // online softmax (per query = per lane pair l, l^32).  The exponentials
+      // are taken against the running maximum first; only when some row
+      // maximum grows by more than the lazy margin are O and l rescaled and
+      // the exponentials recomputed against the new maximum.
+      f32x16 pexp[NB];
       float mx = -INFINITY;
+      {
+        const float nm = -p.c2 * m_run;
 #pragma unroll
-      for (int nb = 0; nb < NB; ++nb)
+        for (int nb = 0; nb < NB; ++nb)
 #pragma unroll
-        for (int v = 0; v < 16; ++v) mx = fmaxf(mx, s[nb][v]);
+          for (int v = 0; v < 16; ++v) {
+            mx = fmaxf(mx, s[nb][v]);
+            pexp[nb][v] = fast_exp2(fmaf(s[nb][v], p.c2, nm));
+          }
+      }
       mx = fmaxf(mx, xor_lane(mx, 32));
       if (__builtin_amdgcn_ballot_w64(mx > m_run + lazy) != 0) {
         const float m_new = fmaxf(m_run, mx);
@@ -381,16 +427,19 @@ __global__ __launch_bounds__(WAVES * 64, 1) void prefill_kernel(PrefillArgs p, i
         for (int i = 0; i < D / 32; ++i)
 #pragma unroll
           for (int v = 0; v < 16; ++v) o[i][v] *= corr;
+        const float nm = -p.c2 * m_run;
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+          for (int v = 0; v < 16; ++v) pexp[nb][v] = fast_exp2(fmaf(s[nb][v], p.c2, nm));
       }
-      const float nm = -p.c2 * m_run;
       float psum = 0.0f;
 #pragma unroll
       for (int nb = 0; nb < NB; ++nb)
 #pragma unroll
         for (int v = 0; v < 16; ++v) {
-          const float e = fast_exp2(fmaf(s[nb][v], p.c2, nm));
-          s[nb][v] = e;
-          psum += e;
+          s[nb][v] = pexp[nb][v];
+          psum += pexp[nb][v];
         }
       l_run += psum;
 
@@ -427,23 +476,23 @@ __global__ __launch_bounds__(WAVES * 64, 1) void prefill_kernel(PrefillArgs p, i
 }
 
 template <typename T, int WAVES, int N>
-hipError_t launch_prefill_t(const PrefillArgs& a, hipStream_t stream) {
+hipError_t launch_prefill_tiles(const PrefillArgs& a, hipStream_t stream) {
   using C = PrefillCfg<T, WAVES, N>;
   const int n_qt = (a.T + C::M - 1) / C::M;
   const int G = a.Hq / a.Hkv;
   const long long n_groups = (long long)n_qt * a.B * a.Hkv;
   const long long grid = ((n_groups + 7) / 8) * 8 * G;
   if (grid > 0x7fffffffLL) return hipErrorInvalidConfiguration;
-  hipLaunchKernelGGL((prefill_kernel<T, WAVES, N>), dim3((unsigned)grid), dim3(C::THREADS), 0, stream, a, n_qt,
-                     (int)n_groups);
+  hipLaunchKernelGGL((prefill_kernel<T, WAVES, N>), dim3((unsigned)grid), dim3(C::THREADS), 0, stream, a,
+                     n_qt, (int)n_groups);
   return hipGetLastError();
 }
 
 }  // namespace
 
 hipError_t launch_prefill(int dtype, const PrefillArgs& a, hipStream_t stream) {
-  if (dtype == 1) return launch_prefill_t<__bf16, 4, 32>(a, stream);
-  return launch_prefill_t<float, 2, 32>(a, stream);
+  if (dtype == 1) return launch_prefill_tiles<__bf16, 4, 32>(a, stream);
+  return launch_prefill_tiles<float, 2, 32>(a, stream);
 }
 
 }  // namespace relattn
