@@ -8,6 +8,8 @@ sequences x 8192 keys (KV GB/s), each against its roofline, and the fp64 CPU
 oracle timed on a bounded sample of the prefill workload.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+       python bench.py --copy-calibration   (a plain 1 GiB device copy, for
+       scaling the HBM byte counters FETCH_SIZE / WRITE_SIZE under rocprofv3)
 """
 
 from __future__ import annotations
@@ -160,19 +162,35 @@ def cpu_baseline(target_s: float = 15.0):
     x = tinputs.make_inputs(w, seed=0)
     threads = torch.get_num_threads()
     stride_rows = lambda n: list(range(w.T - 1, -1, -max(1, w.T // n)))[:n]  # noqa: E731
-    # calibrate on a few rows, then run a sample sized for about target_s
+    run = lambda rows: oracle.prefill(x["q"], x["k"], x["v"], x["r"], x["P"], w.alpha, w.E, w.W,  # noqa: E731
+                                      w.log_scale, rows=rows)
+    # warm up, calibrate on 64 rows, then run a sample sized for about target_s
+    run(stride_rows(8))
     t = time.perf_counter()
-    oracle.prefill(x["q"], x["k"], x["v"], x["r"], x["P"], w.alpha, w.E, w.W, w.log_scale, rows=stride_rows(8))
-    per_row = (time.perf_counter() - t) / 8
-    n = int(max(8, min(w.T, target_s / max(per_row, 1e-6))))
+    run(stride_rows(64))
+    per_row = (time.perf_counter() - t) / 64
+    n = int(max(64, min(w.T, target_s / max(per_row, 1e-6))))
     rows = stride_rows(n)
     t = time.perf_counter()
-    oracle.prefill(x["q"], x["k"], x["v"], x["r"], x["P"], w.alpha, w.E, w.W, w.log_scale, rows=rows)
+    run(rows)
     dt = time.perf_counter() - t
     flops, _, _ = prefill_work(w.T, w.Hq, w.D, w.d_r, w.E, w.W, rows=rows)
     return {"value": flops * w.B / dt / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
             "sample": f"{len(rows)} of {w.T} query rows (all {w.Hq} heads, evenly spaced) of {w.name}, "
                       f"fp64 torch-CPU oracle, {dt:.1f} s wall"}
+
+
+def copy_calibration(nbytes: int = 1 << 30, reps: int = 3):
+    """A plain device-to-device copy of known size: it reads and writes
+    nbytes each, so the counters it produces give the factor between counter
+    readings and bytes."""
+    import torch
+    src = torch.empty(nbytes, dtype=torch.uint8, device="cuda").fill_(1)
+    dst = torch.empty_like(src)
+    for _ in range(reps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes": nbytes, "reps": reps}), flush=True)
 
 
 def main():
@@ -182,6 +200,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU only: the relative-attention kernels run on a single MI355X "
@@ -194,6 +213,9 @@ def main():
     if not torch.cuda.is_available():
         print("no GPU visible", file=sys.stderr)
         sys.exit(1)
+    if args.copy_calibration:
+        copy_calibration()
+        return
 
     w, flops, ms_step, kernel_ms, per = bench_prefill(args.steps, args.warmup)
     print(f"# prefill {w.name}: {ms_step * 1e3:.1f} us/step, kernel {kernel_ms * 1e3:.1f} us "

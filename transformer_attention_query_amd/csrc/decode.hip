@@ -6,21 +6,28 @@
 // single query i = L-1 the bias of key j is s * r.P[:, L-1-j] when
 // L-1-j < E.  The visible keys (all of them, or the last `window`) are cut
 // into num_splits contiguous chunks (the split-KV "num_splits" of the vLLM
-// page, section on the sheared-bias FA4 kernel); each wave owns one
-// (sequence, kv head, group of up to 16 query heads, split) and streams its
-// chunk of K and V exactly once for every query head of the group.  The
+// page, section on the sheared-bias FA4 kernel); each workgroup owns one
+// (sequence, split, kv head, group of up to 16 query heads), its waves take
+// interleaved 32-key steps, and it streams its chunk of K and V exactly once
+// for every query head of the group.  The
 // partial softmax states (unnormalised o, running max m, sum l) go to the
 // caller's workspace and a second kernel merges them by log-sum-exp.
 //
-// Per 32-key step a wave computes S^T = K Q^T with 16x16x32 MFMAs (rows =
-// keys, columns = query heads, padded to 16), adds the bias rows produced by
-// R^T = P_rows r^T where each lane's A-operand row is the P row of its own
-// key's distance (a single query needs no shear), applies the online softmax
-// and accumulates O^T = V^T P^T.  The wave keeps two 32-key steps of K and V
-// in flight in registers (ping-pong, no copies), so HBM latency overlaps the
-// previous step's work.  V goes through a wave-private LDS tile: bf16 tiles
-// are stored row-major and read as MFMA fragments with the gfx950 transpose
-// read (ds_read_b64_tr_b16); fp32 tiles are stored transposed.
+// Three launches on the caller's stream:
+//   1. rel_logits_kernel writes, per (sequence, query head), the bias row
+//      s * log2(e) * r.P[:, d] for the last E distances into the workspace,
+//      stored reversed so that key j reads entry j - L + rl_base and entries
+//      beyond E (and the padding) are zero: a single query needs no shear.
+//   2. decode_split_kernel: per 32-key step a wave computes S^T = K Q^T with
+//      16x16x32 MFMAs (rows = keys, columns = query heads, padded to 16),
+//      adds the bias entries of its keys (clamped 16-byte loads, no branch),
+//      applies the online softmax and accumulates O^T = V^T P^T.  The wave
+//      keeps two 32-key steps of K and V in flight in registers (ping-pong,
+//      no copies), so HBM latency overlaps the previous step's work.  V goes
+//      through a wave-private LDS tile: bf16 tiles are stored row-major and
+//      read as MFMA fragments with the gfx950 transpose read
+//      (ds_read_b64_tr_b16); fp32 tiles are stored transposed.
+//   3. decode_merge_kernel: log-sum-exp merge of the split partials.
 #include "device_common.hpp"
 #include "relattn_internal.hpp"
 
