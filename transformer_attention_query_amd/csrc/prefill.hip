@@ -105,16 +105,18 @@ template <int N> struct PreV<float, N> {
   }
 };
 
-template <typename T, int WAVES, int N>
+template <typename T, int WAVES>
 struct PrefillCfg {
+  static constexpr int N = 32;                // keys per tile = distances per chunk
   static constexpr int M = 32 * WAVES;        // queries per workgroup
-  static constexpr int NB = N / 32;           // 32-key blocks per tile
   static constexpr int PAD = 16 / sizeof(T);  // 16 bytes of padding per K / P row
   static constexpr int KS = kHeadDim + PAD;   // K tile row stride (elements)
   static constexpr int PS = kMaxDr + PAD;     // P ring row stride (elements)
-  static constexpr int WIN = M / N + 1;       // P chunks in a tile's window
-  static constexpr int RING = WIN < 4 ? 4 : 8;  // P chunk slots: a power of two > WIN
-  static constexpr int LS = 100;              // R buffer row stride (floats): 96 columns + 4
+  // A tile reads one new chunk per wave, WAVES consecutive chunks; the next
+  // tile's new chunk replaces the highest of them after the end-of-tile
+  // barrier, so the ring is exactly WAVES slots.
+  static constexpr int RING = WAVES;
+  static constexpr int LS = 2 * N + 4;        // R buffer row stride (floats): 64 columns + 4
   static constexpr int THREADS = WAVES * 64;
   static constexpr int KV_VECS = N * (kHeadDim / 8) / THREADS;  // 8-element vectors per thread per tile
   static constexpr int P_VECS = N * (kMaxDr / 8) / THREADS;     // per thread per P chunk (d_r = 128)
@@ -123,20 +125,18 @@ struct PrefillCfg {
   static constexpr size_t LDS_P = size_t(RING) * N * PS * sizeof(T);
   static constexpr size_t LDS_R = size_t(WAVES) * 32 * LS * sizeof(float);
   static constexpr size_t LDS_TOTAL = LDS_K + LDS_V + LDS_P + LDS_R;
-  static_assert(M % N == 0 && N % 32 == 0, "the P window must be whole chunks of whole blocks");
-  static_assert(WIN < RING && WIN <= 8, "the ring holds the window plus the chunk being filled");
-  static_assert(KV_VECS * THREADS == N * (kHeadDim / 8), "tile must split evenly over threads");
-  static_assert(P_VECS * THREADS == N * (kMaxDr / 8), "chunk must split evenly over threads");
+  static_assert((RING & (RING - 1)) == 0, "ring slots are chunk & (RING-1)");
+  static_assert(KV_VECS >= 1 && KV_VECS * THREADS == N * (kHeadDim / 8), "tile must split evenly over threads");
+  static_assert(P_VECS >= 1 && P_VECS * THREADS == N * (kMaxDr / 8), "chunk must split evenly over threads");
   static_assert(LDS_TOTAL <= 160 * 1024, "LDS budget of one gfx950 workgroup");
 };
 
-template <typename T, int WAVES, int N>
+template <typename T, int WAVES>
 __global__ __launch_bounds__(WAVES * 64, 1) void prefill_kernel(PrefillArgs p, int n_qt, int n_groups) {
-  using C = PrefillCfg<T, WAVES, N>;
-  using VS = PreV<T, N>;
-  constexpr int M = C::M, NB = C::NB;
+  using C = PrefillCfg<T, WAVES>;
+  using VS = PreV<T, C::N>;
+  constexpr int N = C::N, M = C::M;
   constexpr int D = kHeadDim;
-  static_assert(N == 32, "one 32-distance chunk of relative logits per key tile");
 
   __shared__ __attribute__((aligned(16))) unsigned char smem[C::LDS_TOTAL];
   T* Ks = reinterpret_cast<T*>(smem);
@@ -194,9 +194,9 @@ __global__ __launch_bounds__(WAVES * 64, 1) void prefill_kernel(PrefillArgs p, i
 #pragma unroll
     for (int kk = 0; kk < D / 16; ++kk) qreg[kk] = ld8_or_zero<T>(qrow + kk * 16, qvalid);
   }
-  v8_t<T> rreg[kMaxDr / 16];
-  const int nkr = d_r / 16;
+  v8_t<T> rreg[kMaxDr / 16];  // zero past d_r
   {
+    const int nkr = d_r / 16;
     const T* rrow = rg + ((size_t(b) * T_ + (qvalid ? qa : 0)) * Hq + h) * d_r + 8 * h2;
 #pragma unroll
     for (int kk = 0; kk < kMaxDr / 16; ++kk) rreg[kk] = ld8_or_zero<T>(rrow + kk * 16, E > 0 && qvalid && kk < nkr);
@@ -242,22 +242,14 @@ __global__ __launch_bounds__(WAVES * 64, 1) void prefill_kernel(PrefillArgs p, i
   };
 
   // P chunk k holds distances [k*N, k*N + N) in ring slot k mod RING.  Vector
-  // i of this thread covers chunk row vid/16, columns 8*(vid%16) .. +7 (used
-  // when 8*(vid%16) < d_r).
+  // i of this thread covers chunk row vid/16, columns 8*(vid%16) .. +7.
+  // Loads are issued unconditionally from clamped addresses and the zero fill
+  // (rows outside [0, E), columns past d_r) is applied when the chunk is
+  // stored, so the loads stay in flight until then.  Every column of a slot is
+  // written, so the R^T MFMAs always run all kMaxDr/16 k-steps.
   const int vec_per_row = d_r / 8;
   v8_t<T> ppre[C::P_VECS];
-  unsigned pok = 0;  // bit i: vector i of the pending chunk holds P values (else zeros)
-  // Classify chunk k: 0 = not needed (no window that uses it has bias),
-  // 1 = zeros (all its distances are >= E but a window with bias may use it),
-  // 2 = load from P_cols.  Distances < 0 only meet causally masked keys.
-  auto chunk_kind = [&](int k) {
-    const int lo = k * N;
-    if (E == 0 || lo + N <= 0 || lo >= E + 2 * N) return 0;
-    return lo >= E ? 1 : 2;
-  };
-  // Loads are issued unconditionally from clamped addresses and the zero fill
-  // is applied when the chunk is stored, so the loads stay in flight until
-  // then (a select at the load would wait for it there).
+  unsigned pok = 0;  // bit i: vector i of the pending chunk holds P values
   auto fetch_p = [&](int k) {
     pok = 0;
 #pragma unroll
@@ -269,153 +261,140 @@ __global__ __launch_bounds__(WAVES * 64, 1) void prefill_kernel(PrefillArgs p, i
       ppre[i] = ld8<T>(pcg + size_t(min(max(d, 0), max(E - 1, 0))) * d_r + 8 * min(c8, vec_per_row - 1));
     }
   };
-  // every column of the slot is written, zeros past d_r, so the R^T MFMAs can
-  // always run all kMaxDr/16 k-steps
-  auto store_p = [&](int k, bool zeros) {
+  auto store_p = [&](int k) {
     T* base = Pr + size_t(k & (C::RING - 1)) * N * C::PS;
 #pragma unroll
     for (int i = 0; i < C::P_VECS; ++i) {
       const int vid = tid + i * C::THREADS;
-      const bool ok = !zeros && ((pok >> i) & 1u);
-      st8<T>(base + (vid >> 4) * C::PS + (vid & 15) * 8, ok ? ppre[i] : zero8<T>());
+      st8<T>(base + (vid >> 4) * C::PS + (vid & 15) * 8, ((pok >> i) & 1u) ? ppre[i] : zero8<T>());
     }
   };
+  // A chunk is worth staging if some distance in it is below E.
+  auto chunk_needed = [&](int k) { return E > 0 && k * N < E && k * N + N > 0; };
 
-  // ---- prologue: first tile and its P window
+  // ---- prologue: first tile and the chunks its waves read
+  // Tile kt: the wave's first query is 32c keys after the tile's first key,
+  // c = (i0 - 32kt)/32 + w, so the tile's waves read chunks c0-1 .. c0+WAVES-2
+  // with c0 = (i0 - 32kt)/32.
   {
     fetch_kv(kt_lo);
-    const int kc = (i0 - kt_lo * N) / N;  // D0 / N
-    for (int k = kc - 1; k < kc - 1 + C::WIN; ++k) {
-      const int kind = chunk_kind(k);
+    const int c0 = (i0 - kt_lo * N) / N;
+    for (int k = c0 - 1; k < c0 - 1 + C::RING; ++k) {
       fetch_p(k);
-      if (kind != 0) store_p(k, kind == 1);
+      if (chunk_needed(k)) store_p(k);
     }
     store_kv();
   }
 
-  const int ring_base_stride = N * C::PS;
-  // Per-wave buffer of relative logits R(a, d) of this wave's queries, by
-  // distance chunk: chunk k (distances 32k .. 32k+31) at columns 32*(k&1),
-  // even chunks also at 64..95, so that chunks k-1 and k are always 64
-  // contiguous columns.
+  // Per-wave buffer of relative logits R(a, d) of this wave's queries for the
+  // tile's two chunks: chunk c-1 at columns 0..31, chunk c at 32..63, so key
+  // b of query a (distance 32c + a - b) is column 32 + a - b.  Chunk c was
+  // the new chunk of the previous tile and stays in registers (rprev).
   float* rs = Rs + w * 32 * C::LS;
-  int rlast = INT_MIN;  // the newest chunk in the buffer (the one before it is there too)
+  f32x16 rprev = zero16();
+  int rlast = INT_MIN;  // the chunk rprev holds
 
   for (int kt = kt_lo; kt <= kt_hi; ++kt) {
     const int j0 = kt * N;
-    const int D0 = i0 - j0;  // distance between the first query and the first key of the tile
-    __syncthreads();          // tile kt (K, V, P window) is in LDS
+    const int c0 = (i0 - j0) / N;  // exact: i0 and j0 are multiples of N
+    __syncthreads();               // tile kt (K, V and its chunks) is in LDS
 
-    // prefetch tile kt+1 and the one new P chunk its window needs
+    // prefetch tile kt+1 and the one new chunk its waves read (c0 - 2)
     const bool more = kt < kt_hi;
-    const int knew = D0 / N - 2;  // lowest chunk of the next window
-    const int kind_new = more ? chunk_kind(knew) : 0;
+    const int knew = c0 - 2;
+    const bool store_new = more && chunk_needed(knew);
     fetch_kv(more ? kt + 1 : kt);
     fetch_p(knew);
 
-    // ---- per-wave work on the (32 queries) x (N keys) sub-tile
+    // ---- per-wave work on the (32 queries) x (32 keys) sub-tile
     const bool wdead = qw0 >= T_ || j0 > qw0 + 31 || (W > 0 && qw0 - (j0 + N - 1) >= W);
     if (!wdead) {
       const bool wband = E > 0 && max(0, qw0 - (j0 + N - 1)) < E;
       const bool wmask = (j0 + N - 1 > qw0) || (W > 0 && qw0 + 31 - j0 >= W);
 
-      // Scores S^T = K Q^T as two interleaved accumulators (even / odd
-      // k-steps) and, on tiles with bias, the R^T blocks = P_rows r^T for
-      // this wave's distances [Dw - N, Dw + 32): window rows 32*w + 32*rb +
-      // (0..31); window row rho lives in chunk D0/N - 1 + rho/N, row rho%N.
-      // Independent chains keep the matrix cores busy with one wave per SIMD.
-      f32x16 s[NB], s_odd[NB];
-#pragma unroll
-      for (int nb = 0; nb < NB; ++nb) {
-        s[nb] = zero16();
-        s_odd[nb] = zero16();
-      }
-      auto qk_step = [&](int kk) {
-#pragma unroll
-        for (int nb = 0; nb < NB; ++nb) {
-          const v8_t<T> kf = ld8<T>(Ks + (nb * 32 + a) * C::KS + 8 * h2 + kk * 16);
-          if (kk & 1) mma32(kf, qreg[kk], s_odd[nb]);
-          else mma32(kf, qreg[kk], s[nb]);
-        }
-      };
+      // Scores S^T = K Q^T: lane a's column is query a, accumulator v is key
+      // 8*(v/4) + 4*h2 + v%4 of the tile.
+      f32x16 s = zero16();
       if (wband) {
-        // Keys b of this tile sit at distance 32c + a - b from query a, in
-        // chunks c-1 (a < b) and c (a >= b).  Chunk c was made on the previous
-        // tile; chunk c-1 is new: R^T = P_rows r^T over its 32 distances.
-        const int c = D0 / N + w;
-        auto prow = [&](int k) { return Pr + (k & (C::RING - 1)) * ring_base_stride + a * C::PS + 8 * h2; };
-        auto write_chunk = [&](int k, const f32x16& acc) {
-          float* dst = rs + a * C::LS + 32 * (k & 1) + 4 * h2;
+        const int c = c0 + w;
+        if (rlast != c) {
+          // first tile with bias for this wave: chunk c (its distances may
+          // reach below E) straight from P_cols in global memory
+          rprev = zero16();
+          if (chunk_needed(c)) {
+            const int d = c * N + a;
+            const bool rok = d >= 0 && d < E;
+            const T* prow = pcg + size_t(min(max(d, 0), max(E - 1, 0))) * d_r + 8 * h2;
 #pragma unroll
-          for (int g4 = 0; g4 < 4; ++g4) {
-            f32x4 x;
-            x[0] = acc[4 * g4 + 0];
-            x[1] = acc[4 * g4 + 1];
-            x[2] = acc[4 * g4 + 2];
-            x[3] = acc[4 * g4 + 3];
-            *reinterpret_cast<f32x4*>(dst + g4 * 8) = x;
-            if ((k & 1) == 0) *reinterpret_cast<f32x4*>(dst + 64 + g4 * 8) = x;
+            for (int kk = 0; kk < kMaxDr / 16; ++kk)
+              mma32(ld8_or_zero<T>(prow + kk * 16, rok && kk < d_r / 16), rreg[kk], rprev);
           }
-        };
-        if (rlast != c) {  // first tile with bias for this wave
-          f32x16 rc = zero16();
-          const T* pr = prow(c);
-#pragma unroll
-          for (int kk = 0; kk < kMaxDr / 16; ++kk) mma32(ld8<T>(pr + kk * 16), rreg[kk], rc);
-          write_chunk(c, rc);
         }
+        // the new chunk c-1: R^T = P_rows r^T, one MFMA chain beside the QK chain
         f32x16 racc = zero16();
         {
-          const T* pr = prow(c - 1);
+          const T* pr = Pr + ((c - 1) & (C::RING - 1)) * (N * C::PS) + a * C::PS + 8 * h2;
+          const T* kr = Ks + a * C::KS + 8 * h2;
 #pragma unroll
-          for (int kk = 0; kk < kMaxDr / 16; ++kk) {
-            mma32(ld8<T>(Ks + a * C::KS + 8 * h2 + kk * 16), qreg[kk], s[0]);
+          for (int kk = 0; kk < D / 16; ++kk) {
+            mma32(ld8<T>(kr + kk * 16), qreg[kk], s);
             mma32(ld8<T>(pr + kk * 16), rreg[kk], racc);
           }
         }
-        write_chunk(c - 1, racc);
+        // R^T accumulator v is distance 8*(v/4) + 4*h2 + v%4 of its chunk
+#pragma unroll
+        for (int g4 = 0; g4 < 4; ++g4) {
+          float* dst = rs + a * C::LS + 8 * g4 + 4 * h2;
+          f32x4 x0, x1;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            x0[e] = racc[4 * g4 + e];
+            x1[e] = rprev[4 * g4 + e];
+          }
+          *reinterpret_cast<f32x4*>(dst) = x0;
+          *reinterpret_cast<f32x4*>(dst + 32) = x1;
+        }
+        rprev = racc;
         rlast = c - 1;
         wave_lds_fence();
-        // y = S*(c1/c2) + R(a, 32c + a - b): key b of accumulator v is
-        // 8*(v/4) + 4*h2 + v%4, at column 32*((c-1)&1) + 32 + a - b
-        const float* src = rs + a * C::LS + 32 * ((c - 1) & 1) + 32 + a - 4 * h2;
+        // y = S*(c1/c2) + R(a, 32c + a - b), at column 32 + a - b
+        const float* src = rs + a * C::LS + 32 + a - 4 * h2;
 #pragma unroll
-        for (int v = 0; v < 16; ++v) s[0][v] = fmaf(s[0][v], qk_scale, src[-(8 * (v >> 2) + (v & 3))]);
+        for (int v = 0; v < 16; ++v) s[v] = fmaf(s[v], qk_scale, src[-(8 * (v >> 2) + (v & 3))]);
         wave_lds_fence();
       } else {
+        f32x16 s_odd = zero16();  // two chains keep the matrix cores busy
 #pragma unroll
-        for (int kk = 0; kk < D / 16; ++kk) qk_step(kk);
+        for (int kk = 0; kk < D / 16; ++kk) {
+          const v8_t<T> kf = ld8<T>(Ks + a * C::KS + 8 * h2 + kk * 16);
+          if (kk & 1) mma32(kf, qreg[kk], s_odd);
+          else mma32(kf, qreg[kk], s);
+        }
 #pragma unroll
-        for (int nb = 0; nb < NB; ++nb)
-#pragma unroll
-          for (int v = 0; v < 16; ++v) s[nb][v] = (s[nb][v] + s_odd[nb][v]) * qk_scale;
+        for (int v = 0; v < 16; ++v) s[v] = (s[v] + s_odd[v]) * qk_scale;
       }
 
       if (wmask) {
 #pragma unroll
-        for (int nb = 0; nb < NB; ++nb)
-#pragma unroll
-          for (int v = 0; v < 16; ++v) {
-            const int dd = qa - (j0 + nb * 32 + 8 * (v >> 2) + 4 * h2 + (v & 3));
-            if (dd < 0 || (W > 0 && dd >= W)) s[nb][v] = -INFINITY;
-          }
+        for (int v = 0; v < 16; ++v) {
+          const int dd = qa - (j0 + 8 * (v >> 2) + 4 * h2 + (v & 3));
+          if (dd < 0 || (W > 0 && dd >= W)) s[v] = -INFINITY;
+        }
       }
 
       // online softmax (per query = per lane pair l, l^32).  The exponentials
       // are taken against the running maximum first; only when some row
       // maximum grows by more than the lazy margin are O and l rescaled and
       // the exponentials recomputed against the new maximum.
-      f32x16 pexp[NB];
+      f32x16 pexp;
       float mx = -INFINITY;
       {
         const float nm = -p.c2 * m_run;
 #pragma unroll
-        for (int nb = 0; nb < NB; ++nb)
-#pragma unroll
-          for (int v = 0; v < 16; ++v) {
-            mx = fmaxf(mx, s[nb][v]);
-            pexp[nb][v] = fast_exp2(fmaf(s[nb][v], p.c2, nm));
-          }
+        for (int v = 0; v < 16; ++v) {
+          mx = fmaxf(mx, s[v]);
+          pexp[v] = fast_exp2(fmaf(s[v], p.c2, nm));
+        }
       }
       mx = fmaxf(mx, xor_lane(mx, 32));
       if (__builtin_amdgcn_ballot_w64(mx > m_run + lazy) != 0) {
@@ -429,18 +408,11 @@ __global__ __launch_bounds__(WAVES * 64, 1) void prefill_kernel(PrefillArgs p, i
           for (int v = 0; v < 16; ++v) o[i][v] *= corr;
         const float nm = -p.c2 * m_run;
 #pragma unroll
-        for (int nb = 0; nb < NB; ++nb)
-#pragma unroll
-          for (int v = 0; v < 16; ++v) pexp[nb][v] = fast_exp2(fmaf(s[nb][v], p.c2, nm));
+        for (int v = 0; v < 16; ++v) pexp[v] = fast_exp2(fmaf(s[v], p.c2, nm));
       }
       float psum = 0.0f;
 #pragma unroll
-      for (int nb = 0; nb < NB; ++nb)
-#pragma unroll
-        for (int v = 0; v < 16; ++v) {
-          s[nb][v] = pexp[nb][v];
-          psum += pexp[nb][v];
-        }
+      for (int v = 0; v < 16; ++v) psum += pexp[v];
       l_run += psum;
 
       // O^T += V^T P^T
@@ -448,16 +420,16 @@ __global__ __launch_bounds__(WAVES * 64, 1) void prefill_kernel(PrefillArgs p, i
       for (int c16 = 0; c16 < N / 16; ++c16) {
         v8_t<T> pb;
 #pragma unroll
-        for (int t = 0; t < 8; ++t) pb[t] = T(s[c16 >> 1][8 * (c16 & 1) + t]);
+        for (int t = 0; t < 8; ++t) pb[t] = T(pexp[8 * c16 + t]);
 #pragma unroll
         for (int db = 0; db < D / 32; ++db) mma32(VS::frag(Vs, c16, db, lane), pb, o[db]);
       }
     }
 
-    __syncthreads();  // every wave is done with tile kt's K and V
+    __syncthreads();  // every wave is done with tile kt's K, V and chunks
     if (more) {
       store_kv();
-      if (kind_new != 0) store_p(knew, kind_new == 1);
+      if (store_new) store_p(knew);
     }
   }
 
@@ -475,24 +447,24 @@ __global__ __launch_bounds__(WAVES * 64, 1) void prefill_kernel(PrefillArgs p, i
   if (p.lse != nullptr && h2 == 0) p.lse[(size_t(b) * Hq + h) * T_ + qa] = (p.c2 * m_run + log2f(l_tot)) * kLn2;
 }
 
-template <typename T, int WAVES, int N>
+template <typename T, int WAVES>
 hipError_t launch_prefill_tiles(const PrefillArgs& a, hipStream_t stream) {
-  using C = PrefillCfg<T, WAVES, N>;
+  using C = PrefillCfg<T, WAVES>;
   const int n_qt = (a.T + C::M - 1) / C::M;
   const int G = a.Hq / a.Hkv;
   const long long n_groups = (long long)n_qt * a.B * a.Hkv;
   const long long grid = ((n_groups + 7) / 8) * 8 * G;
   if (grid > 0x7fffffffLL) return hipErrorInvalidConfiguration;
-  hipLaunchKernelGGL((prefill_kernel<T, WAVES, N>), dim3((unsigned)grid), dim3(C::THREADS), 0, stream, a,
-                     n_qt, (int)n_groups);
+  hipLaunchKernelGGL((prefill_kernel<T, WAVES>), dim3((unsigned)grid), dim3(C::THREADS), 0, stream, a, n_qt,
+                     (int)n_groups);
   return hipGetLastError();
 }
 
 }  // namespace
 
 hipError_t launch_prefill(int dtype, const PrefillArgs& a, hipStream_t stream) {
-  if (dtype == 1) return launch_prefill_tiles<__bf16, 4, 32>(a, stream);
-  return launch_prefill_tiles<float, 2, 32>(a, stream);
+  if (dtype == 1) return launch_prefill_tiles<__bf16, 8>(a, stream);
+  return launch_prefill_tiles<float, 2>(a, stream);
 }
 
 }  // namespace relattn
