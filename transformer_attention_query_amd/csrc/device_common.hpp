@@ -117,6 +117,21 @@ __device__ __forceinline__ float xor_lane(float x, int mask) {
   return __int_as_float(__builtin_amdgcn_ds_bpermute(src, __float_as_int(x)));
 }
 
+// Reductions over the lane pair (l, l ^ 32) with v_permlane32_swap, which
+// exchanges the upper half of its first operand with the lower half of its
+// second: with x in both, the two results hold x and x of the partner lane
+// (in either order), so their max / sum is the pair's on every lane.
+__device__ __forceinline__ float pair_max32(float x) {
+  const unsigned u = __float_as_uint(x);
+  const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float pair_sum32(float x) {
+  const unsigned u = __float_as_uint(x);
+  const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
 // Orders this wave's LDS writes before its later LDS reads of other lanes'
 // data (LDS executes one wave's operations in order; this keeps the compiler
 // from moving the accesses across each other and waits for the writes).

@@ -396,7 +396,7 @@ __global__ __launch_bounds__(WAVES * 64, 1) void prefill_kernel(PrefillArgs p, i
           pexp[v] = fast_exp2(fmaf(s[v], p.c2, nm));
         }
       }
-      mx = fmaxf(mx, xor_lane(mx, 32));
+      mx = pair_max32(mx);
       if (__builtin_amdgcn_ballot_w64(mx > m_run + lazy) != 0) {
         const float m_new = fmaxf(m_run, mx);
         const float corr = fast_exp2(p.c2 * (m_run - m_new));
@@ -434,7 +434,7 @@ __global__ __launch_bounds__(WAVES * 64, 1) void prefill_kernel(PrefillArgs p, i
   }
 
   // ---- epilogue: normalise and store
-  const float l_tot = l_run + xor_lane(l_run, 32);
+  const float l_tot = pair_sum32(l_run);
   if (!qvalid) return;
   const float inv = 1.0f / l_tot;
   T* orow = static_cast<T*>(p.out) + ((size_t(b) * T_ + qa) * Hq + h) * D;
