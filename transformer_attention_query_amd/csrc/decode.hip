@@ -382,6 +382,49 @@ __global__ __launch_bounds__(kMergeThreads) void decode_merge_kernel(DecodeArgs 
   if (p.lse != nullptr && col0 == 0 && d4 == 0) p.lse[bh] = (M + log2f(den)) * kLn2;
 }
 
+// Few splits: one thread per (sequence, head, 4 output columns) merges them.
+constexpr int kMergeSmallSplits = 16;
+
+template <typename T>
+__global__ __launch_bounds__(256) void decode_merge_small_kernel(DecodeArgs p) {
+  constexpr int D = kHeadDim;
+  const size_t n_bh = size_t(p.B) * p.Hq;
+  const size_t t = size_t(blockIdx.x) * 256 + threadIdx.x;
+  if (t >= n_bh * (D / 4)) return;
+  const size_t bh = t / (D / 4);
+  const int d4 = int(t % (D / 4));
+  const float* ws_o = p.ws;
+  const float* ws_m = p.ws + size_t(p.n_split) * n_bh * D;
+  const float* ws_l = ws_m + size_t(p.n_split) * n_bh;
+  // all splits' partials are loaded first (indices clamped, splits past
+  // n_split weighted by zero), then folded
+  float ms[kMergeSmallSplits], ls[kMergeSmallSplits];
+  f32x4 os[kMergeSmallSplits];
+#pragma unroll
+  for (int s = 0; s < kMergeSmallSplits; ++s) {
+    const size_t sb = size_t(min(s, p.n_split - 1)) * n_bh + bh;
+    ms[s] = ws_m[sb];
+    ls[s] = ws_l[sb];
+    os[s] = *reinterpret_cast<const f32x4*>(ws_o + sb * D + 4 * d4);
+  }
+  float M = ms[0];
+#pragma unroll
+  for (int s = 1; s < kMergeSmallSplits; ++s)
+    if (s < p.n_split) M = fmaxf(M, ms[s]);
+  float den = 0.0f;
+  f32x4 acc = zero4();
+#pragma unroll
+  for (int s = 0; s < kMergeSmallSplits; ++s) {
+    const float wgt = s < p.n_split ? fast_exp2(ms[s] - M) : 0.0f;
+    den += wgt * ls[s];
+#pragma unroll
+    for (int v = 0; v < 4; ++v) acc[v] += wgt * os[s][v];
+  }
+  const float inv = 1.0f / den;
+  st4_f32<T>(static_cast<T*>(p.out) + bh * D + 4 * d4, acc[0] * inv, acc[1] * inv, acc[2] * inv, acc[3] * inv);
+  if (p.lse != nullptr && d4 == 0) p.lse[bh] = (M + log2f(den)) * kLn2;
+}
+
 template <typename T>
 hipError_t launch_decode_t(const DecodeArgs& a, hipStream_t stream) {
   {
@@ -407,8 +450,13 @@ hipError_t launch_decode_t(const DecodeArgs& a, hipStream_t stream) {
   hipLaunchKernelGGL(decode_split_kernel<T>, dim3((unsigned)grid), dim3(kDecWaves * 64), 0, stream, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(decode_merge_kernel<T>, dim3((unsigned)(a.B * a.Hq * (kHeadDim / kMergeCols))),
-                     dim3(kMergeThreads), 0, stream, a);
+  if (a.n_split <= kMergeSmallSplits) {
+    const long long threads = (long long)a.B * a.Hq * (kHeadDim / 4);
+    hipLaunchKernelGGL(decode_merge_small_kernel<T>, dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, stream, a);
+  } else {
+    hipLaunchKernelGGL(decode_merge_kernel<T>, dim3((unsigned)(a.B * a.Hq * (kHeadDim / kMergeCols))),
+                       dim3(kMergeThreads), 0, stream, a);
+  }
   return hipGetLastError();
 }
 

@@ -36,12 +36,25 @@ __global__ __launch_bounds__(kRlWaves * 64) void rel_logits_kernel(RelLogitsArgs
   const bool aok = arow < p.n_rows && E > 0;
   const int d = p.rev_base > 0 ? p.rev_base - 1 - col : col;
   const bool bok = d >= 0 && d < E;
-  const T* arow_p = rg + (aok ? arow : 0) * d_r + 8 * h2;
-  const T* prow = pcg + size_t(bok ? d : 0) * d_r + 8 * h2;
   f32x16 acc = zero16();
+  if (E > 0) {  // with E == 0 (decode without bias) r and P may be NULL: zeros, no loads
+    // every operand load is issued first, from clamped addresses inside r
+    // and P, and zeroed where it falls outside them or past d_r only when used
+    const T* arow_p = rg + (aok ? arow : 0) * d_r + 8 * h2;
+    const T* prow = pcg + size_t(bok ? d : 0) * d_r + 8 * h2;
+    v8_t<T> av[kMaxDr / 16], bv[kMaxDr / 16];
 #pragma unroll
-  for (int kk = 0; kk < kMaxDr / 16; ++kk)
-    if (kk < nk) mma32(ld8_or_zero<T>(arow_p + kk * 16, aok), ld8_or_zero<T>(prow + kk * 16, bok), acc);
+    for (int kk = 0; kk < kMaxDr / 16; ++kk) {
+      const int kc = min(kk, nk - 1) * 16;
+      av[kk] = ld8<T>(arow_p + kc);
+      bv[kk] = ld8<T>(prow + kc);
+    }
+#pragma unroll
+    for (int kk = 0; kk < kMaxDr / 16; ++kk) {
+      const bool ok = kk < nk;
+      mma32((aok && ok) ? av[kk] : zero8<T>(), (bok && ok) ? bv[kk] : zero8<T>(), acc);
+    }
+  }
   // accumulator v of lane (h2, a): row 8*(v/4) + 4*h2 + v%4, column a
   if (col < p.out_cols) {
 #pragma unroll
