@@ -132,10 +132,10 @@ struct PrefillCfg {
 };
 
 template <typename T, int WAVES>
-__global__ __launch_bounds__(WAVES * 64, 1) void prefill_kernel(PrefillArgs p, int n_qt, int n_groups) {
+__global__ __launch_bounds__(WAVES * 64, 1) void prefill_kernel(PrefillArgs p, int n_qt, int n_items, int hpw) {
   using C = PrefillCfg<T, WAVES>;
   using VS = PreV<T, C::N>;
-  constexpr int N = C::N, M = C::M;
+  constexpr int N = C::N;
   constexpr int D = kHeadDim;
 
   __shared__ __attribute__((aligned(16))) unsigned char smem[C::LDS_TOTAL];
@@ -147,32 +147,37 @@ __global__ __launch_bounds__(WAVES * 64, 1) void prefill_kernel(PrefillArgs p, i
   const int T_ = p.T, Hq = p.Hq, Hkv = p.Hkv, G = Hq / Hkv;
   const int d_r = p.d_r, E = p.E, W = p.W;
 
-  // ---- workgroup -> (q-tile, batch, kv head, query head)
-  // Workgroup ids reach the 8 XCDs round-robin.  Groups of G workgroups (the
-  // query heads sharing one kv head, same q-tile) are placed on one XCD so
-  // their K/V tiles are shared through that XCD's L2; groups are ordered
-  // longest-first (late q-tiles see the most keys under the causal mask).
-  const int pid = blockIdx.x;
-  const int xcd = pid & 7;
-  const int slot = pid >> 3;
-  const int gi = (slot / G) * 8 + xcd;
-  if (gi >= n_groups) return;
-  const int member = slot % G;
-  const int BH = p.B * Hkv;
-  const int qt = n_qt - 1 - gi / BH;
-  const int bk = gi % BH;
-  const int b = bk / Hkv;
-  const int kvh = bk % Hkv;
-  const int h = kvh * G + member;
+  // ---- workgroup -> (q-tile, batch, kv head, head subgroup); wave -> (query
+  // block, query head).  The waves of a workgroup are hpw query heads of one
+  // kv head (GQA packing) times nqb = WAVES/hpw blocks of 32 queries: with
+  // hpw = WAVES every wave sees the same keys, the same masks and the same
+  // distance chunks, so no wave idles at a barrier and one P chunk serves
+  // all.  Work items are ordered longest-first (late q-tiles see the most
+  // keys under the causal mask); item i and i+8 share an XCD and are nearby
+  // q-tiles of one kv head, so their K/V tiles meet in that XCD's L2.
+  const int nqb = WAVES / hpw;
+  const int M = 32 * nqb;
+  const int item = blockIdx.x;
+  if (item >= n_items) return;
+  const int n_hs = G / hpw;
+  const int per_qt = p.B * Hkv * n_hs;
+  const int qt = n_qt - 1 - item / per_qt;
+  int rest = item % per_qt;
+  const int hs = rest % n_hs;
+  rest /= n_hs;
+  const int kvh = rest % Hkv;
+  const int b = rest / Hkv;
 
   const int tid = threadIdx.x;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lane = tid & 63;
   const int h2 = lane >> 5;  // half-wave
   const int a = lane & 31;   // this lane's query within the wave
+  const int qb = w / hpw;    // query block of this wave
+  const int h = kvh * G + hs * hpw + (w % hpw);
 
   const int i0 = qt * M;
-  const int qw0 = i0 + 32 * w;
+  const int qw0 = i0 + 32 * qb;
   const int qa = qw0 + a;
   const bool qvalid = qa < T_;
 
@@ -262,7 +267,7 @@ __global__ __launch_bounds__(WAVES * 64, 1) void prefill_kernel(PrefillArgs p, i
     }
   };
   auto store_p = [&](int k) {
-    T* base = Pr + size_t(k & (C::RING - 1)) * N * C::PS;
+    T* base = Pr + size_t(k & (nqb - 1)) * N * C::PS;
 #pragma unroll
     for (int i = 0; i < C::P_VECS; ++i) {
       const int vid = tid + i * C::THREADS;
@@ -274,12 +279,12 @@ __global__ __launch_bounds__(WAVES * 64, 1) void prefill_kernel(PrefillArgs p, i
 
   // ---- prologue: first tile and the chunks its waves read
   // Tile kt: the wave's first query is 32c keys after the tile's first key,
-  // c = (i0 - 32kt)/32 + w, so the tile's waves read chunks c0-1 .. c0+WAVES-2
-  // with c0 = (i0 - 32kt)/32.
+  // c = (i0 - 32kt)/32 + qb, so the tile's waves read chunks c0-1 .. c0+nqb-2
+  // with c0 = (i0 - 32kt)/32; the ring has nqb slots (chunk k in slot k mod nqb).
   {
     fetch_kv(kt_lo);
     const int c0 = (i0 - kt_lo * N) / N;
-    for (int k = c0 - 1; k < c0 - 1 + C::RING; ++k) {
+    for (int k = c0 - 1; k < c0 - 1 + nqb; ++k) {
       fetch_p(k);
       if (chunk_needed(k)) store_p(k);
     }
@@ -316,7 +321,7 @@ __global__ __launch_bounds__(WAVES * 64, 1) void prefill_kernel(PrefillArgs p, i
       // 8*(v/4) + 4*h2 + v%4 of the tile.
       f32x16 s = zero16();
       if (wband) {
-        const int c = c0 + w;
+        const int c = c0 + qb;
         if (rlast != c) {
           // first tile with bias for this wave: chunk c (its distances may
           // reach below E) straight from P_cols in global memory
@@ -333,7 +338,7 @@ __global__ __launch_bounds__(WAVES * 64, 1) void prefill_kernel(PrefillArgs p, i
         // the new chunk c-1: R^T = P_rows r^T, one MFMA chain beside the QK chain
         f32x16 racc = zero16();
         {
-          const T* pr = Pr + ((c - 1) & (C::RING - 1)) * (N * C::PS) + a * C::PS + 8 * h2;
+          const T* pr = Pr + ((c - 1) & (nqb - 1)) * (N * C::PS) + a * C::PS + 8 * h2;
           const T* kr = Ks + a * C::KS + 8 * h2;
 #pragma unroll
           for (int kk = 0; kk < D / 16; ++kk) {
@@ -449,14 +454,16 @@ __global__ __launch_bounds__(WAVES * 64, 1) void prefill_kernel(PrefillArgs p, i
 
 template <typename T, int WAVES>
 hipError_t launch_prefill_tiles(const PrefillArgs& a, hipStream_t stream) {
-  using C = PrefillCfg<T, WAVES>;
-  const int n_qt = (a.T + C::M - 1) / C::M;
+  // heads per workgroup: the largest power of two <= WAVES dividing Hq/Hkv
   const int G = a.Hq / a.Hkv;
-  const long long n_groups = (long long)n_qt * a.B * a.Hkv;
-  const long long grid = ((n_groups + 7) / 8) * 8 * G;
-  if (grid > 0x7fffffffLL) return hipErrorInvalidConfiguration;
-  hipLaunchKernelGGL((prefill_kernel<T, WAVES>), dim3((unsigned)grid), dim3(C::THREADS), 0, stream, a, n_qt,
-                     (int)n_groups);
+  int hpw = 1;
+  while (hpw * 2 <= WAVES && G % (hpw * 2) == 0) hpw *= 2;
+  const int M = 32 * (WAVES / hpw);
+  const int n_qt = (a.T + M - 1) / M;
+  const long long n_items = (long long)n_qt * a.B * a.Hkv * (G / hpw);
+  if (n_items > 0x7fffffffLL) return hipErrorInvalidConfiguration;
+  hipLaunchKernelGGL((prefill_kernel<T, WAVES>), dim3((unsigned)n_items), dim3(PrefillCfg<T, WAVES>::THREADS), 0,
+                     stream, a, n_qt, (int)n_items, hpw);
   return hipGetLastError();
 }
 
