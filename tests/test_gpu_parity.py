@@ -57,12 +57,15 @@ def test_prefill_matches_oracle(case):
     assert_close(out, ref, x["q"].dtype, name, lse, lref)
 
 
+@pytest.mark.parametrize("heads", [(8, 2), (8, 1)], ids=["G4", "G8"])
 @pytest.mark.parametrize("W", [0, 300])
 @pytest.mark.parametrize("variant", ["P_x50", "alpha_0"])
-def test_prefill_bias_sensitivity(variant, W):
-    """Large-bias variants where a shear or rel_extent slip changes the output by O(1)."""
+def test_prefill_bias_sensitivity(variant, W, heads):
+    """Large-bias variants where a shear or rel_extent slip changes the output by O(1).
+    G8 (eight query heads per kv head) takes the eight-heads-per-workgroup kernel."""
     T, E = 777, 200
-    x = tinputs.make_prefill_inputs(1, T, 8, 2, 128, 64, E, "bf16", seed=5)
+    Hq, Hkv = heads
+    x = tinputs.make_prefill_inputs(1, T, Hq, Hkv, 128, 64, E, "bf16", seed=5)
     alpha = ALPHA
     if variant == "P_x50":
         x["P"] = (x["P"].float() * 50).to(torch.bfloat16)

@@ -438,18 +438,36 @@ __global__ __launch_bounds__(WAVES * 64, 1) void prefill_kernel(PrefillArgs p, i
     }
   }
 
-  // ---- epilogue: normalise and store
+  // ---- epilogue: normalise, stage the wave's 32 x D output tile in LDS and
+  // write it back as whole rows in 16-byte pieces (each lane holds only
+  // 4-element fragments of its query's row)
   const float l_tot = pair_sum32(l_run);
-  if (!qvalid) return;
   const float inv = 1.0f / l_tot;
-  T* orow = static_cast<T*>(p.out) + ((size_t(b) * T_ + qa) * Hq + h) * D;
+  __syncthreads();  // every wave is done with the tile buffers
+  constexpr int OS = D + 16 / int(sizeof(T));  // staged row stride (elements)
+  static_assert(size_t(WAVES) * 32 * OS * sizeof(T) <= C::LDS_TOTAL, "output staging fits the LDS");
+  T* ot = reinterpret_cast<T*>(smem) + size_t(w) * 32 * OS;
 #pragma unroll
   for (int db = 0; db < D / 32; ++db)
 #pragma unroll
     for (int g4 = 0; g4 < 4; ++g4)
-      st4_f32<T>(orow + db * 32 + g4 * 8 + 4 * h2, o[db][4 * g4] * inv, o[db][4 * g4 + 1] * inv,
+      st4_f32<T>(ot + a * OS + db * 32 + g4 * 8 + 4 * h2, o[db][4 * g4] * inv, o[db][4 * g4 + 1] * inv,
                  o[db][4 * g4 + 2] * inv, o[db][4 * g4 + 3] * inv);
-  if (p.lse != nullptr && h2 == 0) p.lse[(size_t(b) * Hq + h) * T_ + qa] = (p.c2 * m_run + log2f(l_tot)) * kLn2;
+  wave_lds_fence();
+  typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+  constexpr int EPV = 16 / int(sizeof(T));  // elements per 16-byte piece
+  constexpr int VPR = D / EPV;              // pieces per row
+  static_assert((32 * VPR) % 64 == 0, "whole pieces per lane");
+#pragma unroll
+  for (int it = 0; it < 32 * VPR / 64; ++it) {
+    const int i = lane + 64 * it;
+    const int row = i / VPR, cv = i % VPR;
+    const int q = qw0 + row;
+    if (q < T_)
+      *reinterpret_cast<u32x4*>(static_cast<T*>(p.out) + ((size_t(b) * T_ + q) * Hq + h) * D + cv * EPV) =
+          *reinterpret_cast<const u32x4*>(ot + row * OS + cv * EPV);
+  }
+  if (p.lse != nullptr && h2 == 0 && qvalid) p.lse[(size_t(b) * Hq + h) * T_ + qa] = (p.c2 * m_run + log2f(l_tot)) * kLn2;
 }
 
 template <typename T, int WAVES>
