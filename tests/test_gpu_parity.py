@@ -42,6 +42,13 @@ PREFILL_CASES = [
     ("T1100_E1024_W1024", "bf16", 1, 1100, 8, 1, 128, 1024, 1024, False),
     ("fp32_T300_W70", "fp32", 1, 300, 4, 2, 64, 100, 70, False),
     ("fp32_T129", "fp32", 2, 129, 2, 1, 16, 7, 0, False),
+    # eight or more query heads per kv head: 64-key tiles, two distance chunks per tile
+    ("G8_T97_E33", "bf16", 2, 97, 8, 1, 16, 33, 0, False),
+    ("G8_T160_W1_E1", "bf16", 1, 160, 8, 1, 32, 1, 1, False),
+    ("G8_T333_W65_E63", "bf16", 1, 333, 16, 2, 64, 63, 65, False),
+    ("G8_T64_E0", "bf16", 1, 64, 8, 1, 32, 0, 0, False),
+    ("G8_T700_E600_log", "bf16", 1, 700, 8, 1, 128, 600, 0, True),
+    ("G16_T450_W130_E129", "bf16", 1, 450, 16, 1, 48, 129, 130, False),
 ]
 
 
