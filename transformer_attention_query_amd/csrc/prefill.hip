@@ -39,6 +39,9 @@
 //     current window does not use.
 //   * The next tile's K, V and P chunk are fetched into registers while the
 //     current tile computes and are written to LDS between two barriers.
+//     (bf16 with eight or more query heads per kv head takes
+//     prefill_dma_kernel below instead: LDS DMA into double-buffered tiles,
+//     one barrier per tile.)
 //   * Softmax works in units of c2 = s*log2(e): y = S*(c1/c2) + R, so the bias
 //     rows need no scaling, and p = exp2(c2*y - c2*m).  O is rescaled only
 //     when a row maximum grows by more than 2^8 (exact either way: O and l
@@ -485,10 +488,337 @@ hipError_t launch_prefill_tiles(const PrefillArgs& a, hipStream_t stream) {
   return hipGetLastError();
 }
 
+// ---------------------------------------------------------------------------
+// bf16, Hq/Hkv a multiple of 8: the eight waves of a workgroup are eight query
+// heads of one kv head on the same 32 queries (one K, V and P tile serves all
+// of them), and the next tile streams into LDS by DMA while this one computes.
+//
+// global_load_lds_dwordx4 writes each lane's 16 bytes at M0 + 16*lane, so a
+// wave instruction fills 1 KB = four 256-byte tile rows.  Lanes choose their
+// source chunk so that a row's 16-byte chunks land XOR-swizzled: chunk q of
+// row r sits at slot q ^ sw(r), with sw(r) = r & 7 for K and P (the 8 lanes of
+// a 16-byte fragment read hit 8 distinct bank groups) and sw(r) = 2*(r & 3)
+// for V (the 16 lanes of a transpose read cover the 32 banks once).  Tiles are
+// double-buffered: one barrier per tile, after which the waves issue the next
+// tile's DMA into the other buffer and compute on this one, then wait for
+// their own DMA.  P rows are fetched from clamped addresses; distances at or
+// beyond E are zeroed in the relative-logit accumulators instead.
+// ---------------------------------------------------------------------------
+struct DmaCfg {
+  static constexpr int N = 32;
+  static constexpr int ROWB = kHeadDim * 2;  // bytes per K / V / P tile row (d_r padded to 128)
+  static constexpr int TILEB = N * ROWB;     // 8 KB
+  static constexpr int LS = 2 * N + 4;       // R buffer row stride (floats)
+  static constexpr int THREADS = 512;
+  static constexpr size_t OFF_K = 0, OFF_V = 2 * TILEB, OFF_P = 4 * TILEB, OFF_R = 6 * TILEB;
+  static constexpr size_t LDS_TOTAL = OFF_R + size_t(8) * 32 * LS * sizeof(float);
+  static_assert(kMaxDr == kHeadDim, "P rows share the K tile geometry");
+  static_assert(LDS_TOTAL <= 160 * 1024, "LDS budget of one gfx950 workgroup");
+};
+
+// M0 (the DMA's LDS base) is saved and restored around the load, so the
+// compiler's own use of M0 is untouched.
+__device__ __forceinline__ void dma16(const void* src, unsigned lds_base) {
+  unsigned saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %2\n\t"
+      "global_load_lds_dwordx4 %1, off\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "v"(src), "s"(lds_base)
+      : "memory");
+}
+__device__ __forceinline__ void dma_wait() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
+__global__ __launch_bounds__(512, 1) void prefill_dma_kernel(PrefillArgs p, int n_qt, int n_items) {
+  using C = DmaCfg;
+  using T = __bf16;
+  constexpr int N = C::N;
+  constexpr int D = kHeadDim;
+
+  __shared__ __attribute__((aligned(16))) unsigned char smem[C::LDS_TOTAL];
+  float* const Rs = reinterpret_cast<float*>(smem + C::OFF_R);
+
+  const int T_ = p.T, Hq = p.Hq, Hkv = p.Hkv, G = Hq / Hkv;
+  const int d_r = p.d_r, E = p.E, W = p.W;
+
+  // ---- workgroup -> (32-query tile, batch, kv head, group of 8 heads),
+  // longest query tiles first
+  const int item = blockIdx.x;
+  if (item >= n_items) return;
+  const int n_hs = G / 8;
+  const int per_qt = p.B * Hkv * n_hs;
+  const int qt = n_qt - 1 - item / per_qt;
+  int rest = item % per_qt;
+  const int hs = rest % n_hs;
+  rest /= n_hs;
+  const int kvh = rest % Hkv;
+  const int b = rest / Hkv;
+
+  const int tid = threadIdx.x;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = tid & 63;
+  const int h2 = lane >> 5;
+  const int a = lane & 31;
+  const int h = kvh * G + hs * 8 + w;
+
+  const int q0 = qt * N;
+  const int qa = q0 + a;
+  const bool qvalid = qa < T_;
+
+  const T* qg = static_cast<const T*>(p.q);
+  const T* kg = static_cast<const T*>(p.k);
+  const T* vg = static_cast<const T*>(p.v);
+  const T* rg = static_cast<const T*>(p.r);
+  const T* pcg = E > 0 ? static_cast<const T*>(p.pc) : kg;
+
+  const float qk_scale = p.c1 / p.c2;
+  const float lazy = kLazyRescaleLog2 / p.c2;
+
+  bf16x8 qreg[D / 16];
+  {
+    const T* qrow = qg + ((size_t(b) * T_ + (qvalid ? qa : 0)) * Hq + h) * D + 8 * h2;
+#pragma unroll
+    for (int kk = 0; kk < D / 16; ++kk) qreg[kk] = ld8_or_zero<T>(qrow + kk * 16, qvalid);
+  }
+  bf16x8 rreg[kMaxDr / 16];  // zero past d_r
+  {
+    const int nkr = d_r / 16;
+    const T* rrow = rg + ((size_t(b) * T_ + (qvalid ? qa : 0)) * Hq + h) * d_r + 8 * h2;
+#pragma unroll
+    for (int kk = 0; kk < kMaxDr / 16; ++kk) rreg[kk] = ld8_or_zero<T>(rrow + kk * 16, E > 0 && qvalid && kk < nkr);
+  }
+
+  f32x16 o[D / 32];
+#pragma unroll
+  for (int i = 0; i < D / 32; ++i) o[i] = zero16();
+  float m_run = -1e30f;
+  float l_run = 0.0f;
+
+  const int i_last = min(q0 + N - 1, T_ - 1);
+  const int kt_lo = W > 0 ? max(0, q0 - W + 1) / N : 0;
+  const int kt_hi = i_last / N;
+
+  // ---- DMA of one tile: this wave fills rows 4w .. 4w+3 of the K, V and P
+  // tiles; lane l writes slot l%16 of row 4w + l/16
+  const int drow = 4 * w + (lane >> 4);
+  const int dslot = lane & 15;
+  const int qk_src = dslot ^ (drow & 7);        // K / P chunk landing in this slot
+  const int qv_src = dslot ^ (2 * (drow & 3));  // V chunk landing in this slot
+  const size_t kv_row_stride = size_t(Hkv) * D;
+  const T* kbase = kg + (size_t(b) * T_ * Hkv + kvh) * D;
+  const T* vbase = vg + (size_t(b) * T_ * Hkv + kvh) * D;
+  const int pvec = d_r / 8;
+  const unsigned lds0 = unsigned(reinterpret_cast<size_t>(smem)) + 1024u * unsigned(w);
+  auto chunk0 = [&](int kt) { return (q0 - kt * N) / N; };
+  auto issue_tile = [&](int kt) {
+    const int buf = kt & 1;
+    const size_t j = size_t(min(kt * N + drow, T_ - 1)) * kv_row_stride;
+    dma16(kbase + j + 8 * qk_src, __builtin_amdgcn_readfirstlane(lds0 + C::OFF_K + buf * C::TILEB));
+    dma16(vbase + j + 8 * qv_src, __builtin_amdgcn_readfirstlane(lds0 + C::OFF_V + buf * C::TILEB));
+    if (E > 0) {
+      const int d = (chunk0(kt) - 1) * N + drow;  // the tile's new distance chunk
+      dma16(pcg + size_t(min(max(d, 0), E - 1)) * d_r + 8 * min(qk_src, pvec - 1),
+            __builtin_amdgcn_readfirstlane(lds0 + C::OFF_P + buf * C::TILEB));
+    }
+  };
+
+  // ---- prologue: tile kt_lo.  The compiler-visible wait also retires the q
+  // and r loads, so no wait for them lands inside the tile loop.
+  issue_tile(kt_lo);
+  dma_wait();
+  __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0)
+
+  // Per-wave relative-logit buffer: chunk c-1 at columns 0..31, chunk c at
+  // 32..63, so key b of query a (distance 32c + a - b) is column 32 + a - b.
+  float* const rs = Rs + w * 32 * C::LS;
+  f32x16 rprev = zero16();  // chunk rlast, made on the previous tile
+  int rlast = INT_MIN;
+
+  for (int kt = kt_lo; kt <= kt_hi; ++kt) {
+    const int j0 = kt * N;
+    const int c0 = chunk0(kt);
+    __syncthreads();  // tile kt is in LDS; every wave is done with tile kt-1
+    if (kt < kt_hi) issue_tile(kt + 1);
+
+    const unsigned char* kt_b = smem + C::OFF_K + (kt & 1) * C::TILEB;
+    const unsigned char* vt_b = smem + C::OFF_V + (kt & 1) * C::TILEB;
+    const unsigned char* pt_b = smem + C::OFF_P + (kt & 1) * C::TILEB;
+    // fragment of row a, chunk q (16 bytes) of a K / P tile
+    auto frag_kp = [&](const unsigned char* t, int q) {
+      return ld8<T>(reinterpret_cast<const T*>(t + a * C::ROWB + ((q ^ (a & 7)) << 4)));
+    };
+
+    const bool live = !(j0 > q0 + 31 || (W > 0 && q0 - (j0 + N - 1) >= W));
+    if (live) {
+      const bool band = E > 0 && max(0, q0 - (j0 + N - 1)) < E;
+      const bool mask = (j0 + N - 1 > q0) || (W > 0 && q0 + 31 - j0 >= W);
+      f32x16 s = zero16();
+      if (band) {
+        if (rlast != c0) {
+          // first tile with bias: chunk c0 straight from P_cols in global memory
+          const int d = c0 * N + a;
+          const bool rok = d >= 0 && d < E;
+          const int nk = d_r / 16;
+          const T* prow = pcg + size_t(min(max(d, 0), E - 1)) * d_r + 8 * h2;
+          bf16x8 pf[kMaxDr / 16];
+#pragma unroll
+          for (int kk = 0; kk < kMaxDr / 16; ++kk) pf[kk] = ld8<T>(prow + min(kk, nk - 1) * 16);
+          rprev = zero16();
+#pragma unroll
+          for (int kk = 0; kk < kMaxDr / 16; ++kk) mma32((rok && kk < nk) ? pf[kk] : zero8<T>(), rreg[kk], rprev);
+        }
+        f32x16 racc = zero16();
+#pragma unroll
+        for (int kk = 0; kk < D / 16; ++kk) {
+          mma32(frag_kp(kt_b, h2 + 2 * kk), qreg[kk], s);
+          mma32(frag_kp(pt_b, h2 + 2 * kk), rreg[kk], racc);
+        }
+        // distances at or beyond E hold no bias (their P rows were clamped)
+        const int dlo = (c0 - 1) * N;
+        if (dlo + N > E) {
+#pragma unroll
+          for (int v = 0; v < 16; ++v)
+            if (dlo + 8 * (v >> 2) + 4 * h2 + (v & 3) >= E) racc[v] = 0.0f;
+        }
+        // R^T accumulator v is distance 8*(v/4) + 4*h2 + v%4 of its chunk
+#pragma unroll
+        for (int g4 = 0; g4 < 4; ++g4) {
+          float* dst = rs + a * C::LS + 8 * g4 + 4 * h2;
+          f32x4 x0, x1;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            x0[e] = racc[4 * g4 + e];
+            x1[e] = rprev[4 * g4 + e];
+          }
+          *reinterpret_cast<f32x4*>(dst) = x0;
+          *reinterpret_cast<f32x4*>(dst + 32) = x1;
+        }
+        rprev = racc;
+        rlast = c0 - 1;
+        wave_lds_fence();
+        const float* src = rs + a * C::LS + 32 + a - 4 * h2;
+#pragma unroll
+        for (int v = 0; v < 16; ++v) s[v] = fmaf(s[v], qk_scale, src[-(8 * (v >> 2) + (v & 3))]);
+        wave_lds_fence();
+      } else {
+        f32x16 s_odd = zero16();
+#pragma unroll
+        for (int kk = 0; kk < D / 16; ++kk) {
+          const bf16x8 kf = frag_kp(kt_b, h2 + 2 * kk);
+          if (kk & 1) mma32(kf, qreg[kk], s_odd);
+          else mma32(kf, qreg[kk], s);
+        }
+#pragma unroll
+        for (int v = 0; v < 16; ++v) s[v] = (s[v] + s_odd[v]) * qk_scale;
+      }
+      if (mask) {
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          const int dd = qa - (j0 + 8 * (v >> 2) + 4 * h2 + (v & 3));
+          if (dd < 0 || (W > 0 && dd >= W)) s[v] = -INFINITY;
+        }
+      }
+
+      f32x16 pexp;
+      float mx = -INFINITY;
+      {
+        const float nm = -p.c2 * m_run;
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          mx = fmaxf(mx, s[v]);
+          pexp[v] = fast_exp2(fmaf(s[v], p.c2, nm));
+        }
+      }
+      mx = pair_max32(mx);
+      if (__builtin_amdgcn_ballot_w64(mx > m_run + lazy) != 0) {
+        const float m_new = fmaxf(m_run, mx);
+        const float corr = fast_exp2(p.c2 * (m_run - m_new));
+        m_run = m_new;
+        l_run *= corr;
+#pragma unroll
+        for (int i = 0; i < D / 32; ++i)
+#pragma unroll
+          for (int v = 0; v < 16; ++v) o[i][v] *= corr;
+        const float nm = -p.c2 * m_run;
+#pragma unroll
+        for (int v = 0; v < 16; ++v) pexp[v] = fast_exp2(fmaf(s[v], p.c2, nm));
+      }
+      float psum = 0.0f;
+#pragma unroll
+      for (int v = 0; v < 16; ++v) psum += pexp[v];
+      l_run += psum;
+
+      // O^T += V^T P^T: the transpose read of PreV<__bf16> with V's swizzle.
+      // Lane (G, s) reads rows 16*c16 + 4*(G/2) + s/4 (+8), columns
+      // 32*db + 16*(G%2) + 4*(s%4): chunk 4*db + 2*(G%2) + (s%4)/2, half s%2.
+      const int Gq = lane >> 4, sq = lane & 15;
+      const int vsw = 2 * ((sq >> 2) & 3);  // rows r and r+8 share r & 3 = s/4
+#pragma unroll
+      for (int c16 = 0; c16 < N / 16; ++c16) {
+        bf16x8 pb;
+#pragma unroll
+        for (int t = 0; t < 8; ++t) pb[t] = T(pexp[8 * c16 + t]);
+        const unsigned char* r0 = vt_b + (16 * c16 + 4 * (Gq >> 1) + (sq >> 2)) * C::ROWB + ((sq & 1) << 3);
+#pragma unroll
+        for (int db = 0; db < D / 32; ++db) {
+          const int q = 4 * db + 2 * (Gq & 1) + ((sq & 3) >> 1);
+          const T* p0 = reinterpret_cast<const T*>(r0 + ((q ^ vsw) << 4));
+          const s16x4 x = lds_read_tr(p0);
+          const s16x4 y = lds_read_tr(p0 + 8 * (C::ROWB / 2));
+          const bf16x8 vf = __builtin_bit_cast(bf16x8, __builtin_shufflevector(x, y, 0, 1, 2, 3, 4, 5, 6, 7));
+          mma32(vf, pb, o[db]);
+        }
+      }
+    }
+    dma_wait();  // this wave's part of tile kt+1 has landed
+  }
+
+  // ---- epilogue: normalise, stage the wave's 32 x D tile in LDS, write whole
+  // rows in 16-byte pieces
+  const float l_tot = pair_sum32(l_run);
+  const float inv = 1.0f / l_tot;
+  __syncthreads();
+  constexpr int OS = D + 8;
+  static_assert(size_t(8) * 32 * OS * sizeof(T) <= C::LDS_TOTAL, "output staging fits the LDS");
+  T* ot = reinterpret_cast<T*>(smem) + size_t(w) * 32 * OS;
+#pragma unroll
+  for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+    for (int g4 = 0; g4 < 4; ++g4)
+      st4_f32<T>(ot + a * OS + db * 32 + g4 * 8 + 4 * h2, o[db][4 * g4] * inv, o[db][4 * g4 + 1] * inv,
+                 o[db][4 * g4 + 2] * inv, o[db][4 * g4 + 3] * inv);
+  wave_lds_fence();
+  typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+#pragma unroll
+  for (int it = 0; it < 8; ++it) {
+    const int i = lane + 64 * it;
+    const int row = i >> 4, cv = i & 15;
+    const int q = q0 + row;
+    if (q < T_)
+      *reinterpret_cast<u32x4*>(static_cast<T*>(p.out) + ((size_t(b) * T_ + q) * Hq + h) * D + cv * 8) =
+          *reinterpret_cast<const u32x4*>(ot + row * OS + cv * 8);
+  }
+  if (p.lse != nullptr && h2 == 0 && qvalid) p.lse[(size_t(b) * Hq + h) * T_ + qa] = (p.c2 * m_run + log2f(l_tot)) * kLn2;
+}
+
+hipError_t launch_prefill_dma(const PrefillArgs& a, hipStream_t stream) {
+  const int n_qt = (a.T + 31) / 32;
+  const long long n_items = (long long)n_qt * a.B * a.Hkv * (a.Hq / a.Hkv / 8);
+  if (n_items > 0x7fffffffLL) return hipErrorInvalidConfiguration;
+  hipLaunchKernelGGL(prefill_dma_kernel, dim3((unsigned)n_items), dim3(DmaCfg::THREADS), 0, stream, a, n_qt,
+                     (int)n_items);
+  return hipGetLastError();
+}
+
 }  // namespace
 
 hipError_t launch_prefill(int dtype, const PrefillArgs& a, hipStream_t stream) {
-  if (dtype == 1) return launch_prefill_tiles<__bf16, 8>(a, stream);
+  if (dtype == 1) {
+    if ((a.Hq / a.Hkv) % 8 == 0) return launch_prefill_dma(a, stream);
+    return launch_prefill_tiles<__bf16, 8>(a, stream);
+  }
   return launch_prefill_tiles<float, 2>(a, stream);
 }
 
