@@ -508,7 +508,7 @@ struct DmaCfg {
   static constexpr int N = 32;
   static constexpr int ROWB = kHeadDim * 2;  // bytes per K / V / P tile row (d_r padded to 128)
   static constexpr int TILEB = N * ROWB;     // 8 KB
-  static constexpr int LS = 2 * N + 4;       // R buffer row stride (floats)
+  static constexpr int LS = 3 * N + 4;       // R buffer row stride (floats): three chunk slots + 4
   static constexpr int THREADS = 512;
   static constexpr size_t OFF_K = 0, OFF_V = 2 * TILEB, OFF_P = 4 * TILEB, OFF_R = 6 * TILEB;
   static constexpr size_t LDS_TOTAL = OFF_R + size_t(8) * 32 * LS * sizeof(float);
@@ -630,11 +630,25 @@ __global__ __launch_bounds__(512, 1) void prefill_dma_kernel(PrefillArgs p, int 
   dma_wait();
   __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0)
 
-  // Per-wave relative-logit buffer: chunk c-1 at columns 0..31, chunk c at
-  // 32..63, so key b of query a (distance 32c + a - b) is column 32 + a - b.
+  // Per-wave relative-logit buffer [query][distance]: chunk k at columns
+  // 32*(k&1), even chunks also at 64..95, so a tile's chunks c-1 and c are
+  // always 64 contiguous columns from 32*((c-1)&1) and each tile writes only
+  // its new chunk; key b of query a (distance 32c + a - b) is column
+  // 32*((c-1)&1) + 32 + a - b.  R^T accumulator v is distance
+  // 8*(v/4) + 4*h2 + v%4 of its chunk.
   float* const rs = Rs + w * 32 * C::LS;
-  f32x16 rprev = zero16();  // chunk rlast, made on the previous tile
-  int rlast = INT_MIN;
+  auto put_chunk = [&](int k, const f32x16& acc) {
+    float* const dst = rs + a * C::LS + 32 * (k & 1) + 4 * h2;
+#pragma unroll
+    for (int g4 = 0; g4 < 4; ++g4) {
+      f32x4 x;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) x[e] = acc[4 * g4 + e];
+      *reinterpret_cast<f32x4*>(dst + 8 * g4) = x;
+      if ((k & 1) == 0) *reinterpret_cast<f32x4*>(dst + 64 + 8 * g4) = x;
+    }
+  };
+  int rlast = INT_MIN;  // newest chunk in the buffer
 
   for (int kt = kt_lo; kt <= kt_hi; ++kt) {
     const int j0 = kt * N;
@@ -665,9 +679,10 @@ __global__ __launch_bounds__(512, 1) void prefill_dma_kernel(PrefillArgs p, int 
           bf16x8 pf[kMaxDr / 16];
 #pragma unroll
           for (int kk = 0; kk < kMaxDr / 16; ++kk) pf[kk] = ld8<T>(prow + min(kk, nk - 1) * 16);
-          rprev = zero16();
+          f32x16 rc = zero16();
 #pragma unroll
-          for (int kk = 0; kk < kMaxDr / 16; ++kk) mma32((rok && kk < nk) ? pf[kk] : zero8<T>(), rreg[kk], rprev);
+          for (int kk = 0; kk < kMaxDr / 16; ++kk) mma32((rok && kk < nk) ? pf[kk] : zero8<T>(), rreg[kk], rc);
+          put_chunk(c0, rc);
         }
         f32x16 racc = zero16();
 #pragma unroll
@@ -682,23 +697,10 @@ __global__ __launch_bounds__(512, 1) void prefill_dma_kernel(PrefillArgs p, int 
           for (int v = 0; v < 16; ++v)
             if (dlo + 8 * (v >> 2) + 4 * h2 + (v & 3) >= E) racc[v] = 0.0f;
         }
-        // R^T accumulator v is distance 8*(v/4) + 4*h2 + v%4 of its chunk
-#pragma unroll
-        for (int g4 = 0; g4 < 4; ++g4) {
-          float* dst = rs + a * C::LS + 8 * g4 + 4 * h2;
-          f32x4 x0, x1;
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            x0[e] = racc[4 * g4 + e];
-            x1[e] = rprev[4 * g4 + e];
-          }
-          *reinterpret_cast<f32x4*>(dst) = x0;
-          *reinterpret_cast<f32x4*>(dst + 32) = x1;
-        }
-        rprev = racc;
+        put_chunk(c0 - 1, racc);
         rlast = c0 - 1;
         wave_lds_fence();
-        const float* src = rs + a * C::LS + 32 + a - 4 * h2;
+        const float* src = rs + a * (C::LS + 1) + 32 * ((c0 - 1) & 1) + 32 - 4 * h2;
 #pragma unroll
         for (int v = 0; v < 16; ++v) s[v] = fmaf(s[v], qk_scale, src[-(8 * (v >> 2) + (v & 3))]);
         wave_lds_fence();
