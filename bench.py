@@ -29,7 +29,7 @@ PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA, published
 PEAK_HBM_GBPS = 8000.0      # MI355X HBM3E, published
 PREFILL_WORKLOAD = "swa_prefill_8k"
 DECODE_WORKLOAD = "decode_64x8k"
-PREFILL_KERNEL = "prefill_kernel"
+PREFILL_KERNEL = "prefill_dma_kernel"  # the bf16 path for eight or more query heads per kv head
 DECODE_KERNEL = "decode_split_kernel"
 
 
