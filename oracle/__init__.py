@@ -7,7 +7,9 @@ Only ``tests/``, ``__graft_entry__.smoke()`` and the ``cpu_baseline`` leg of
 from .relattn_oracle import (  # noqa: F401
     attention_weights,
     brute_force_prefill,
+    cache_rows,
     decode,
+    extend,
     logit_rows,
     prefill,
     rel_logits,

@@ -41,6 +41,12 @@ Readings where the pages are silent (each listed in the design notes):
   full causal.
 * decode: the single query sits at position L-1 of its cache and sees keys
   0..L-1 (its own key included).
+* extend (chunked prefill over a cache, the "extend" kernels of the SGLang
+  page's AMD path): sequence b holds kv_len[b] tokens in its cache, the last
+  n_b of which are the new query rows; new row t sits at position
+  kv_len[b] - n_b + t.  s uses Lseq = kv_len[b], one scalar per sequence.
+  A paged cache stores key j of sequence b in slot j % page_size of page
+  block_table[b][j // page_size].
 
 Parity status: every function here is pinned by the CPU tests in
 ``tests/test_oracle_pins.py`` (brute force on tiny inputs, a hand-worked
@@ -64,6 +70,8 @@ __all__ = [
     "sheared_bias",
     "prefill",
     "decode",
+    "extend",
+    "cache_rows",
     "brute_force_prefill",
     "attention_weights",
 ]
@@ -214,6 +222,65 @@ def decode(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, r: Optional[torch.
                 o, l = _softmax_rows(lg, V)
                 out[b, h] = o[0]
                 lse[b, h] = l[0]
+    return out, lse
+
+
+def cache_rows(cache: torch.Tensor, b: int, n: int, block_table=None, page_size: int = 0) -> torch.Tensor:
+    """Rows 0..n-1 of sequence b of a KV cache, as [n, Hkv, D].
+
+    Contiguous cache [B, Lcap, Hkv, D]: rows cache[b, :n].  Paged cache
+    [num_pages, page_size, Hkv, D] with ``block_table`` [B][max_pages]: row j
+    is slot j % page_size of page block_table[b][j // page_size].
+    """
+    if block_table is None:
+        return cache[b, :n]
+    idx = [(int(block_table[b][j // page_size]), j % page_size) for j in range(n)]
+    return torch.stack([cache[pg, sl] for pg, sl in idx]) if n > 0 else cache[0, :0]
+
+
+def extend(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, r: Optional[torch.Tensor],
+           P: Optional[torch.Tensor], alpha: float, rel_extent: int, window: int,
+           log_scale: bool, q_start: Sequence[int], kv_len: Sequence[int],
+           block_table=None, page_size: int = 0, row_block: int = 1024):
+    """New query rows of several sequences against their KV caches.
+
+    q [total_q, Hq, D] and r [total_q, Hq, d_r] are packed: rows
+    q_start[b] .. q_start[b+1]-1 belong to sequence b.  k/v is a contiguous
+    cache [B, Lcap, Hkv, D] or, with ``block_table``, a paged one (see
+    ``cache_rows``).  New row t of sequence b sits at position
+    kv_len[b] - n_b + t (n_b its number of new rows) and sees the cached keys
+    0..position under the causal / window mask, with the bias of the eq. for
+    l(i,j,h); s uses Lseq = kv_len[b].  Returns out [total_q, Hq, D] and
+    lse [Hq, total_q], fp64.
+    """
+    total_q, Hq, D = q.shape
+    Hkv = k.shape[2]
+    G = Hq // Hkv
+    B = len(kv_len)
+    out = torch.zeros(total_q, Hq, D, dtype=torch.float64)
+    lse = torch.zeros(Hq, total_q, dtype=torch.float64)
+    for b in range(B):
+        L = int(kv_len[b])
+        r0, r1 = int(q_start[b]), int(q_start[b + 1])
+        n = r1 - r0
+        if n == 0:
+            continue
+        s = scale_factor(L, log_scale)
+        Kb = cache_rows(k, b, L, block_table, page_size)
+        Vb = cache_rows(v, b, L, block_table, page_size)
+        pos_all = torch.arange(L - n, L, dtype=torch.int64)
+        for g in range(Hkv):
+            K = Kb[:, g].to(torch.float64)
+            V = Vb[:, g].to(torch.float64)
+            for h in range(g * G, (g + 1) * G):
+                for t0 in range(0, n, row_block):
+                    pos = pos_all[t0:t0 + row_block]
+                    rows = torch.arange(r0 + t0, r0 + t0 + pos.numel())
+                    lg = logit_rows(q[rows, h], r[rows, h] if rel_extent > 0 else None, pos,
+                                    K, P, alpha, rel_extent, window, s)
+                    o, l = _softmax_rows(lg, V)
+                    out[rows, h] = o
+                    lse[h, rows] = l
     return out, lse
 
 

@@ -289,3 +289,87 @@ def test_oracle_accepts_bf16_inputs_exactly():
     a, _ = oracle.prefill(c["q"], c["k"], c["v"], c["r"], c["P"], 0.25, 6, 0)
     b, _ = oracle.prefill(*(c[n].double() for n in ("q", "k", "v", "r", "P")), 0.25, 6, 0)
     assert torch.equal(a, b)
+
+
+# ---------------------------------------------------------------- extend (chunked prefill over a cache)
+
+def _extend_from_full(seqs, n_new):
+    """Pack the last n_new[b] rows of full sequences (dicts of [1,T,...] tensors) as extend inputs."""
+    q = torch.cat([c["q"][0, c["q"].shape[1] - n:] for c, n in zip(seqs, n_new)])
+    r = torch.cat([c["r"][0, c["r"].shape[1] - n:] for c, n in zip(seqs, n_new)])
+    Lcap = max(c["k"].shape[1] for c in seqs)
+    Hkv, D = seqs[0]["k"].shape[2], seqs[0]["k"].shape[3]
+    k = torch.zeros(len(seqs), Lcap, Hkv, D, dtype=torch.float64)
+    v = torch.zeros_like(k)
+    for b, c in enumerate(seqs):
+        k[b, :c["k"].shape[1]] = c["k"][0]
+        v[b, :c["v"].shape[1]] = c["v"][0]
+    q_start = [0]
+    for n in n_new:
+        q_start.append(q_start[-1] + n)
+    return q, r, k, v, q_start, [c["q"].shape[1] for c in seqs]
+
+
+@pytest.mark.parametrize("log_scale,W", [(False, 0), (False, 6), (True, 0)])
+def test_extend_rows_equal_prefill_of_whole_sequence(log_scale, W):
+    """Chunked prefill is exact: the new rows over a cached prefix are the last
+    rows of the prefill of the whole sequence (s from its full length)."""
+    Ts = [4200, 4500] if log_scale else [23, 40]
+    n_new = [5, 17]
+    seqs = [_small_case(B=1, T=T, Hq=4, Hkv=2, D=8, d_r=4, E=9, seed=T) for T in Ts]
+    for c in seqs:
+        c["P"] = seqs[0]["P"]
+    q, r, k, v, q_start, kv_len = _extend_from_full(seqs, n_new)
+    out, lse = oracle.extend(q, k, v, r, seqs[0]["P"], 0.4, 9, W, log_scale, q_start, kv_len)
+    for b, (c, n) in enumerate(zip(seqs, n_new)):
+        T = c["q"].shape[1]
+        rows = list(range(T - n, T))
+        ref, lref = oracle.prefill(c["q"], c["k"], c["v"], c["r"], c["P"], 0.4, 9, W, log_scale, rows=rows)
+        assert torch.allclose(out[q_start[b]:q_start[b + 1]], ref[0], atol=1e-13, rtol=0)
+        assert torch.allclose(lse[:, q_start[b]:q_start[b + 1]], lref[0], atol=1e-12, rtol=0)
+
+
+def test_extend_matches_brute_force_and_skips_empty_sequences():
+    """Scalar brute force on tiny sequences; a sequence with no new rows
+    contributes nothing, and one with no prefix is a plain prefill."""
+    seqs = [_small_case(B=1, T=T, Hq=2, Hkv=1, D=4, d_r=3, E=4, seed=30 + T) for T in (7, 5, 6)]
+    for c in seqs:
+        c["P"] = seqs[0]["P"]
+    n_new = [3, 0, 6]
+    q, r, k, v, q_start, kv_len = _extend_from_full(seqs, n_new)
+    out, lse = oracle.extend(q, k, v, r, seqs[0]["P"], 0.6, 4, 0, False, q_start, kv_len)
+    for b, (c, n) in enumerate(zip(seqs, n_new)):
+        if n == 0:
+            continue
+        T = c["q"].shape[1]
+        bo, bl = oracle.brute_force_prefill(c["q"].tolist(), c["k"].tolist(), c["v"].tolist(), c["r"].tolist(),
+                                            c["P"].tolist(), 0.6, 4, 0)
+        for t in range(n):
+            i = T - n + t
+            for h in range(2):
+                assert max(abs(x - y) for x, y in zip(out[q_start[b] + t, h].tolist(), bo[0][i][h])) < 1e-12
+                assert abs(lse[h, q_start[b] + t].item() - bl[0][h][i]) < 1e-12
+
+
+def test_extend_paged_cache_equals_contiguous():
+    """A paged cache (pages at a shuffled permutation of slots) holds the same rows."""
+    x = tinputs.make_extend_inputs([70, 9, 64], [11, 9, 1], 4, 2, 16, 16, 12, "bf16", seed=4, page_size=8)
+    qs, kl = x["q_start"].tolist(), x["kv_len"].tolist()
+    a, la = oracle.extend(x["q"], x["k"], x["v"], x["r"], x["P"], 0.3, 12, 0, False, qs, kl)
+    b, lb = oracle.extend(x["q"], x["k_pages"], x["v_pages"], x["r"], x["P"], 0.3, 12, 0, False, qs, kl,
+                          block_table=x["block_table"].tolist(), page_size=8)
+    assert torch.equal(a, b) and torch.equal(la, lb)
+    # the page permutation really is a permutation (no two pages share a slot)
+    used = [x["block_table"][bb, p].item() for bb, L in enumerate(kl) for p in range((L + 7) // 8)]
+    assert sorted(used) == list(range(len(used)))
+
+
+@pytest.mark.parametrize("log_scale", [False, True])
+def test_decode_equals_extend_of_one_row(log_scale):
+    L = 4300 if log_scale else 50
+    c = _small_case(B=2, T=L, Hq=4, Hkv=2, D=8, d_r=4, E=12, seed=77)
+    dec, ldec = oracle.decode(c["q"][:, L - 1], c["k"], c["v"], c["r"][:, L - 1], c["P"], 0.4, 12, 0, log_scale)
+    ext, lext = oracle.extend(c["q"][:, L - 1], c["k"], c["v"], c["r"][:, L - 1], c["P"], 0.4, 12, 0, log_scale,
+                              [0, 1, 2], [L, L])
+    assert torch.allclose(ext, dec, atol=1e-13, rtol=0)
+    assert torch.allclose(lext, ldec.t(), atol=1e-12, rtol=0)

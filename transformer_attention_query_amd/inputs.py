@@ -11,6 +11,11 @@ P ~ N(0, 0.02^2)); every tensor is then rounded to the workload dtype.
 
 * prefill: q [B,T,Hq,D], k [B,T,Hkv,D], v [B,T,Hkv,D], r [B,T,Hq,d_r], P [d_r,E]
 * decode:  q [B,Hq,D],   k [B,L,Hkv,D], v [B,L,Hkv,D], r [B,Hq,d_r],   P [d_r,E]
+* extend:  q [total_q,Hq,D] (packed new rows), k, v [B,Lcap,Hkv,D] (caches),
+           r [total_q,Hq,d_r], P [d_r,E]; then, without further draws, the
+           same caches cut into pages of ``page_size`` rows, placed at a
+           seeded random permutation of page slots (a block table), when a
+           page size is given.
 
 P is drawn in the orientation of the method's notation (column d holds the
 projection for distance d).  The library takes it distance-major, as
@@ -26,8 +31,8 @@ from typing import Dict, Optional
 
 import torch
 
-__all__ = ["Workload", "WORKLOADS", "make_prefill_inputs", "make_decode_inputs", "make_inputs",
-           "torch_dtype"]
+__all__ = ["Workload", "WORKLOADS", "make_prefill_inputs", "make_decode_inputs", "make_extend_inputs",
+           "make_inputs", "torch_dtype"]
 
 
 def torch_dtype(name: str) -> torch.dtype:
@@ -38,10 +43,10 @@ def torch_dtype(name: str) -> torch.dtype:
 class Workload:
     """One named relative-attention workload (shapes, masks and dtype)."""
     name: str
-    kind: str            # "prefill" or "decode"
+    kind: str            # "prefill", "decode" or "extend"
     dtype: str           # "bf16" or "fp32"
     B: int
-    T: int               # prefill: sequence length; decode: kv length L
+    T: int               # prefill: sequence length; decode, extend: kv length L
     Hq: int
     Hkv: int
     D: int
@@ -51,6 +56,8 @@ class Workload:
     log_scale: bool = False
     alpha: float = 1.0 / math.sqrt(128.0)
     num_splits: int = 0  # decode only; 0 = library's choice
+    n_new: int = 0       # extend only: new query rows per sequence (the last n_new of its T)
+    page_size: int = 0   # extend only: rows per KV page; 0 = contiguous caches
     notes: str = field(default="", compare=False)
 
 
@@ -71,6 +78,10 @@ WORKLOADS: Dict[str, Workload] = {
     "decode_1x1m_log": Workload(
         "decode_1x1m_log", "decode", "bf16", B=1, T=1 << 20, Hq=16, Hkv=2, D=128, d_r=128, E=1024,
         log_scale=True, notes="1 sequence x 1 token, kv length 2^20, log-scale s = 5/3"),
+    "extend_4x1k_8k_paged": Workload(
+        "extend_4x1k_8k_paged", "extend", "bf16", B=4, T=8192, Hq=16, Hkv=2, D=128, d_r=128, E=1024,
+        n_new=1024, page_size=64,
+        notes="chunked prefill: 4 sequences x 1024 new rows over 7168 cached ones, paged KV (64 rows)"),
 }
 
 
@@ -112,8 +123,59 @@ def make_decode_inputs(B: int, L: int, Hq: int, Hkv: int, D: int, d_r: int, E: i
     return out
 
 
+def make_extend_inputs(kv_lens, new_lens, Hq: int, Hkv: int, D: int, d_r: int, E: int,
+                       dtype: str = "bf16", seed: int = 0, p_std: float = 0.02, page_size: int = 0,
+                       device: Optional[str] = None) -> Dict[str, torch.Tensor]:
+    """Seeded extend inputs: sequence b has kv_lens[b] cached rows, the last
+    new_lens[b] of which are its new query rows (packed in q and r).
+
+    Returns q, r, k, v (contiguous caches [B, Lcap, Hkv, D], Lcap = max kv
+    length), P, P_cols, q_start [B+1] and kv_len [B] (int32); with a page size
+    also k_pages, v_pages [num_pages, page_size, Hkv, D] and block_table
+    [B, max_pages] (int32, unused entries 0).
+    """
+    B = len(kv_lens)
+    assert len(new_lens) == B and all(0 <= n <= L for n, L in zip(new_lens, kv_lens))
+    gen = torch.Generator("cpu").manual_seed(seed)
+    dt = torch_dtype(dtype)
+    total_q = int(sum(new_lens))
+    Lcap = max(max(kv_lens), 1)
+    q = _draw(gen, (total_q, Hq, D)).to(dt)
+    k = _draw(gen, (B, Lcap, Hkv, D)).to(dt)
+    v = _draw(gen, (B, Lcap, Hkv, D)).to(dt)
+    r = _draw(gen, (total_q, Hq, d_r)).to(dt)
+    P = (_draw(gen, (d_r, E)) * p_std).to(dt)
+    q_start = torch.tensor([0] + list(torch.cumsum(torch.tensor(list(new_lens)), 0).tolist()), dtype=torch.int32)
+    out = {"q": q, "k": k, "v": v, "r": r, "P": P, "P_cols": P.t().contiguous(), "q_start": q_start,
+           "kv_len": torch.tensor(list(kv_lens), dtype=torch.int32)}
+    if page_size > 0:
+        pages = [(L + page_size - 1) // page_size for L in kv_lens]
+        max_pages = max(max(pages), 1)
+        n_pages = max(sum(pages), 1)
+        perm = torch.randperm(n_pages, generator=gen)
+        kp = torch.zeros(n_pages, page_size, Hkv, D, dtype=dt)
+        vp = torch.zeros(n_pages, page_size, Hkv, D, dtype=dt)
+        table = torch.zeros(B, max_pages, dtype=torch.int32)
+        slot = 0
+        for b, L in enumerate(kv_lens):
+            for pg in range(pages[b]):
+                dst = int(perm[slot])
+                slot += 1
+                table[b, pg] = dst
+                lo, hi = pg * page_size, min(L, (pg + 1) * page_size)
+                kp[dst, :hi - lo] = k[b, lo:hi]
+                vp[dst, :hi - lo] = v[b, lo:hi]
+        out.update(k_pages=kp, v_pages=vp, block_table=table)
+    if device is not None:
+        out = {n: t.to(device) for n, t in out.items()}
+    return out
+
+
 def make_inputs(w: Workload, seed: int = 0, device: Optional[str] = None) -> Dict[str, torch.Tensor]:
     """Inputs of a named workload."""
+    if w.kind == "extend":
+        return make_extend_inputs([w.T] * w.B, [w.n_new] * w.B, w.Hq, w.Hkv, w.D, w.d_r, w.E, w.dtype, seed,
+                                  page_size=w.page_size, device=device)
     if w.kind == "prefill":
         return make_prefill_inputs(w.B, w.T, w.Hq, w.Hkv, w.D, w.d_r, w.E, w.dtype, seed, device=device)
     return make_decode_inputs(w.B, w.T, w.Hq, w.Hkv, w.D, w.d_r, w.E, w.dtype, seed, device=device)
