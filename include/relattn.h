@@ -77,6 +77,41 @@ int rel_attn_prefill(const void* q, const void* k, const void* v, const void* r,
                      void* stream);
 
 /*
+ * Extend: the new rows of several sequences against their KV caches
+ * (chunked prefill over a cached prefix, packed variable-length batches,
+ * paged caches -- the "extend" kernels of the SGLang page's AMD path).
+ * Sequence b holds kv_len[b] tokens in its cache, the last
+ * n_b = q_start[b+1] - q_start[b] of which are its new rows: new row t of b
+ * (packed row q_start[b] + t) sits at position kv_len[b] - n_b + t and sees
+ * the cached keys at positions 0 .. its own under the causal / window mask,
+ * with the relative bias by distance as in prefill.  s uses Lseq = kv_len[b]
+ * (one scale per sequence, computed on the device in float32).
+ *   q [total_q, Hq, D]   r [total_q, Hq, d_r]   P_cols [E, d_r]
+ *   out [total_q, Hq, D] (dtype)   lse [Hq, total_q] float32 or NULL
+ *   q_start [B+1], kv_len [B]: int32 device arrays (4-byte aligned),
+ *     q_start[0] = 0, non-decreasing, q_start[B] = total_q.
+ *   Contiguous caches (block_table == NULL): k, v [B, cache_len, Hkv, D].
+ *   Paged caches: k, v [num_pages, page_size, Hkv, D]; key j of sequence b
+ *     is slot j % page_size of page block_table[b * max_pages + j / page_size]
+ *     (int32 device array [B, max_pages]); page_size a positive multiple of
+ *     32 (else RA_ERR_UNSUPPORTED).
+ *   max_q: a host bound on every n_b; it sizes the launch.
+ * The device arrays are not read on the host.  Whatever they hold, every
+ * access stays in bounds: kv_len is clamped to the cache capacity (cache_len,
+ * or max_pages * page_size), n_b to [0, min(kv_len[b], max_q)] and to the
+ * packed rows that remain, page ids to [0, num_pages); out rows and lse
+ * entries that no sequence covers are left untouched.
+ * B == 0, total_q == 0 or max_q == 0 is a no-op that returns RA_OK.
+ */
+int rel_attn_extend(const void* q, const void* k, const void* v, const void* r,
+                    const void* P_cols, void* out, float* lse, int dtype,
+                    int B, int total_q, int max_q, const int* q_start, const int* kv_len,
+                    int cache_len, const int* block_table, int max_pages, int num_pages, int page_size,
+                    int Hq, int Hkv, int D, int d_r,
+                    float alpha, int rel_extent, int window, int log_scale,
+                    void* stream);
+
+/*
  * Decode plan: a pure function of the shape.  Writes the number of KV splits
  * the decode call will use (num_splits_req > 0 asks for that many; the plan
  * may use fewer so that every split holds at least one 32-key step; 0 lets

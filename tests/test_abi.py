@@ -35,7 +35,7 @@ def _declared_functions():
 
 def test_header_declares_the_boundary():
     names = _declared_functions()
-    for n in ("rel_attn_prefill", "rel_attn_decode", "rel_attn_decode_plan", "rel_logits",
+    for n in ("rel_attn_prefill", "rel_attn_extend", "rel_attn_decode", "rel_attn_decode_plan", "rel_logits",
               "rel_attn_last_error", "rel_attn_version", "rel_attn_scale_factor"):
         assert n in names
 
@@ -203,3 +203,38 @@ def test_scale_factor_reading(lib):
     assert f(1, 4096) == 1.0 and f(1, 100) == 1.0
     assert abs(f(1, 32768) - 1.25) < 1e-15
     assert abs(f(1, 1 << 20) - 5.0 / 3.0) < 1e-15
+
+
+def _extend(lib, **kw):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, r=FAKE, P=FAKE, out=FAKE + 0x1000, lse=None, dtype=RA_BF16, B=2,
+             total_q=10, max_q=8, q_start=FAKE, kv_len=FAKE, cache_len=64, block_table=None, max_pages=0,
+             num_pages=0, page_size=0, Hq=8, Hkv=1, D=128, d_r=64, alpha=0.1, E=32, W=0, ls=0)
+    a.update(kw)
+    return lib.rel_attn_extend(a["q"], a["k"], a["v"], a["r"], a["P"], a["out"], a["lse"], a["dtype"], a["B"],
+                               a["total_q"], a["max_q"], a["q_start"], a["kv_len"], a["cache_len"],
+                               a["block_table"], a["max_pages"], a["num_pages"], a["page_size"], a["Hq"],
+                               a["Hkv"], a["D"], a["d_r"], a["alpha"], a["E"], a["W"], a["ls"], None)
+
+
+@pytest.mark.parametrize("kw,code,frag", [
+    (dict(block_table=FAKE, page_size=48, max_pages=4, num_pages=8), RA_ERR_UNSUPPORTED, "page_size"),
+    (dict(block_table=FAKE, page_size=0, max_pages=4, num_pages=8), RA_ERR_UNSUPPORTED, "page_size"),
+    (dict(block_table=FAKE, page_size=64, max_pages=0, num_pages=8), RA_ERR_INVALID_ARG, "max_pages"),
+    (dict(cache_len=0), RA_ERR_INVALID_ARG, "cache_len"),
+    (dict(q_start=None), RA_ERR_INVALID_ARG, "q_start"),
+    (dict(kv_len=FAKE + 2), RA_ERR_INVALID_ARG, "aligned"),
+    (dict(max_q=-1), RA_ERR_INVALID_ARG, "max_q"),
+    (dict(D=64), RA_ERR_UNSUPPORTED, "head dim"),
+    (dict(d_r=40), RA_ERR_UNSUPPORTED, "d_r"),
+    (dict(out=FAKE), RA_ERR_INVALID_ARG, "alias"),
+    (dict(Hq=6, Hkv=4), RA_ERR_INVALID_ARG, "multiple"),
+    (dict(r=None), RA_ERR_INVALID_ARG, "r is NULL"),
+])
+def test_extend_rejects_bad_arguments(lib, kw, code, frag):
+    assert _extend(lib, **kw) == code
+    assert frag in lib.rel_attn_last_error().decode()
+
+
+def test_extend_empty_is_a_noop(lib):
+    for kw in (dict(B=0), dict(total_q=0), dict(max_q=0)):
+        assert _extend(lib, q=None, k=None, v=None, out=None, q_start=None, kv_len=None, **kw) == RA_OK

@@ -1,0 +1,85 @@
+"""GPU parity of the extend path (new rows of packed sequences over their KV
+caches, contiguous or paged) through the C ABI against the fp64 oracle:
+prefixes of different lengths, sequences with no prefix, one new row or none,
+rows that start in the middle of a tile, windows, the log-scale per sequence,
+GQA ratios that take both workgroup shapes, and fp32."""
+
+import zlib
+
+import pytest
+import torch
+
+import oracle
+import transformer_attention_query_amd as ra
+from transformer_attention_query_amd import inputs as tinputs
+from parity import assert_close
+
+pytestmark = pytest.mark.gpu
+
+ALPHA = 1.0 / 128 ** 0.5
+
+# name, dtype, kv_lens, new_lens, Hq, Hkv, d_r, E, W, log_scale, page_size (0 = contiguous)
+CASES = [
+    ("g8_contig", "bf16", [300, 64, 1000], [37, 64, 1], 8, 1, 32, 100, 0, False, 0),
+    ("g4_paged32_window", "bf16", [513, 77, 1], [200, 5, 1], 8, 2, 64, 64, 50, False, 32),
+    ("g8_paged64_empty_seq", "bf16", [129, 700, 40], [129, 0, 33], 16, 2, 128, 300, 0, False, 64),
+    ("mha_paged128_E1", "bf16", [260, 31], [100, 31], 3, 3, 16, 1, 0, False, 128),
+    ("g8_log_scale", "bf16", [5000, 4200], [40, 70], 8, 1, 64, 200, 0, True, 64),
+    ("fp32_paged32", "fp32", [90, 200], [90, 45], 4, 2, 32, 50, 17, False, 32),
+    ("fp32_contig_E0", "fp32", [70, 33], [7, 33], 2, 1, 16, 0, 0, False, 0),
+]
+
+
+def _run(x, E, W, ls, page_size, alpha=ALPHA):
+    xd = {n: t.cuda() for n, t in x.items()}
+    paged = page_size > 0
+    new = (xd["q_start"][1:] - xd["q_start"][:-1]).cpu()
+    out, lse = ra.extend(xd["q"], xd["k_pages"] if paged else xd["k"], xd["v_pages"] if paged else xd["v"],
+                         xd["r"], xd["P_cols"] if E > 0 else None, alpha, E, W, ls, xd["q_start"], xd["kv_len"],
+                         int(new.max()), block_table=xd["block_table"] if paged else None)
+    torch.cuda.synchronize()
+    return out, lse
+
+
+@pytest.mark.parametrize("case", CASES, ids=[c[0] for c in CASES])
+def test_extend_matches_oracle(case):
+    name, dt, kv_lens, new_lens, Hq, Hkv, d_r, E, W, ls, page = case
+    x = tinputs.make_extend_inputs(kv_lens, new_lens, Hq, Hkv, 128, d_r, max(E, 1), dt,
+                                   seed=zlib.crc32(name.encode()) % 1000, page_size=page)
+    if E == 0:
+        x["P_cols"] = x["P_cols"][:0]
+    out, lse = _run(x, E, W, ls, page)
+    ref, lref = oracle.extend(x["q"], x["k"], x["v"], x["r"], x["P"], ALPHA, E, W, ls,
+                              x["q_start"].tolist(), x["kv_len"].tolist())
+    assert_close(out, ref, x["q"].dtype, name, lse, lref)
+
+
+@pytest.mark.parametrize("heads", [(8, 1), (8, 2)], ids=["G8", "G4"])
+def test_extend_bias_sensitivity_paged(heads):
+    """Large relative logits: a slip in positions, the shear or the page
+    mapping changes the output by O(1)."""
+    Hq, Hkv = heads
+    x = tinputs.make_extend_inputs([600, 333], [150, 90], Hq, Hkv, 128, 64, 200, "bf16", seed=9, page_size=32)
+    x["P"] = (x["P"].float() * 50).to(torch.bfloat16)
+    x["P_cols"] = x["P"].t().contiguous()
+    out, lse = _run(x, 200, 0, False, 32)
+    ref, lref = oracle.extend(x["q"], x["k"], x["v"], x["r"], x["P"], ALPHA, 200, 0, False,
+                              x["q_start"].tolist(), x["kv_len"].tolist())
+    assert_close(out, ref, torch.bfloat16, "P_x50", lse, lref)
+
+
+def test_extend_of_whole_sequences_equals_prefill():
+    """No prefix: extend over T new rows is a prefill of length T (both paths
+    against the oracle, and against each other within the tolerance)."""
+    T, Hq, Hkv = 300, 8, 1
+    x = tinputs.make_extend_inputs([T, T], [T, T], Hq, Hkv, 128, 64, 128, "bf16", seed=21)
+    out, lse = _run(x, 128, 0, False, 0)
+    q = x["q"].view(2, T, Hq, 128).cuda()
+    r = x["r"].view(2, T, Hq, 64).cuda()
+    pout, plse = ra.prefill(q, x["k"].cuda(), x["v"].cuda(), r, x["P_cols"].cuda(), ALPHA, 128, 0, False)
+    torch.cuda.synchronize()
+    ref, lref = oracle.extend(x["q"], x["k"], x["v"], x["r"], x["P"], ALPHA, 128, 0, False,
+                              x["q_start"].tolist(), x["kv_len"].tolist())
+    assert_close(out, ref, torch.bfloat16, "extend", lse, lref)
+    assert_close(pout.view(2 * T, Hq, 128), ref, torch.bfloat16, "prefill",
+                 plse.permute(1, 0, 2).reshape(Hq, 2 * T), lref)

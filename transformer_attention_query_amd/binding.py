@@ -16,7 +16,7 @@ from typing import Optional, Tuple
 
 import torch
 
-__all__ = ["RelAttnError", "library_path", "load_library", "prefill", "decode", "decode_plan",
+__all__ = ["RelAttnError", "library_path", "load_library", "prefill", "extend", "decode", "decode_plan",
            "rel_logits", "scale_factor", "version"]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -45,6 +45,9 @@ def _declare(lib):
     lib.rel_attn_prefill.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32,
                                      f32, i32, i32, i32, vp]
     lib.rel_attn_prefill.restype = i32
+    lib.rel_attn_extend.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, vp, vp, i32, vp, i32, i32,
+                                    i32, i32, i32, i32, i32, f32, i32, i32, i32, vp]
+    lib.rel_attn_extend.restype = i32
     lib.rel_attn_decode_plan.argtypes = [i32, i32, i32, i32, i32, i32, i32, i32,
                                          c.POINTER(i32), c.POINTER(sz)]
     lib.rel_attn_decode_plan.restype = i32
@@ -160,6 +163,76 @@ def prefill(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, r: Optional[torch
     _check(lib.rel_attn_prefill(_ptr(q), _ptr(k), _ptr(v), _ptr(r), _ptr(P_cols), _ptr(out), _ptr(lse),
                                 _DTYPE_CODE[dt], B, T, Hq, Hkv, D, d_r, float(alpha), int(rel_extent),
                                 int(window), 1 if log_scale else 0, _stream(dev)))
+    return out, lse
+
+
+def extend(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, r: Optional[torch.Tensor],
+           P_cols: Optional[torch.Tensor], alpha: float, rel_extent: int, window: int,
+           log_scale: bool, q_start: torch.Tensor, kv_len: torch.Tensor, max_q: int,
+           block_table: Optional[torch.Tensor] = None, return_lse: bool = True,
+           out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None
+           ) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+    """New rows of packed sequences against their KV caches (rel_attn_extend).
+
+    q [total_q,Hq,D], r [total_q,Hq,d_r] packed by ``q_start`` [B+1] (int32,
+    device); ``kv_len`` [B] (int32, device) cached tokens per sequence, the
+    last q_start[b+1]-q_start[b] of which are the new rows; ``max_q`` a host
+    bound on the new rows of any sequence.  k/v: contiguous caches
+    [B,cache_len,Hkv,D], or with ``block_table`` [B,max_pages] (int32, device)
+    paged caches [num_pages,page_size,Hkv,D].  Returns out [total_q,Hq,D] and
+    lse [Hq,total_q] fp32 (or None).
+    """
+    lib = load_library()
+    dev = q.device
+    dt = q.dtype
+    if dt not in _DTYPE_CODE:
+        raise TypeError(f"unsupported dtype {dt}")
+    _need(q, "q", dt, dev, 3)
+    _need(k, "k", dt, dev, 4)
+    _need(v, "v", dt, dev, 4)
+    _need(q_start, "q_start", torch.int32, dev, 1)
+    _need(kv_len, "kv_len", torch.int32, dev, 1)
+    total_q, Hq, D = q.shape
+    B = kv_len.shape[0]
+    if q_start.shape[0] != B + 1:
+        raise ValueError(f"q_start must have B+1 = {B + 1} entries, got {q_start.shape[0]}")
+    if v.shape != k.shape:
+        raise ValueError(f"v shape {tuple(v.shape)} differs from k {tuple(k.shape)}")
+    Hkv = k.shape[2]
+    if block_table is None:
+        cache_len, max_pages, num_pages, page_size = k.shape[1], 0, 0, 0
+        if k.shape[0] != B:
+            raise ValueError(f"contiguous caches must be [B={B}, cache_len, Hkv, D], got {tuple(k.shape)}")
+    else:
+        _need(block_table, "block_table", torch.int32, dev, 2)
+        if block_table.shape[0] != B:
+            raise ValueError(f"block_table must be [B={B}, max_pages], got {tuple(block_table.shape)}")
+        cache_len, max_pages, num_pages, page_size = 0, block_table.shape[1], k.shape[0], k.shape[1]
+    d_r = 0
+    if rel_extent > 0:
+        _need(r, "r", dt, dev, 3)
+        _need(P_cols, "P_cols", dt, dev, 2)
+        d_r = r.shape[2]
+        if r.shape[:2] != (total_q, Hq):
+            raise ValueError(f"r shape {tuple(r.shape)} does not match q")
+        if P_cols.shape != (rel_extent, d_r):
+            raise ValueError(f"P_cols must be [rel_extent={rel_extent}, d_r={d_r}], got {tuple(P_cols.shape)}")
+    else:
+        r = None
+        P_cols = None
+    if out is None:
+        out = torch.empty_like(q)
+    else:
+        _need(out, "out", dt, dev, 3)
+    if return_lse and lse is None:
+        lse = torch.empty(Hq, total_q, dtype=torch.float32, device=dev)
+    elif not return_lse:
+        lse = None
+    _check(lib.rel_attn_extend(_ptr(q), _ptr(k), _ptr(v), _ptr(r), _ptr(P_cols), _ptr(out), _ptr(lse),
+                               _DTYPE_CODE[dt], B, total_q, int(max_q), _ptr(q_start), _ptr(kv_len),
+                               cache_len, _ptr(block_table), max_pages, num_pages, page_size,
+                               Hq, Hkv, D, d_r, float(alpha), int(rel_extent), int(window),
+                               1 if log_scale else 0, _stream(dev)))
     return out, lse
 
 

@@ -102,6 +102,50 @@ int rel_attn_prefill(const void* q, const void* k, const void* v, const void* r,
   return ok();
 }
 
+int rel_attn_extend(const void* q, const void* k, const void* v, const void* r, const void* P_cols, void* out,
+                    float* lse, int dtype, int B, int total_q, int max_q, const int* q_start, const int* kv_len,
+                    int cache_len, const int* block_table, int max_pages, int num_pages, int page_size, int Hq,
+                    int Hkv, int D, int d_r, float alpha, int rel_extent, int window, int log_scale, void* stream) {
+  int rc = check_common(dtype, B, total_q, Hq, Hkv, D, d_r, alpha, rel_extent, window, log_scale, "total_q");
+  if (rc) return rc;
+  if (max_q < 0) return fail(RA_ERR_INVALID_ARG, "max_q = %d < 0", max_q);
+  if (B == 0 || total_q == 0 || max_q == 0) return ok();
+  if ((rc = check_ptr(q, "q", true)) || (rc = check_ptr(k, "k", true)) || (rc = check_ptr(v, "v", true)) ||
+      (rc = check_ptr(out, "out", true)) || (rc = check_ptr(lse, "lse", false)) ||
+      (rc = check_ptr(r, "r", rel_extent > 0)) || (rc = check_ptr(P_cols, "P_cols", rel_extent > 0)))
+    return rc;
+  if (q_start == nullptr || kv_len == nullptr) return fail(RA_ERR_INVALID_ARG, "q_start and kv_len must not be NULL");
+  if ((reinterpret_cast<uintptr_t>(q_start) | reinterpret_cast<uintptr_t>(kv_len) |
+       reinterpret_cast<uintptr_t>(block_table)) & 3u)
+    return fail(RA_ERR_INVALID_ARG, "q_start, kv_len and block_table must be 4-byte aligned");
+  if (out == q || out == k || out == v || out == r) return fail(RA_ERR_INVALID_ARG, "out aliases an input");
+  if (block_table == nullptr) {
+    if (cache_len <= 0) return fail(RA_ERR_INVALID_ARG, "cache_len = %d: contiguous caches need cache_len >= 1", cache_len);
+  } else {
+    if (page_size <= 0 || page_size % 32 != 0)
+      return fail(RA_ERR_UNSUPPORTED, "page_size = %d: supported values are positive multiples of 32", page_size);
+    if (max_pages <= 0 || num_pages <= 0)
+      return fail(RA_ERR_INVALID_ARG, "max_pages = %d and num_pages = %d must be positive", max_pages, num_pages);
+    if ((long long)max_pages * page_size > 0x7fffffffLL)
+      return fail(RA_ERR_UNSUPPORTED, "max_pages * page_size too large");
+  }
+  if ((long long)total_q * Hq > 0x7fffffffLL / relattn::kHeadDim)
+    return fail(RA_ERR_UNSUPPORTED, "total_q * Hq = %lld too large for one launch", (long long)total_q * Hq);
+
+  relattn::PrefillArgs a;
+  a.q = q; a.k = k; a.v = v; a.r = r; a.pc = P_cols; a.out = out; a.lse = lse;
+  a.B = B; a.T = 0; a.Hq = Hq; a.Hkv = Hkv; a.d_r = rel_extent > 0 ? d_r : 16; a.E = rel_extent; a.W = window;
+  a.c1 = (float)((double)alpha * 1.4426950408889634);
+  a.c2 = (float)1.4426950408889634;
+  a.q_start = q_start; a.kv_len = kv_len; a.btab = block_table;
+  a.total_q = total_q; a.max_q = max_q; a.cap = block_table == nullptr ? cache_len : 0;
+  a.max_pages = max_pages; a.num_pages = num_pages; a.page_size = page_size;
+  a.log_scale = log_scale; a.alpha = alpha;
+  hipError_t e = relattn::launch_extend(dtype, a, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(RA_ERR_HIP, "extend launch failed: %s", hipGetErrorString(e));
+  return ok();
+}
+
 int rel_attn_decode_plan(int B, int L, int Hq, int Hkv, int D, int num_splits_req, int window, int rel_extent,
                          int* num_splits_out, size_t* workspace_bytes_out) {
   if (num_splits_out == nullptr || workspace_bytes_out == nullptr)

@@ -134,7 +134,11 @@ struct PrefillCfg {
   static_assert(LDS_TOTAL <= 160 * 1024, "LDS budget of one gfx950 workgroup");
 };
 
-template <typename T, int WAVES>
+// EXT: the extend form (new rows of packed sequences over their KV caches,
+// contiguous or paged; see rel_attn_extend).  Positions are global: query
+// row t of sequence b sits at kv_len[b] - n_b + t, and query tiles are
+// aligned to multiples of M positions, so the chunk arithmetic is unchanged.
+template <typename T, int WAVES, bool EXT>
 __global__ __launch_bounds__(WAVES * 64, 1) void prefill_kernel(PrefillArgs p, int n_qt, int n_items, int hpw) {
   using C = PrefillCfg<T, WAVES>;
   using VS = PreV<T, C::N>;
@@ -147,7 +151,7 @@ __global__ __launch_bounds__(WAVES * 64, 1) void prefill_kernel(PrefillArgs p, i
   T* Pr = reinterpret_cast<T*>(smem + C::LDS_K + C::LDS_V);
   float* Rs = reinterpret_cast<float*>(smem + C::LDS_K + C::LDS_V + C::LDS_P);
 
-  const int T_ = p.T, Hq = p.Hq, Hkv = p.Hkv, G = Hq / Hkv;
+  const int Hq = p.Hq, Hkv = p.Hkv, G = Hq / Hkv;
   const int d_r = p.d_r, E = p.E, W = p.W;
 
   // ---- workgroup -> (q-tile, batch, kv head, head subgroup); wave -> (query
@@ -179,10 +183,34 @@ __global__ __launch_bounds__(WAVES * 64, 1) void prefill_kernel(PrefillArgs p, i
   const int qb = w / hpw;    // query block of this wave
   const int h = kvh * G + hs * hpw + (w % hpw);
 
-  const int i0 = qt * M;
+  // T_: keys (and positions) of this sequence; [pos0, T_) are its query
+  // positions, packed from row row0 of q, r and out
+  int T_ = p.T, pos0 = 0, row0 = 0;
+  float c1 = p.c1, c2 = p.c2;
+  int qt_abs = qt;
+  if constexpr (EXT) {
+    const int cap = p.btab != nullptr ? p.max_pages * p.page_size : p.cap;
+    T_ = max(0, min(p.kv_len[b], cap));
+    row0 = min(max(p.q_start[b], 0), p.total_q);
+    const int n = max(0, min(min(p.q_start[b + 1] - p.q_start[b], min(T_, p.max_q)), p.total_q - row0));
+    pos0 = T_ - n;
+    qt_abs = pos0 / M + qt;
+    if (n == 0 || qt_abs * M >= T_) return;
+    if (p.log_scale) {  // s = max(1, ln(kv_len) / ln(4096)), one per sequence
+      const float sc = fmaxf(1.0f, logf(float(T_)) * (1.0f / 8.317766166719343f));
+      c2 = sc * 1.4426950408889634f;
+      c1 = c2 * p.alpha;
+    }
+  }
+  const int i0 = qt_abs * M;
   const int qw0 = i0 + 32 * qb;
   const int qa = qw0 + a;
-  const bool qvalid = qa < T_;
+  const bool qvalid = qa >= pos0 && qa < T_;
+  // packed row of query position x of this sequence (plain prefill: b*T + x)
+  auto qrow_of = [&](int x) -> size_t {
+    if constexpr (EXT) return size_t(row0 + x - pos0);
+    else return size_t(b) * T_ + x;
+  };
 
   const T* qg = static_cast<const T*>(p.q);
   const T* kg = static_cast<const T*>(p.k);
@@ -192,20 +220,20 @@ __global__ __launch_bounds__(WAVES * 64, 1) void prefill_kernel(PrefillArgs p, i
   const T* pcg = E > 0 ? static_cast<const T*>(p.pc) : kg;
 
   // softmax constants in units of c2 (c2 = s*log2(e) > 0)
-  const float qk_scale = p.c1 / p.c2;
-  const float lazy = kLazyRescaleLog2 / p.c2;
+  const float qk_scale = c1 / c2;
+  const float lazy = kLazyRescaleLog2 / c2;
 
   // ---- this lane's query and relative feature, as MFMA B operands
   v8_t<T> qreg[D / 16];
   {
-    const T* qrow = qg + ((size_t(b) * T_ + (qvalid ? qa : 0)) * Hq + h) * D + 8 * h2;
+    const T* qrow = qg + (qrow_of(qvalid ? qa : pos0) * Hq + h) * D + 8 * h2;
 #pragma unroll
     for (int kk = 0; kk < D / 16; ++kk) qreg[kk] = ld8_or_zero<T>(qrow + kk * 16, qvalid);
   }
   v8_t<T> rreg[kMaxDr / 16];  // zero past d_r
   {
     const int nkr = d_r / 16;
-    const T* rrow = rg + ((size_t(b) * T_ + (qvalid ? qa : 0)) * Hq + h) * d_r + 8 * h2;
+    const T* rrow = rg + (qrow_of(qvalid ? qa : pos0) * Hq + h) * d_r + 8 * h2;
 #pragma unroll
     for (int kk = 0; kk < kMaxDr / 16; ++kk) rreg[kk] = ld8_or_zero<T>(rrow + kk * 16, E > 0 && qvalid && kk < nkr);
   }
@@ -224,19 +252,35 @@ __global__ __launch_bounds__(WAVES * 64, 1) void prefill_kernel(PrefillArgs p, i
   const int kt_hi = i_last / N;
 
   // ---- K/V tile and P chunk prefetch through registers
+  // Key j of this sequence: row b*cap + j of a contiguous cache (b*T + j in
+  // plain prefill), or slot j % page_size of page btab[b][j / page_size] of
+  // a paged one (page_size a multiple of N, so a tile lies in one page; page
+  // ids are clamped to the pool).
   const size_t kv_row_stride = size_t(Hkv) * D;
-  const T* kbase = kg + (size_t(b) * T_ * Hkv + kvh) * D;
-  const T* vbase = vg + (size_t(b) * T_ * Hkv + kvh) * D;
+  const size_t seq_rows = EXT ? size_t(p.cap) : size_t(T_);
+  const T* kbase = kg + (size_t(b) * seq_rows * Hkv + kvh) * D;
+  const T* vbase = vg + (size_t(b) * seq_rows * Hkv + kvh) * D;
   v8_t<T> kpre[C::KV_VECS], vpre[C::KV_VECS];
   auto fetch_kv = [&](int kt) {
     const int j0 = kt * N;
+    const T* kb = kbase;
+    const T* vb = vbase;
+    int jpage0 = 0;  // first key of the tile's page
+    if constexpr (EXT) {
+      if (p.btab != nullptr) {
+        const int pg = min(max(p.btab[size_t(b) * p.max_pages + j0 / p.page_size], 0), p.num_pages - 1);
+        jpage0 = j0 - j0 % p.page_size;
+        kb = kg + (size_t(pg) * p.page_size * Hkv + kvh) * D;
+        vb = vg + (size_t(pg) * p.page_size * Hkv + kvh) * D;
+      }
+    }
 #pragma unroll
     for (int i = 0; i < C::KV_VECS; ++i) {
       const int vid = tid + i * C::THREADS;
       const int j = min(j0 + (vid >> 4), T_ - 1);  // rows past T: clamped, masked later
-      const size_t off = size_t(j) * kv_row_stride + (vid & 15) * 8;
-      kpre[i] = ld8<T>(kbase + off);
-      vpre[i] = ld8<T>(vbase + off);
+      const size_t off = size_t(j - jpage0) * kv_row_stride + (vid & 15) * 8;
+      kpre[i] = ld8<T>(kb + off);
+      vpre[i] = ld8<T>(vb + off);
     }
   };
   auto store_kv = [&]() {
@@ -315,7 +359,7 @@ __global__ __launch_bounds__(WAVES * 64, 1) void prefill_kernel(PrefillArgs p, i
     fetch_p(knew);
 
     // ---- per-wave work on the (32 queries) x (32 keys) sub-tile
-    const bool wdead = qw0 >= T_ || j0 > qw0 + 31 || (W > 0 && qw0 - (j0 + N - 1) >= W);
+    const bool wdead = qw0 >= T_ || qw0 + 31 < pos0 || j0 > qw0 + 31 || (W > 0 && qw0 - (j0 + N - 1) >= W);
     if (!wdead) {
       const bool wband = E > 0 && max(0, qw0 - (j0 + N - 1)) < E;
       const bool wmask = (j0 + N - 1 > qw0) || (W > 0 && qw0 + 31 - j0 >= W);
@@ -397,26 +441,26 @@ __global__ __launch_bounds__(WAVES * 64, 1) void prefill_kernel(PrefillArgs p, i
       f32x16 pexp;
       float mx = -INFINITY;
       {
-        const float nm = -p.c2 * m_run;
+        const float nm = -c2 * m_run;
 #pragma unroll
         for (int v = 0; v < 16; ++v) {
           mx = fmaxf(mx, s[v]);
-          pexp[v] = fast_exp2(fmaf(s[v], p.c2, nm));
+          pexp[v] = fast_exp2(fmaf(s[v], c2, nm));
         }
       }
       mx = pair_max32(mx);
       if (__builtin_amdgcn_ballot_w64(mx > m_run + lazy) != 0) {
         const float m_new = fmaxf(m_run, mx);
-        const float corr = fast_exp2(p.c2 * (m_run - m_new));
+        const float corr = fast_exp2(c2 * (m_run - m_new));
         m_run = m_new;
         l_run *= corr;
 #pragma unroll
         for (int i = 0; i < D / 32; ++i)
 #pragma unroll
           for (int v = 0; v < 16; ++v) o[i][v] *= corr;
-        const float nm = -p.c2 * m_run;
+        const float nm = -c2 * m_run;
 #pragma unroll
-        for (int v = 0; v < 16; ++v) pexp[v] = fast_exp2(fmaf(s[v], p.c2, nm));
+        for (int v = 0; v < 16; ++v) pexp[v] = fast_exp2(fmaf(s[v], c2, nm));
       }
       float psum = 0.0f;
 #pragma unroll
@@ -466,24 +510,29 @@ __global__ __launch_bounds__(WAVES * 64, 1) void prefill_kernel(PrefillArgs p, i
     const int i = lane + 64 * it;
     const int row = i / VPR, cv = i % VPR;
     const int q = qw0 + row;
-    if (q < T_)
-      *reinterpret_cast<u32x4*>(static_cast<T*>(p.out) + ((size_t(b) * T_ + q) * Hq + h) * D + cv * EPV) =
+    if (q >= pos0 && q < T_)
+      *reinterpret_cast<u32x4*>(static_cast<T*>(p.out) + (qrow_of(q) * Hq + h) * D + cv * EPV) =
           *reinterpret_cast<const u32x4*>(ot + row * OS + cv * EPV);
   }
-  if (p.lse != nullptr && h2 == 0 && qvalid) p.lse[(size_t(b) * Hq + h) * T_ + qa] = (p.c2 * m_run + log2f(l_tot)) * kLn2;
+  if (p.lse != nullptr && h2 == 0 && qvalid) {
+    const size_t li = EXT ? size_t(h) * p.total_q + qrow_of(qa) : (size_t(b) * Hq + h) * T_ + qa;
+    p.lse[li] = (c2 * m_run + log2f(l_tot)) * kLn2;
+  }
 }
 
-template <typename T, int WAVES>
+template <typename T, int WAVES, bool EXT = false>
 hipError_t launch_prefill_tiles(const PrefillArgs& a, hipStream_t stream) {
   // heads per workgroup: the largest power of two <= WAVES dividing Hq/Hkv
   const int G = a.Hq / a.Hkv;
   int hpw = 1;
   while (hpw * 2 <= WAVES && G % (hpw * 2) == 0) hpw *= 2;
   const int M = 32 * (WAVES / hpw);
-  const int n_qt = (a.T + M - 1) / M;
+  // extend: the tiles of a sequence cover max_q rows at any alignment
+  const int n_qt = EXT ? (a.max_q + M - 1) / M + 1 : (a.T + M - 1) / M;
   const long long n_items = (long long)n_qt * a.B * a.Hkv * (G / hpw);
   if (n_items > 0x7fffffffLL) return hipErrorInvalidConfiguration;
-  hipLaunchKernelGGL((prefill_kernel<T, WAVES>), dim3((unsigned)n_items), dim3(PrefillCfg<T, WAVES>::THREADS), 0,
+  if (n_items == 0) return hipSuccess;
+  hipLaunchKernelGGL((prefill_kernel<T, WAVES, EXT>), dim3((unsigned)n_items), dim3(PrefillCfg<T, WAVES>::THREADS), 0,
                      stream, a, n_qt, (int)n_items, hpw);
   return hipGetLastError();
 }
@@ -815,6 +864,11 @@ hipError_t launch_prefill_dma(const PrefillArgs& a, hipStream_t stream) {
 }
 
 }  // namespace
+
+hipError_t launch_extend(int dtype, const PrefillArgs& a, hipStream_t stream) {
+  if (dtype == 1) return launch_prefill_tiles<__bf16, 8, true>(a, stream);
+  return launch_prefill_tiles<float, 2, true>(a, stream);
+}
 
 hipError_t launch_prefill(int dtype, const PrefillArgs& a, hipStream_t stream) {
   if (dtype == 1) {

@@ -25,6 +25,15 @@ struct PrefillArgs {
   float* lse;       // may be null
   int B, T, Hq, Hkv, d_r, E, W;
   float c1, c2;
+  // extend only (see rel_attn_extend); device arrays and their host bounds
+  const int* q_start = nullptr;  // [B+1] packed row offsets
+  const int* kv_len = nullptr;   // [B] cached tokens per sequence
+  const int* btab = nullptr;     // [B, max_pages] page ids, or null (contiguous caches)
+  int total_q = 0, max_q = 0;    // packed rows; bound on the new rows of any sequence
+  int cap = 0;                   // contiguous caches: rows per sequence
+  int max_pages = 0, num_pages = 0, page_size = 0;
+  int log_scale = 0;             // s per sequence from kv_len (c1, c2 unused then)
+  float alpha = 0.0f;
 };
 
 struct DecodeArgs {
@@ -75,6 +84,7 @@ DecodePlan plan_decode(int B, int L, int Hq, int Hkv, int num_splits_req, int wi
 
 // Launchers: return hipSuccess or the launch error.  dtype: 1 = bf16, 2 = fp32.
 hipError_t launch_prefill(int dtype, const PrefillArgs& a, hipStream_t stream);
+hipError_t launch_extend(int dtype, const PrefillArgs& a, hipStream_t stream);
 hipError_t launch_decode(int dtype, const DecodeArgs& a, hipStream_t stream);
 hipError_t launch_rel_logits(int dtype, const RelLogitsArgs& a, hipStream_t stream);
 
