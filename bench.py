@@ -29,6 +29,7 @@ PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA, published
 PEAK_HBM_GBPS = 8000.0      # MI355X HBM3E, published
 PREFILL_WORKLOAD = "swa_prefill_8k"
 DECODE_WORKLOAD = "decode_64x8k"
+EXTEND_WORKLOAD = "extend_4x1k_8k_paged"
 PREFILL_KERNEL = "prefill_dma_kernel"  # the bf16 path for eight or more query heads per kv head
 DECODE_KERNEL = "decode_split_kernel"
 
@@ -152,6 +153,31 @@ def bench_decode(steps: int, warmup: int):
     return w, nbytes, kv, total_ms / steps, sum(per) / len(per), ns
 
 
+def bench_extend(steps: int, warmup: int):
+    """Chunked prefill over a paged cache: the new rows of every sequence."""
+    import torch
+    import transformer_attention_query_amd as ra
+    from transformer_attention_query_amd import inputs as tinputs
+
+    w = tinputs.WORKLOADS[EXTEND_WORKLOAD]
+    x = {n: t.cuda() for n, t in tinputs.make_inputs(w, seed=0).items()}
+    paged = w.page_size > 0
+    k = x["k_pages"] if paged else x["k"]
+    v = x["v_pages"] if paged else x["v"]
+    bt = x["block_table"] if paged else None
+    out = torch.empty_like(x["q"])
+    lse = torch.empty(w.Hq, x["q"].shape[0], dtype=torch.float32, device="cuda")
+    stream = torch.cuda.current_stream()
+
+    def step(_i):
+        ra.extend(x["q"], k, v, x["r"], x["P_cols"], w.alpha, w.E, w.W, w.log_scale, x["q_start"], x["kv_len"],
+                  w.n_new, block_table=bt, out=out, lse=lse)
+
+    total_ms, per = _time_launches(step, steps, warmup, stream)
+    flops, _, _ = prefill_work(w.T, w.Hq, w.D, w.d_r, w.E, w.W, rows=range(w.T - w.n_new, w.T))
+    return w, flops * w.B, total_ms / steps, sum(per) / len(per)
+
+
 def cpu_baseline(target_s: float = 15.0):
     """The fp64 oracle, as it stands, on query rows of the prefill workload."""
     import torch
@@ -200,6 +226,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--no-extend", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
@@ -255,6 +282,18 @@ def main():
                                        "frac": round(kgbps / PEAK_HBM_GBPS, 4),
                                        "traffic": _traffic(DECODE_KERNEL, _src_hash("decode.hip", "device_common.hpp")),
                                        "avg_launch_us": round(d_kernel_ms * 1e3, 2)}}
+    if not args.no_extend:
+        ew, e_flops, e_ms, e_kernel_ms = bench_extend(args.steps, args.warmup)
+        print(f"# extend {ew.name}: {e_ms * 1e3:.1f} us/step", file=sys.stderr, flush=True)
+        e_ach = e_flops / (e_kernel_ms * 1e-3) / 1e12
+        line["extend"] = {"workload": ew.name, "value": round(e_flops / (e_ms * 1e-3) / 1e12, 2), "unit": "TFLOP/s",
+                          "ms_per_step": round(e_ms, 5), "algorithmic_flops": e_flops,
+                          "config": {"B": ew.B, "kv_len": ew.T, "new_rows": ew.n_new, "page_size": ew.page_size,
+                                     "Hq": ew.Hq, "Hkv": ew.Hkv, "d_r": ew.d_r, "rel_extent": ew.E, "window": ew.W},
+                          "roofline": {"bound": "mfma", "kernel": "prefill_kernel (extend)",
+                                       "achieved": round(e_ach, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                                       "frac": round(e_ach / PEAK_BF16_TFLOPS, 4), "traffic": None,
+                                       "avg_launch_us": round(e_kernel_ms * 1e3, 2)}}
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline()
     print(json.dumps(line), flush=True)
