@@ -144,6 +144,30 @@ int rel_attn_decode(const void* q, const void* k, const void* v, const void* r,
                     int num_splits, void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * Paged decode: one query token per sequence at position kv_len[b]-1 of its
+ * paged KV cache, with per-sequence cache lengths (the decode kernels of the
+ * serving systems' paged caches).
+ *   q [B, Hq, D]   r [B, Hq, d_r]   P_cols [E, d_r]   out [B, Hq, D]   lse [B, Hq] or NULL
+ *   k_pages, v_pages [num_pages, page_size, Hkv, D]: key j of sequence b is
+ *     slot j % page_size of page block_table[b * max_pages + j / page_size]
+ *     (int32 device array [B, max_pages]); page_size a positive multiple of 32.
+ *   kv_len [B]: int32 device array of cache lengths, each in [1, max_len].
+ * s uses Lseq = kv_len[b] (one scale per sequence, float32 on the device).
+ * num_splits and the workspace come from rel_attn_decode_plan with
+ * L = max_len; a split past a shorter sequence's keys contributes nothing.
+ * The device arrays are not read on the host; whatever they hold, accesses
+ * stay in bounds (kv_len clamped to [1, min(max_len, max_pages*page_size)],
+ * page ids to [0, num_pages)).
+ */
+int rel_attn_decode_paged(const void* q, const void* k_pages, const void* v_pages, const void* r,
+                          const void* P_cols, void* out, float* lse, int dtype,
+                          int B, int max_len, const int* kv_len, const int* block_table,
+                          int max_pages, int num_pages, int page_size,
+                          int Hq, int Hkv, int D, int d_r,
+                          float alpha, int rel_extent, int window, int log_scale,
+                          int num_splits, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * Dense relative logits (eq. for rel_logits in the same section):
  *   out[t, h, d] = s * sum_c r[t, h, c] * P_cols[d, c]   for every d < rel_extent
  *   r [n_tok, H, d_r] (dtype)   P_cols [E, d_r] (dtype)   out [n_tok, H, E] float32

@@ -35,7 +35,8 @@ def _declared_functions():
 
 def test_header_declares_the_boundary():
     names = _declared_functions()
-    for n in ("rel_attn_prefill", "rel_attn_extend", "rel_attn_decode", "rel_attn_decode_plan", "rel_logits",
+    for n in ("rel_attn_prefill", "rel_attn_extend", "rel_attn_decode", "rel_attn_decode_paged",
+              "rel_attn_decode_plan", "rel_logits",
               "rel_attn_last_error", "rel_attn_version", "rel_attn_scale_factor"):
         assert n in names
 
@@ -238,3 +239,32 @@ def test_extend_rejects_bad_arguments(lib, kw, code, frag):
 def test_extend_empty_is_a_noop(lib):
     for kw in (dict(B=0), dict(total_q=0), dict(max_q=0)):
         assert _extend(lib, q=None, k=None, v=None, out=None, q_start=None, kv_len=None, **kw) == RA_OK
+
+
+def _decode_paged(lib, **kw):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, r=FAKE, P=FAKE, out=FAKE + 0x1000, lse=None, dtype=RA_BF16, B=2, max_len=100,
+             kv_len=FAKE, bt=FAKE, max_pages=4, num_pages=8, page_size=32, Hq=8, Hkv=1, D=128, d_r=64,
+             alpha=0.1, E=32, W=0, ls=0, ns=0, ws=None, ws_bytes=0)
+    a.update(kw)
+    return lib.rel_attn_decode_paged(a["q"], a["k"], a["v"], a["r"], a["P"], a["out"], a["lse"], a["dtype"], a["B"],
+                                     a["max_len"], a["kv_len"], a["bt"], a["max_pages"], a["num_pages"],
+                                     a["page_size"], a["Hq"], a["Hkv"], a["D"], a["d_r"], a["alpha"], a["E"],
+                                     a["W"], a["ls"], a["ns"], a["ws"], a["ws_bytes"], None)
+
+
+@pytest.mark.parametrize("kw,code,frag", [
+    (dict(page_size=48), RA_ERR_UNSUPPORTED, "page_size"),
+    (dict(max_pages=0), RA_ERR_INVALID_ARG, "max_pages"),
+    (dict(bt=None), RA_ERR_INVALID_ARG, "block_table"),
+    (dict(kv_len=FAKE + 1), RA_ERR_INVALID_ARG, "aligned"),
+    (dict(max_len=0), RA_ERR_INVALID_ARG, "max_len"),
+    (dict(D=96), RA_ERR_UNSUPPORTED, "head dim"),
+    (dict(out=FAKE), RA_ERR_INVALID_ARG, "alias"),
+    (dict(ns=-1), RA_ERR_INVALID_ARG, "num_splits"),
+    (dict(), RA_ERR_WORKSPACE, "workspace is NULL"),
+    (dict(ws=FAKE + 16, ws_bytes=1 << 30), RA_ERR_WORKSPACE, "256-byte"),
+    (dict(ws=FAKE, ws_bytes=16), RA_ERR_WORKSPACE, "smaller"),
+])
+def test_decode_paged_rejects_bad_arguments(lib, kw, code, frag):
+    assert _decode_paged(lib, **kw) == code
+    assert frag in lib.rel_attn_last_error().decode()

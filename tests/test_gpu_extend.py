@@ -83,3 +83,30 @@ def test_extend_of_whole_sequences_equals_prefill():
     assert_close(out, ref, torch.bfloat16, "extend", lse, lref)
     assert_close(pout.view(2 * T, Hq, 128), ref, torch.bfloat16, "prefill",
                  plse.permute(1, 0, 2).reshape(Hq, 2 * T), lref)
+
+
+# ---------------------------------------------------------------- paged decode
+
+# name, dtype, kv_lens, Hq, Hkv, d_r, E, W, log_scale, page_size, num_splits (0 = plan's choice)
+DECODE_CASES = [
+    ("g8_mixed_lengths", "bf16", [1, 31, 32, 700, 3000], 8, 1, 32, 100, 0, False, 32, 0),
+    ("g4_window_log", "bf16", [4097, 64, 500], 8, 2, 64, 64, 300, True, 64, 0),
+    ("g8_forced_splits_short_seq", "bf16", [2050, 40], 16, 2, 128, 1024, 0, False, 128, 8),
+    ("mha_E0", "bf16", [129, 257], 2, 2, 16, 0, 0, False, 32, 0),
+    ("fp32_paged", "fp32", [257, 1, 90], 4, 2, 32, 40, 0, False, 32, 0),
+]
+
+
+@pytest.mark.parametrize("case", DECODE_CASES, ids=[c[0] for c in DECODE_CASES])
+def test_decode_paged_matches_oracle(case):
+    name, dt, kv_lens, Hq, Hkv, d_r, E, W, ls, page, ns = case
+    B = len(kv_lens)
+    x = tinputs.make_extend_inputs(kv_lens, [1] * B, Hq, Hkv, 128, d_r, max(E, 1), dt,
+                                   seed=zlib.crc32(name.encode()) % 1000, page_size=page)
+    xd = {n: t.cuda() for n, t in x.items()}
+    out, lse = ra.decode_paged(xd["q"], xd["k_pages"], xd["v_pages"], xd["r"], xd["P_cols"][:E] if E else None,
+                               ALPHA, E, W, ls, xd["kv_len"], xd["block_table"], max(kv_lens), num_splits=ns)
+    torch.cuda.synchronize()
+    ref, lref = oracle.extend(x["q"], x["k_pages"], x["v_pages"], x["r"], x["P"], ALPHA, E, W, ls,
+                              x["q_start"].tolist(), kv_lens, block_table=x["block_table"].tolist(), page_size=page)
+    assert_close(out, ref, x["q"].dtype, name, lse, lref.t())

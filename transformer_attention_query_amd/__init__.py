@@ -1,6 +1,6 @@
 """MI355X (gfx950) relative-attention forward: HIP kernels behind a C ABI.
 
-``prefill``, ``extend``, ``decode``, ``decode_plan`` and ``rel_logits`` call the compiled
+``prefill``, ``extend``, ``decode``, ``decode_paged``, ``decode_plan`` and ``rel_logits`` call the compiled
 library ``librelattn.so`` (built in-tree by ``__graft_entry__.build()`` or
 ``python -m transformer_attention_query_amd.build``).  There is no fallback:
 if the library is missing the calls raise.
@@ -9,6 +9,7 @@ if the library is missing the calls raise.
 from .binding import (  # noqa: F401
     RelAttnError,
     decode,
+    decode_paged,
     decode_plan,
     extend,
     library_path,

@@ -16,7 +16,8 @@ from typing import Optional, Tuple
 
 import torch
 
-__all__ = ["RelAttnError", "library_path", "load_library", "prefill", "extend", "decode", "decode_plan",
+__all__ = ["RelAttnError", "library_path", "load_library", "prefill", "extend", "decode", "decode_paged",
+           "decode_plan",
            "rel_logits", "scale_factor", "version"]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -54,6 +55,9 @@ def _declare(lib):
     lib.rel_attn_decode.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32,
                                     f32, i32, i32, i32, i32, vp, sz, vp]
     lib.rel_attn_decode.restype = i32
+    lib.rel_attn_decode_paged.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, vp, vp, i32, i32, i32,
+                                          i32, i32, i32, i32, f32, i32, i32, i32, i32, vp, sz, vp]
+    lib.rel_attn_decode_paged.restype = i32
     lib.rel_logits.argtypes = [vp, vp, vp, i32, i64, i32, i32, i32, i32, i64, vp]
     lib.rel_logits.restype = i32
     lib.rel_attn_last_error.argtypes = []
@@ -311,3 +315,51 @@ def rel_logits(r: torch.Tensor, P_cols: torch.Tensor, log_scale: bool = False,
     _check(lib.rel_logits(_ptr(r), _ptr(P_cols), _ptr(out), _DTYPE_CODE[dt], n, H, d_r, E,
                           1 if log_scale else 0, int(seq_len if seq_len else n), _stream(dev)))
     return out
+
+
+def decode_paged(q: torch.Tensor, k_pages: torch.Tensor, v_pages: torch.Tensor, r: Optional[torch.Tensor],
+                 P_cols: Optional[torch.Tensor], alpha: float, rel_extent: int, window: int, log_scale: bool,
+                 kv_len: torch.Tensor, block_table: torch.Tensor, max_len: int, num_splits: int = 0,
+                 return_lse: bool = True, workspace: Optional[torch.Tensor] = None
+                 ) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+    """Split-KV decode over paged caches with per-sequence lengths (rel_attn_decode_paged).
+
+    q [B,Hq,D], k_pages/v_pages [num_pages,page_size,Hkv,D], block_table
+    [B,max_pages] and kv_len [B] (int32, device; each in [1, max_len]),
+    r [B,Hq,d_r], P_cols [E,d_r].  Returns out [B,Hq,D] and lse [B,Hq] fp32.
+    """
+    lib = load_library()
+    dev = q.device
+    dt = q.dtype
+    if dt not in _DTYPE_CODE:
+        raise TypeError(f"unsupported dtype {dt}")
+    _need(q, "q", dt, dev, 3)
+    _need(k_pages, "k_pages", dt, dev, 4)
+    _need(v_pages, "v_pages", dt, dev, 4)
+    _need(kv_len, "kv_len", torch.int32, dev, 1)
+    _need(block_table, "block_table", torch.int32, dev, 2)
+    B, Hq, D = q.shape
+    num_pages, page_size, Hkv = k_pages.shape[0], k_pages.shape[1], k_pages.shape[2]
+    if v_pages.shape != k_pages.shape:
+        raise ValueError("v_pages shape differs from k_pages")
+    if kv_len.shape[0] != B or block_table.shape[0] != B:
+        raise ValueError("kv_len and block_table need one entry / row per sequence")
+    d_r = 0
+    if rel_extent > 0:
+        _need(r, "r", dt, dev, 3)
+        _need(P_cols, "P_cols", dt, dev, 2)
+        d_r = r.shape[2]
+    else:
+        r = None
+        P_cols = None
+    ns, ws_bytes = decode_plan(B, max_len, Hq, Hkv, D, num_splits, window, rel_extent)
+    if workspace is None:
+        workspace = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
+    out = torch.empty_like(q)
+    lse = torch.empty(B, Hq, dtype=torch.float32, device=dev) if return_lse else None
+    _check(lib.rel_attn_decode_paged(_ptr(q), _ptr(k_pages), _ptr(v_pages), _ptr(r), _ptr(P_cols), _ptr(out),
+                                     _ptr(lse), _DTYPE_CODE[dt], B, int(max_len), _ptr(kv_len), _ptr(block_table),
+                                     block_table.shape[1], num_pages, page_size, Hq, Hkv, D, d_r, float(alpha),
+                                     int(rel_extent), int(window), 1 if log_scale else 0, ns, _ptr(workspace),
+                                     workspace.numel() * workspace.element_size(), _stream(dev)))
+    return out, lse

@@ -207,6 +207,60 @@ int rel_attn_decode(const void* q, const void* k, const void* v, const void* r, 
   return ok();
 }
 
+int rel_attn_decode_paged(const void* q, const void* k_pages, const void* v_pages, const void* r,
+                          const void* P_cols, void* out, float* lse, int dtype, int B, int max_len,
+                          const int* kv_len, const int* block_table, int max_pages, int num_pages, int page_size,
+                          int Hq, int Hkv, int D, int d_r, float alpha, int rel_extent, int window, int log_scale,
+                          int num_splits, void* workspace, size_t workspace_bytes, void* stream) {
+  int rc = check_common(dtype, B, max_len, Hq, Hkv, D, d_r, alpha, rel_extent, window, log_scale, "max_len");
+  if (rc) return rc;
+  if (max_len == 0) return fail(RA_ERR_INVALID_ARG, "max_len = 0: a cache holds at least the query's own token");
+  if ((rc = check_ptr(q, "q", true)) || (rc = check_ptr(k_pages, "k_pages", true)) ||
+      (rc = check_ptr(v_pages, "v_pages", true)) || (rc = check_ptr(out, "out", true)) ||
+      (rc = check_ptr(lse, "lse", false)) || (rc = check_ptr(r, "r", rel_extent > 0)) ||
+      (rc = check_ptr(P_cols, "P_cols", rel_extent > 0)))
+    return rc;
+  if (kv_len == nullptr || block_table == nullptr)
+    return fail(RA_ERR_INVALID_ARG, "kv_len and block_table must not be NULL");
+  if ((reinterpret_cast<uintptr_t>(kv_len) | reinterpret_cast<uintptr_t>(block_table)) & 3u)
+    return fail(RA_ERR_INVALID_ARG, "kv_len and block_table must be 4-byte aligned");
+  if (out == q || out == k_pages || out == v_pages || out == r) return fail(RA_ERR_INVALID_ARG, "out aliases an input");
+  if (page_size <= 0 || page_size % 32 != 0)
+    return fail(RA_ERR_UNSUPPORTED, "page_size = %d: supported values are positive multiples of 32", page_size);
+  if (max_pages <= 0 || num_pages <= 0)
+    return fail(RA_ERR_INVALID_ARG, "max_pages = %d and num_pages = %d must be positive", max_pages, num_pages);
+  if ((long long)max_pages * page_size > 0x7fffffffLL) return fail(RA_ERR_UNSUPPORTED, "max_pages * page_size too large");
+  if (num_splits < 0) return fail(RA_ERR_INVALID_ARG, "num_splits = %d < 0", num_splits);
+  relattn::DecodePlan pl = relattn::plan_decode(B, max_len, Hq, Hkv, num_splits, window, rel_extent);
+  if (B == 0) return ok();
+  if (workspace == nullptr) return fail(RA_ERR_WORKSPACE, "workspace is NULL (need %zu bytes)", pl.ws_bytes);
+  if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0)
+    return fail(RA_ERR_WORKSPACE, "workspace is not 256-byte aligned");
+  if (workspace_bytes < pl.ws_bytes)
+    return fail(RA_ERR_WORKSPACE, "workspace of %zu bytes is smaller than the %zu the plan needs", workspace_bytes,
+                pl.ws_bytes);
+
+  relattn::DecodeArgs a;
+  a.q = q; a.k = k_pages; a.v = v_pages; a.r = r; a.pc = P_cols; a.out = out; a.lse = lse;
+  a.ws = static_cast<float*>(workspace);
+  a.B = B; a.L = max_len; a.Hq = Hq; a.Hkv = Hkv; a.d_r = rel_extent > 0 ? d_r : 16; a.E = rel_extent; a.W = window;
+  a.c1 = (float)((double)alpha * 1.4426950408889634);
+  a.c2 = (float)1.4426950408889634;
+  a.n_split = pl.n_split;
+  a.chunk = pl.chunk;
+  a.kv_lo = pl.kv_lo;
+  a.n_hg = pl.n_hg;
+  a.rl_base = pl.rl_base;
+  a.rl_stride = pl.rl_stride;
+  a.rl = reinterpret_cast<const float*>(static_cast<char*>(workspace) + pl.ws_partial_bytes);
+  a.kv_len = kv_len; a.btab = block_table;
+  a.max_pages = max_pages; a.num_pages = num_pages; a.page_size = page_size;
+  a.log_scale = log_scale; a.alpha = alpha;
+  hipError_t e = relattn::launch_decode_paged(dtype, a, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(RA_ERR_HIP, "decode launch failed: %s", hipGetErrorString(e));
+  return ok();
+}
+
 int rel_logits(const void* r, const void* P_cols, float* out, int dtype, long long n_tok, int H, int d_r,
                int rel_extent, int log_scale, long long seq_len, void* stream) {
   if (dtype != RA_BF16 && dtype != RA_F32) return fail(RA_ERR_INVALID_ARG, "dtype %d is not RA_BF16 or RA_F32", dtype);

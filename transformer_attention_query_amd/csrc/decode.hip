@@ -119,7 +119,11 @@ struct DecReduce {
   float o[kDecWaves][16][kHeadDim];
 };
 
-template <typename T>
+// PAGED: the paged form (rel_attn_decode_paged): per-sequence cache lengths
+// kv_len[b] (at most L), pages of page_size keys (a multiple of 32) through a
+// block table, steps aligned to 32 keys so each lies in one page, and bias
+// rows in distance order scaled by log2(e) only (s applied here per sequence).
+template <typename T, bool PAGED>
 __global__ __launch_bounds__(kDecWaves * 64, sizeof(T) == 2 ? 2 : 1) void decode_split_kernel(DecodeArgs p) {
   using VS = DecV<T>;
   constexpr int D = kHeadDim;
@@ -146,8 +150,21 @@ __global__ __launch_bounds__(kDecWaves * 64, sizeof(T) == 2 ? 2 : 1) void decode
   const int split = (int)(rest % p.n_split);
   const int b = (int)(rest / p.n_split);
 
-  const int ks = p.kv_lo + split * p.chunk;
-  const int ke = min(ks + p.chunk, L);
+  // keys [ks_lo, ke) of this split; steps start at ks (= ks_lo, or ks_lo
+  // rounded down to 32 keys in the paged form, the keys below ks_lo masked)
+  int Lb = L, ks_lo = p.kv_lo + split * p.chunk;
+  float c1 = p.c1, bscale = 1.0f;
+  if constexpr (PAGED) {
+    Lb = min(max(p.kv_len[b], 1), min(L, p.max_pages * p.page_size));
+    ks_lo = ((p.W > 0 && Lb > p.W) ? Lb - p.W : 0) + split * p.chunk;
+    if (p.log_scale) {  // s = max(1, ln(kv_len) / ln(4096)), one per sequence
+      bscale = fmaxf(1.0f, logf(float(Lb)) * (1.0f / 8.317766166719343f));
+      c1 = bscale * p.alpha * 1.4426950408889634f;
+    }
+  }
+  const int ks = PAGED ? (ks_lo & ~31) : ks_lo;
+  const int ke = min(ks_lo + p.chunk, Lb);
+  const bool empty = ks_lo >= Lb;  // a split past a short sequence's keys
 
   const int hin = hg * 16 + c;  // head within the kv group
   const bool hvalid = hin < G;
@@ -181,25 +198,50 @@ __global__ __launch_bounds__(kDecWaves * 64, sizeof(T) == 2 ? 2 : 1) void decode
   // past the split end are clamped to its last key (masked later, weight
   // exactly 0 against finite data).
   auto fetch = [&](int j0, Chunk<T>& ch) {
+    // rows past the split end are clamped to its last key; in the paged form
+    // the clamped rows of a step share one page: the page of min(j0, ke-1)
+    const T* kb = kbase;
+    const T* vb = vbase;
+    int jp = 0;  // first key of that page
+    if constexpr (PAGED) {
+      const int jsel = max(min(j0, ke - 1), 0);
+      const int pi = min(jsel / p.page_size, p.max_pages - 1);
+      const int pg = min(max(p.btab[size_t(b) * p.max_pages + pi], 0), p.num_pages - 1);
+      jp = pi * p.page_size;
+      kb = kg + (size_t(pg) * p.page_size * Hkv + kvh) * D;
+      vb = vg + (size_t(pg) * p.page_size * Hkv + kvh) * D;
+    }
 #pragma unroll
     for (int blk = 0; blk < 2; ++blk) {
       const int j = min(j0 + 16 * blk + c, ke - 1);
-      const T* src = kbase + size_t(j) * row_stride + 8 * g;
+      const T* src = kb + size_t(j - jp) * row_stride + 8 * g;
 #pragma unroll
       for (int st = 0; st < D / 32; ++st) ch.k[blk][st] = ld8<T>(src + 32 * st);
     }
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
       const int j = min(j0 + 8 * g + i, ke - 1);
-      ch.v[i] = ld8<T>(vbase + size_t(j) * row_stride + 8 * c);
+      ch.v[i] = ld8<T>(vb + size_t(j - jp) * row_stride + 8 * c);
     }
-    // Bias of keys j0+16*blk+4g .. +3: entries j - L + rl_base.  Clamping keeps
-    // the read inside the row; a clamped key is at distance >= E, whose entry
-    // (like every entry beyond the extent) holds exactly 0.
+    if constexpr (PAGED) {
+      // bias of key j at entry d = Lb-1-j of the distance-ordered row (0 past E)
 #pragma unroll
-    for (int blk = 0; blk < 2; ++blk) {
-      const int idx = min(max(j0 + 16 * blk + 4 * g - L + p.rl_base, 0), p.rl_stride - 4);
-      ch.rl[blk] = *reinterpret_cast<const f32x4*>(rlrow + idx);
+      for (int blk = 0; blk < 2; ++blk)
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+          const int d = Lb - 1 - (j0 + 16 * blk + 4 * g + v);
+          const float x = rlrow[min(max(d, 0), max(p.E - 1, 0))];
+          ch.rl[blk][v] = (d >= 0 && d < p.E) ? x : 0.0f;
+        }
+    } else {
+      // Bias of keys j0+16*blk+4g .. +3: entries j - L + rl_base.  Clamping
+      // keeps the read inside the row; a clamped key is at distance >= E, whose
+      // entry (like every entry beyond the extent) holds exactly 0.
+#pragma unroll
+      for (int blk = 0; blk < 2; ++blk) {
+        const int idx = min(max(j0 + 16 * blk + 4 * g - L + p.rl_base, 0), p.rl_stride - 4);
+        ch.rl[blk] = *reinterpret_cast<const f32x4*>(rlrow + idx);
+      }
     }
   };
 
@@ -217,13 +259,15 @@ __global__ __launch_bounds__(kDecWaves * 64, sizeof(T) == 2 ? 2 : 1) void decode
 #pragma unroll
     for (int blk = 0; blk < 2; ++blk)
 #pragma unroll
-      for (int v = 0; v < 4; ++v) x[blk][v] = fmaf(x[blk][v], p.c1, ch.rl[blk][v]);
-    if (j0 + kDecKeys > ke) {  // ragged end of the split
+      for (int v = 0; v < 4; ++v) x[blk][v] = fmaf(x[blk][v], c1, PAGED ? bscale * ch.rl[blk][v] : ch.rl[blk][v]);
+    if (j0 + kDecKeys > ke || (PAGED && j0 < ks_lo)) {  // ragged end (or aligned start) of the split
 #pragma unroll
       for (int blk = 0; blk < 2; ++blk)
 #pragma unroll
-        for (int v = 0; v < 4; ++v)
-          if (j0 + 16 * blk + 4 * g + v >= ke) x[blk][v] = -INFINITY;
+        for (int v = 0; v < 4; ++v) {
+          const int j = j0 + 16 * blk + 4 * g + v;
+          if (j >= ke || (PAGED && j < ks_lo)) x[blk][v] = -INFINITY;
+        }
     }
 
     // online softmax per head (lanes c, c+16, c+32, c+48); O is rescaled only
@@ -268,9 +312,16 @@ __global__ __launch_bounds__(kDecWaves * 64, sizeof(T) == 2 ? 2 : 1) void decode
   constexpr int NB = kDecDepth;
   constexpr int STRIDE = kDecWaves * kDecKeys;
   Chunk<T> ring[NB];
+  // steps of this split: the plan's chunk, or (paged) up to the sequence's
+  // end in whole ring turns; none for an empty split
+  int j_end = ks + p.chunk;
+  if constexpr (PAGED) {
+    const int span = ke - ks;
+    j_end = empty ? ks : ks + min(p.chunk + 32, (span + NB * STRIDE - 1) / (NB * STRIDE) * (NB * STRIDE));
+  }
 #pragma unroll
   for (int bfi = 0; bfi < NB - 1; ++bfi) fetch(ks + w * kDecKeys + bfi * STRIDE, ring[bfi]);
-  for (int j0 = ks + w * kDecKeys; j0 < ks + p.chunk; j0 += NB * STRIDE) {
+  for (int j0 = ks + w * kDecKeys; j0 < j_end; j0 += NB * STRIDE) {
 #pragma unroll
     for (int bfi = 0; bfi < NB; ++bfi) {
       fetch(j0 + (bfi + NB - 1) * STRIDE, ring[(bfi + NB - 1) % NB]);
@@ -425,12 +476,13 @@ __global__ __launch_bounds__(256) void decode_merge_small_kernel(DecodeArgs p) {
   if (p.lse != nullptr && d4 == 0) p.lse[bh] = (M + log2f(den)) * kLn2;
 }
 
-template <typename T>
+template <typename T, bool PAGED>
 hipError_t launch_decode_t(const DecodeArgs& a, hipStream_t stream) {
   {
     // bias rows of every (sequence, head): s * log2(e) * r.P[:, d], stored
     // reversed so that key j finds its distance L-1-j at entry j - L + rl_base
-    // (all zeros when E == 0)
+    // (all zeros when E == 0).  Paged form: log2(e) * r.P[:, d] in distance
+    // order (the lengths, hence s, are per sequence and known on the device).
     RelLogitsArgs ra;
     ra.r = a.r;
     ra.pc = a.pc;
@@ -438,16 +490,18 @@ hipError_t launch_decode_t(const DecodeArgs& a, hipStream_t stream) {
     ra.n_rows = (long long)a.B * a.Hq;
     ra.d_r = a.d_r;
     ra.E = a.E;
-    ra.s = a.c2;
-    ra.out_cols = a.rl_stride;
+    ra.s = PAGED ? 1.4426950408889634f : a.c2;
+    ra.out_cols = PAGED ? a.E : a.rl_stride;
     ra.out_stride = a.rl_stride;
-    ra.rev_base = a.rl_base;
-    hipError_t e = launch_rel_logits(sizeof(T) == 2 ? 1 : 2, ra, stream);
-    if (e != hipSuccess) return e;
+    ra.rev_base = PAGED ? 0 : a.rl_base;
+    if (!PAGED || a.E > 0) {
+      hipError_t e = launch_rel_logits(sizeof(T) == 2 ? 1 : 2, ra, stream);
+      if (e != hipSuccess) return e;
+    }
   }
   const long long grid = (long long)a.B * a.Hkv * a.n_hg * a.n_split;
   if (grid > 0x7fffffffLL) return hipErrorInvalidConfiguration;
-  hipLaunchKernelGGL(decode_split_kernel<T>, dim3((unsigned)grid), dim3(kDecWaves * 64), 0, stream, a);
+  hipLaunchKernelGGL((decode_split_kernel<T, PAGED>), dim3((unsigned)grid), dim3(kDecWaves * 64), 0, stream, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   if (a.n_split <= kMergeSmallSplits) {
@@ -504,8 +558,13 @@ DecodePlan plan_decode(int B, int L, int Hq, int Hkv, int num_splits_req, int wi
 }
 
 hipError_t launch_decode(int dtype, const DecodeArgs& a, hipStream_t stream) {
-  if (dtype == 1) return launch_decode_t<__bf16>(a, stream);
-  return launch_decode_t<float>(a, stream);
+  if (dtype == 1) return launch_decode_t<__bf16, false>(a, stream);
+  return launch_decode_t<float, false>(a, stream);
+}
+
+hipError_t launch_decode_paged(int dtype, const DecodeArgs& a, hipStream_t stream) {
+  if (dtype == 1) return launch_decode_t<__bf16, true>(a, stream);
+  return launch_decode_t<float, true>(a, stream);
 }
 
 }  // namespace relattn

@@ -54,6 +54,12 @@ struct DecodeArgs {
   int n_hg;         // groups of 16 query heads per kv head
   int rl_base;      // key j reads bias row entry j - L + rl_base
   int rl_stride;    // floats per bias row
+  // paged form only (see rel_attn_decode_paged): L is then the bound on kv_len
+  const int* kv_len = nullptr;  // [B] cached tokens per sequence
+  const int* btab = nullptr;    // [B, max_pages] page ids
+  int max_pages = 0, num_pages = 0, page_size = 0;
+  int log_scale = 0;            // s per sequence from kv_len
+  float alpha = 0.0f;
 };
 
 // out[row * out_stride + oc] = s * r[row] . P_cols[d(oc)] for oc < out_cols,
@@ -86,6 +92,7 @@ DecodePlan plan_decode(int B, int L, int Hq, int Hkv, int num_splits_req, int wi
 hipError_t launch_prefill(int dtype, const PrefillArgs& a, hipStream_t stream);
 hipError_t launch_extend(int dtype, const PrefillArgs& a, hipStream_t stream);
 hipError_t launch_decode(int dtype, const DecodeArgs& a, hipStream_t stream);
+hipError_t launch_decode_paged(int dtype, const DecodeArgs& a, hipStream_t stream);
 hipError_t launch_rel_logits(int dtype, const RelLogitsArgs& a, hipStream_t stream);
 
 }  // namespace relattn
