@@ -30,6 +30,7 @@ PEAK_HBM_GBPS = 8000.0      # MI355X HBM3E, published
 PREFILL_WORKLOAD = "swa_prefill_8k"
 DECODE_WORKLOAD = "decode_64x8k"
 EXTEND_WORKLOAD = "extend_4x1k_8k_paged"
+PAGED_DECODE_WORKLOAD = "decode_paged_64x8k"
 PREFILL_KERNEL = "prefill_dma_kernel"  # the bf16 path for eight or more query heads per kv head
 DECODE_KERNEL = "decode_split_kernel"
 
@@ -178,6 +179,30 @@ def bench_extend(steps: int, warmup: int):
     return w, flops * w.B, total_ms / steps, sum(per) / len(per)
 
 
+def bench_decode_paged(steps: int, warmup: int):
+    """decode_64x8k over a paged cache: the same bytes through a block table."""
+    import torch
+    import transformer_attention_query_amd as ra
+    from transformer_attention_query_amd import inputs as tinputs
+
+    w = tinputs.WORKLOADS[PAGED_DECODE_WORKLOAD]
+    x = {n: t.cuda() for n, t in tinputs.make_inputs(w, seed=0).items()}
+    # two copies of the page pool, used alternately (each launch reads 512 MiB)
+    kp = [x["k_pages"], x["k_pages"].clone()]
+    vp = [x["v_pages"], x["v_pages"].clone()]
+    ns, ws_bytes = ra.decode_plan(w.B, w.T, w.Hq, w.Hkv, w.D, 0, w.W, w.E)
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device="cuda")
+    stream = torch.cuda.current_stream()
+
+    def step(i):
+        ra.decode_paged(x["q"], kp[i % 2], vp[i % 2], x["r"], x["P_cols"], w.alpha, w.E, w.W, w.log_scale,
+                        x["kv_len"], x["block_table"], w.T, num_splits=ns, workspace=ws)
+
+    total_ms, per = _time_launches(step, steps, warmup, stream)
+    nbytes, _ = decode_bytes(w.B, w.T, w.Hq, w.Hkv, w.D, w.d_r, w.E, w.W)
+    return w, nbytes, total_ms / steps, sum(per) / len(per), ns
+
+
 def cpu_baseline(target_s: float = 15.0):
     """The fp64 oracle, as it stands, on query rows of the prefill workload."""
     import torch
@@ -282,6 +307,16 @@ def main():
                                        "frac": round(kgbps / PEAK_HBM_GBPS, 4),
                                        "traffic": _traffic(DECODE_KERNEL, _src_hash("decode.hip", "device_common.hpp")),
                                        "avg_launch_us": round(d_kernel_ms * 1e3, 2)}}
+    if not args.no_decode:
+        pw, p_bytes, p_ms, p_kernel_ms, p_ns = bench_decode_paged(args.steps, args.warmup)
+        print(f"# decode {pw.name}: {p_ms * 1e3:.1f} us/step ({p_ns} splits)", file=sys.stderr, flush=True)
+        pk = p_bytes / (p_kernel_ms * 1e-3) / 1e9
+        line["decode_paged"] = {"workload": pw.name, "value": round(p_bytes / (p_ms * 1e-3) / 1e9, 1), "unit": "GB/s",
+                                "ms_per_step": round(p_ms, 5), "num_splits": p_ns, "algorithmic_bytes": p_bytes,
+                                "roofline": {"bound": "hbm", "kernel": DECODE_KERNEL + " (paged)+merge",
+                                             "achieved": round(pk, 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
+                                             "frac": round(pk / PEAK_HBM_GBPS, 4), "traffic": None,
+                                             "avg_launch_us": round(p_kernel_ms * 1e3, 2)}}
     if not args.no_extend:
         ew, e_flops, e_ms, e_kernel_ms = bench_extend(args.steps, args.warmup)
         print(f"# extend {ew.name}: {e_ms * 1e3:.1f} us/step", file=sys.stderr, flush=True)

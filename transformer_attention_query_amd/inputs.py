@@ -78,6 +78,10 @@ WORKLOADS: Dict[str, Workload] = {
     "decode_1x1m_log": Workload(
         "decode_1x1m_log", "decode", "bf16", B=1, T=1 << 20, Hq=16, Hkv=2, D=128, d_r=128, E=1024,
         log_scale=True, notes="1 sequence x 1 token, kv length 2^20, log-scale s = 5/3"),
+    "decode_paged_64x8k": Workload(
+        "decode_paged_64x8k", "extend", "bf16", B=64, T=8192, Hq=16, Hkv=2, D=128, d_r=128, E=1024,
+        n_new=1, page_size=64,
+        notes="decode_64x8k over a paged cache (64-row pages at shuffled slots), per-sequence lengths"),
     "extend_4x1k_8k_paged": Workload(
         "extend_4x1k_8k_paged", "extend", "bf16", B=4, T=8192, Hq=16, Hkv=2, D=128, d_r=128, E=1024,
         n_new=1024, page_size=64,
