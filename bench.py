@@ -315,7 +315,9 @@ def main():
                                 "ms_per_step": round(p_ms, 5), "num_splits": p_ns, "algorithmic_bytes": p_bytes,
                                 "roofline": {"bound": "hbm", "kernel": DECODE_KERNEL + " (paged)+merge",
                                              "achieved": round(pk, 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
-                                             "frac": round(pk / PEAK_HBM_GBPS, 4), "traffic": None,
+                                             "frac": round(pk / PEAK_HBM_GBPS, 4),
+                                             "traffic": _traffic(DECODE_KERNEL + "_paged",
+                                                                 _src_hash("decode.hip", "device_common.hpp")),
                                              "avg_launch_us": round(p_kernel_ms * 1e3, 2)}}
     if not args.no_extend:
         ew, e_flops, e_ms, e_kernel_ms = bench_extend(args.steps, args.warmup)
@@ -327,7 +329,9 @@ def main():
                                      "Hq": ew.Hq, "Hkv": ew.Hkv, "d_r": ew.d_r, "rel_extent": ew.E, "window": ew.W},
                           "roofline": {"bound": "mfma", "kernel": "prefill_kernel (extend)",
                                        "achieved": round(e_ach, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                                       "frac": round(e_ach / PEAK_BF16_TFLOPS, 4), "traffic": None,
+                                       "frac": round(e_ach / PEAK_BF16_TFLOPS, 4),
+                                       "traffic": _traffic("prefill_kernel_extend",
+                                                           _src_hash("prefill.hip", "device_common.hpp")),
                                        "avg_launch_us": round(e_kernel_ms * 1e3, 2)}}
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline()
