@@ -41,7 +41,7 @@
 //     current tile computes and are written to LDS between two barriers.
 //     (bf16 with eight or more query heads per kv head takes
 //     prefill_dma_kernel below instead: LDS DMA into double-buffered tiles,
-//     one barrier per tile.)
+//     one barrier per tile, and a tile loop software-pipelined per wave.)
 //   * Softmax works in units of c2 = s*log2(e): y = S*(c1/c2) + R, so the bias
 //     rows need no scaling, and p = exp2(c2*y - c2*m).  O is rescaled only
 //     when a row maximum grows by more than 2^8 (exact either way: O and l
@@ -547,11 +547,16 @@ hipError_t launch_prefill_tiles(const PrefillArgs& a, hipStream_t stream) {
 // source chunk so that a row's 16-byte chunks land XOR-swizzled: chunk q of
 // row r sits at slot q ^ sw(r), with sw(r) = r & 7 for K and P (the 8 lanes of
 // a 16-byte fragment read hit 8 distinct bank groups) and sw(r) = 2*(r & 3)
-// for V (the 16 lanes of a transpose read cover the 32 banks once).  Tiles are
-// double-buffered: one barrier per tile, after which the waves issue the next
-// tile's DMA into the other buffer and compute on this one, then wait for
-// their own DMA.  P rows are fetched from clamped addresses; distances at or
-// beyond E are zeroed in the relative-logit accumulators instead.
+// for V (the 16 lanes of a transpose read cover the 32 banks once).
+//
+// The tile loop is software-pipelined inside each wave: one iteration runs
+// the softmax and PV of tile t together with the scores and relative logits
+// of tile t+1, in one straight-line block, so the matrix cores work on tile
+// t+1 while the VALU runs tile t's exponentials.  LDS holds K and P of tile
+// t+1 and V of tile t; the DMA fills K and P of tile t+2 and V of tile t+1
+// (all double-buffered by tile parity, one barrier per tile).  The loop is
+// unrolled by two so every LDS address is a per-lane offset plus a constant.
+// P rows for distances outside [0, E) are DMA'd from a zero row.
 // ---------------------------------------------------------------------------
 struct DmaCfg {
   static constexpr int N = 32;
@@ -579,6 +584,12 @@ __device__ __forceinline__ void dma16(const void* src, unsigned lds_base) {
       : "memory");
 }
 __device__ __forceinline__ void dma_wait() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
+// A zero P row: DMA source for distances outside [0, E), so their relative
+// logits come out zero without a test.
+__device__ __attribute__((aligned(16))) const __bf16 kZeroPRow[kMaxDr] = {};
+
+template <int V> struct IntC { static constexpr int value = V; };
 
 __global__ __launch_bounds__(512, 1) void prefill_dma_kernel(PrefillArgs p, int n_qt, int n_items) {
   using C = DmaCfg;
@@ -624,6 +635,7 @@ __global__ __launch_bounds__(512, 1) void prefill_dma_kernel(PrefillArgs p, int 
 
   const float qk_scale = p.c1 / p.c2;
   const float lazy = kLazyRescaleLog2 / p.c2;
+  const float c2 = p.c2;
 
   bf16x8 qreg[D / 16];
   {
@@ -649,8 +661,8 @@ __global__ __launch_bounds__(512, 1) void prefill_dma_kernel(PrefillArgs p, int 
   const int kt_lo = W > 0 ? max(0, q0 - W + 1) / N : 0;
   const int kt_hi = i_last / N;
 
-  // ---- DMA of one tile: this wave fills rows 4w .. 4w+3 of the K, V and P
-  // tiles; lane l writes slot l%16 of row 4w + l/16
+  // ---- DMA: this wave fills rows 4w .. 4w+3 of a K, V or P tile; lane l
+  // writes slot l%16 of row 4w + l/16
   const int drow = 4 * w + (lane >> 4);
   const int dslot = lane & 15;
   const int qk_src = dslot ^ (drow & 7);        // K / P chunk landing in this slot
@@ -661,169 +673,270 @@ __global__ __launch_bounds__(512, 1) void prefill_dma_kernel(PrefillArgs p, int 
   const int pvec = d_r / 8;
   const unsigned lds0 = unsigned(reinterpret_cast<size_t>(smem)) + 1024u * unsigned(w);
   auto chunk0 = [&](int kt) { return (q0 - kt * N) / N; };
-  auto issue_tile = [&](int kt) {
+  // K and the tile's new distance chunk of P rows (buffer kt & 1)
+  auto issue_kp = [&](int kt) {
     const int buf = kt & 1;
     const size_t j = size_t(min(kt * N + drow, T_ - 1)) * kv_row_stride;
     dma16(kbase + j + 8 * qk_src, __builtin_amdgcn_readfirstlane(lds0 + C::OFF_K + buf * C::TILEB));
-    dma16(vbase + j + 8 * qv_src, __builtin_amdgcn_readfirstlane(lds0 + C::OFF_V + buf * C::TILEB));
     if (E > 0) {
-      const int d = (chunk0(kt) - 1) * N + drow;  // the tile's new distance chunk
-      dma16(pcg + size_t(min(max(d, 0), E - 1)) * d_r + 8 * min(qk_src, pvec - 1),
-            __builtin_amdgcn_readfirstlane(lds0 + C::OFF_P + buf * C::TILEB));
+      const int d = (chunk0(kt) - 1) * N + drow;
+      const T* src = (d >= 0 && d < E) ? pcg + size_t(d) * d_r + 8 * min(qk_src, pvec - 1) : kZeroPRow + 8 * qk_src;
+      dma16(src, __builtin_amdgcn_readfirstlane(lds0 + C::OFF_P + buf * C::TILEB));
     }
   };
+  auto issue_v = [&](int kt) {
+    const int buf = kt & 1;
+    const size_t j = size_t(min(kt * N + drow, T_ - 1)) * kv_row_stride;
+    dma16(vbase + j + 8 * qv_src, __builtin_amdgcn_readfirstlane(lds0 + C::OFF_V + buf * C::TILEB));
+  };
+  auto band_of = [&](int kt) { return E > 0 && max(0, q0 - (kt * N + N - 1)) < E; };
+  auto mask_of = [&](int kt) {
+    const int j0 = kt * N;
+    return (j0 + N - 1 > q0) || (W > 0 && q0 + 31 - j0 >= W);
+  };
+  // Lane byte offsets of the MFMA fragments.  K / P A-operand of k-step kk:
+  // row a, chunk (h2 + 2kk) ^ (a & 7); k-steps kk and kk+4 are 128 bytes
+  // apart (chunk bit 3 lies outside the swizzle).
+  int offkp[4];
+#pragma unroll
+  for (int kk = 0; kk < 4; ++kk) offkp[kk] = a * C::ROWB + (((h2 + 2 * kk) ^ (a & 7)) << 4);
+  auto frag_kp = [&](const unsigned char* t, int kk) {
+    return ld8<T>(reinterpret_cast<const T*>(t + offkp[kk & 3] + 128 * (kk >> 2)));
+  };
+  // V transpose reads (PreV<__bf16> layout with V's swizzle): lane (G, s)
+  // reads rows 16*c16 + 4*(G/2) + s/4 (+8), columns 32*db + 16*(G%2) +
+  // 4*(s%4): chunk 4*db + 2*(G%2) + (s%4)/2, half s%2.  Column blocks db and
+  // db+2 are 128 bytes apart.
+  int offv[2];
+  {
+    const int Gq = lane >> 4, sq = lane & 15;
+    const int vsw = 2 * ((sq >> 2) & 3);  // rows r and r+8 share r & 3 = s/4
+#pragma unroll
+    for (int db = 0; db < 2; ++db) {
+      const int q = 4 * db + 2 * (Gq & 1) + ((sq & 3) >> 1);
+      offv[db] = (4 * (Gq >> 1) + (sq >> 2)) * C::ROWB + ((sq & 1) << 3) + ((q ^ vsw) << 4);
+    }
+  }
 
-  // ---- prologue: tile kt_lo.  The compiler-visible wait also retires the q
-  // and r loads, so no wait for them lands inside the tile loop.
-  issue_tile(kt_lo);
-  dma_wait();
-  __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0)
-
-  // Per-wave relative-logit buffer [query][distance]: chunk k at columns
-  // 32*(k&1), even chunks also at 64..95, so a tile's chunks c-1 and c are
-  // always 64 contiguous columns from 32*((c-1)&1) and each tile writes only
-  // its new chunk; key b of query a (distance 32c + a - b) is column
-  // 32*((c-1)&1) + 32 + a - b.  R^T accumulator v is distance
+  // Per-wave relative-logit buffer [query][distance].  The chunk made on
+  // tile t (its new chunk, distances 32(c-1) .. 32c-1 with c = qt - t) sits
+  // at columns 32*(t&1), and chunks of even t also at 64..95, so tile t's
+  // chunks c-1 and c are 64 contiguous columns from 32*(t&1) and each tile
+  // writes only its new chunk; key b of query a (distance 32c + a - b) is
+  // column 32*(t&1) + 32 + a - b.  R^T accumulator v is distance
   // 8*(v/4) + 4*h2 + v%4 of its chunk.
   float* const rs = Rs + w * 32 * C::LS;
-  auto put_chunk = [&](int k, const f32x16& acc) {
-    float* const dst = rs + a * C::LS + 32 * (k & 1) + 4 * h2;
+  float* const rput = rs + a * C::LS + 4 * h2;
+  const float* const rsh = rs + a * (C::LS + 1) + 32 - 4 * h2;
+  auto put_chunk = [&](int t, const f32x16& acc) {
+    float* const dst = rput + 32 * (t & 1);
 #pragma unroll
     for (int g4 = 0; g4 < 4; ++g4) {
       f32x4 x;
 #pragma unroll
       for (int e = 0; e < 4; ++e) x[e] = acc[4 * g4 + e];
       *reinterpret_cast<f32x4*>(dst + 8 * g4) = x;
-      if ((k & 1) == 0) *reinterpret_cast<f32x4*>(dst + 64 + 8 * g4) = x;
+      if ((t & 1) == 0) *reinterpret_cast<f32x4*>(dst + 64 + 8 * g4) = x;
     }
   };
-  int rlast = INT_MIN;  // newest chunk in the buffer
-
-  for (int kt = kt_lo; kt <= kt_hi; ++kt) {
+  // First tile t with bias: chunk c0 (made, by the rule above, on tile t-1)
+  // straight from P_cols in global memory.
+  auto first_chunk = [&](int t) {
+    const int c0 = chunk0(t);
+    const int d = c0 * N + a;
+    const bool rok = d >= 0 && d < E;
+    const int nk = d_r / 16;
+    const T* prow = pcg + size_t(min(max(d, 0), E - 1)) * d_r + 8 * h2;
+    bf16x8 pf[kMaxDr / 16];
+#pragma unroll
+    for (int kk = 0; kk < kMaxDr / 16; ++kk) pf[kk] = ld8<T>(prow + min(kk, nk - 1) * 16);
+    f32x16 rc = zero16();
+#pragma unroll
+    for (int kk = 0; kk < kMaxDr / 16; ++kk) mma32((rok && kk < nk) ? pf[kk] : zero8<T>(), rreg[kk], rc);
+    put_chunk(t - 1, rc);
+  };
+  // s <- s*(c1/c2) + bias along the shear, once tile t's new chunk is stored
+  auto shear_add = [&](int t, f32x16& s) {
+    wave_lds_fence();
+    const float* src = rsh + 32 * (t & 1);
+#pragma unroll
+    for (int v = 0; v < 16; ++v) s[v] = fmaf(s[v], qk_scale, src[-(8 * (v >> 2) + (v & 3))]);
+  };
+  auto apply_mask = [&](int kt, f32x16& s) {
     const int j0 = kt * N;
-    const int c0 = chunk0(kt);
-    __syncthreads();  // tile kt is in LDS; every wave is done with tile kt-1
-    if (kt < kt_hi) issue_tile(kt + 1);
-
-    const unsigned char* kt_b = smem + C::OFF_K + (kt & 1) * C::TILEB;
-    const unsigned char* vt_b = smem + C::OFF_V + (kt & 1) * C::TILEB;
-    const unsigned char* pt_b = smem + C::OFF_P + (kt & 1) * C::TILEB;
-    // fragment of row a, chunk q (16 bytes) of a K / P tile
-    auto frag_kp = [&](const unsigned char* t, int q) {
-      return ld8<T>(reinterpret_cast<const T*>(t + a * C::ROWB + ((q ^ (a & 7)) << 4)));
-    };
-
-    const bool live = !(j0 > q0 + 31 || (W > 0 && q0 - (j0 + N - 1) >= W));
-    if (live) {
-      const bool band = E > 0 && max(0, q0 - (j0 + N - 1)) < E;
-      const bool mask = (j0 + N - 1 > q0) || (W > 0 && q0 + 31 - j0 >= W);
-      f32x16 s = zero16();
-      if (band) {
-        if (rlast != c0) {
-          // first tile with bias: chunk c0 straight from P_cols in global memory
-          const int d = c0 * N + a;
-          const bool rok = d >= 0 && d < E;
-          const int nk = d_r / 16;
-          const T* prow = pcg + size_t(min(max(d, 0), E - 1)) * d_r + 8 * h2;
-          bf16x8 pf[kMaxDr / 16];
 #pragma unroll
-          for (int kk = 0; kk < kMaxDr / 16; ++kk) pf[kk] = ld8<T>(prow + min(kk, nk - 1) * 16);
-          f32x16 rc = zero16();
+    for (int v = 0; v < 16; ++v) {
+      const int dd = qa - (j0 + 8 * (v >> 2) + 4 * h2 + (v & 3));
+      if (dd < 0 || (W > 0 && dd >= W)) s[v] = -INFINITY;
+    }
+  };
+  // p = exp2(c2*y - c2*m), its row sum, and the bf16 PV operand
+  auto exps = [&](const f32x16& s, float nm, bf16x8 (&pb)[2], float& psum) {
+    f32x16 pe;
 #pragma unroll
-          for (int kk = 0; kk < kMaxDr / 16; ++kk) mma32((rok && kk < nk) ? pf[kk] : zero8<T>(), rreg[kk], rc);
-          put_chunk(c0, rc);
-        }
-        f32x16 racc = zero16();
+    for (int v = 0; v < 16; ++v) pe[v] = fast_exp2(fmaf(s[v], c2, nm));
+    psum = 0.0f;
 #pragma unroll
-        for (int kk = 0; kk < D / 16; ++kk) {
-          mma32(frag_kp(kt_b, h2 + 2 * kk), qreg[kk], s);
-          mma32(frag_kp(pt_b, h2 + 2 * kk), rreg[kk], racc);
-        }
-        // distances at or beyond E hold no bias (their P rows were clamped)
-        const int dlo = (c0 - 1) * N;
-        if (dlo + N > E) {
+    for (int v = 0; v < 16; ++v) psum += pe[v];
 #pragma unroll
-          for (int v = 0; v < 16; ++v)
-            if (dlo + 8 * (v >> 2) + 4 * h2 + (v & 3) >= E) racc[v] = 0.0f;
-        }
-        put_chunk(c0 - 1, racc);
-        rlast = c0 - 1;
-        wave_lds_fence();
-        const float* src = rs + a * (C::LS + 1) + 32 * ((c0 - 1) & 1) + 32 - 4 * h2;
+    for (int c16 = 0; c16 < 2; ++c16)
 #pragma unroll
-        for (int v = 0; v < 16; ++v) s[v] = fmaf(s[v], qk_scale, src[-(8 * (v >> 2) + (v & 3))]);
-        wave_lds_fence();
-      } else {
-        f32x16 s_odd = zero16();
+      for (int t = 0; t < 8; ++t) pb[c16][t] = T(pe[8 * c16 + t]);
+  };
+  // O^T += V^T P^T
+  auto pv = [&](const unsigned char* vt_b, const bf16x8 (&pb)[2]) {
 #pragma unroll
-        for (int kk = 0; kk < D / 16; ++kk) {
-          const bf16x8 kf = frag_kp(kt_b, h2 + 2 * kk);
-          if (kk & 1) mma32(kf, qreg[kk], s_odd);
-          else mma32(kf, qreg[kk], s);
-        }
+    for (int c16 = 0; c16 < N / 16; ++c16) {
 #pragma unroll
-        for (int v = 0; v < 16; ++v) s[v] = (s[v] + s_odd[v]) * qk_scale;
-      }
-      if (mask) {
-#pragma unroll
-        for (int v = 0; v < 16; ++v) {
-          const int dd = qa - (j0 + 8 * (v >> 2) + 4 * h2 + (v & 3));
-          if (dd < 0 || (W > 0 && dd >= W)) s[v] = -INFINITY;
-        }
-      }
-
-      f32x16 pexp;
-      float mx = -INFINITY;
-      {
-        const float nm = -p.c2 * m_run;
-#pragma unroll
-        for (int v = 0; v < 16; ++v) {
-          mx = fmaxf(mx, s[v]);
-          pexp[v] = fast_exp2(fmaf(s[v], p.c2, nm));
-        }
-      }
-      mx = pair_max32(mx);
-      if (__builtin_amdgcn_ballot_w64(mx > m_run + lazy) != 0) {
-        const float m_new = fmaxf(m_run, mx);
-        const float corr = fast_exp2(p.c2 * (m_run - m_new));
-        m_run = m_new;
-        l_run *= corr;
-#pragma unroll
-        for (int i = 0; i < D / 32; ++i)
-#pragma unroll
-          for (int v = 0; v < 16; ++v) o[i][v] *= corr;
-        const float nm = -p.c2 * m_run;
-#pragma unroll
-        for (int v = 0; v < 16; ++v) pexp[v] = fast_exp2(fmaf(s[v], p.c2, nm));
-      }
-      float psum = 0.0f;
-#pragma unroll
-      for (int v = 0; v < 16; ++v) psum += pexp[v];
-      l_run += psum;
-
-      // O^T += V^T P^T: the transpose read of PreV<__bf16> with V's swizzle.
-      // Lane (G, s) reads rows 16*c16 + 4*(G/2) + s/4 (+8), columns
-      // 32*db + 16*(G%2) + 4*(s%4): chunk 4*db + 2*(G%2) + (s%4)/2, half s%2.
-      const int Gq = lane >> 4, sq = lane & 15;
-      const int vsw = 2 * ((sq >> 2) & 3);  // rows r and r+8 share r & 3 = s/4
-#pragma unroll
-      for (int c16 = 0; c16 < N / 16; ++c16) {
-        bf16x8 pb;
-#pragma unroll
-        for (int t = 0; t < 8; ++t) pb[t] = T(pexp[8 * c16 + t]);
-        const unsigned char* r0 = vt_b + (16 * c16 + 4 * (Gq >> 1) + (sq >> 2)) * C::ROWB + ((sq & 1) << 3);
-#pragma unroll
-        for (int db = 0; db < D / 32; ++db) {
-          const int q = 4 * db + 2 * (Gq & 1) + ((sq & 3) >> 1);
-          const T* p0 = reinterpret_cast<const T*>(r0 + ((q ^ vsw) << 4));
-          const s16x4 x = lds_read_tr(p0);
-          const s16x4 y = lds_read_tr(p0 + 8 * (C::ROWB / 2));
-          const bf16x8 vf = __builtin_bit_cast(bf16x8, __builtin_shufflevector(x, y, 0, 1, 2, 3, 4, 5, 6, 7));
-          mma32(vf, pb, o[db]);
-        }
+      for (int db = 0; db < D / 32; ++db) {
+        const T* p0 = reinterpret_cast<const T*>(vt_b + 16 * c16 * C::ROWB + offv[db & 1] + 128 * (db >> 1));
+        const s16x4 x = lds_read_tr(p0);
+        const s16x4 y = lds_read_tr(p0 + 8 * (C::ROWB / 2));
+        const bf16x8 vf = __builtin_bit_cast(bf16x8, __builtin_shufflevector(x, y, 0, 1, 2, 3, 4, 5, 6, 7));
+        mma32(vf, pb[c16], o[db]);
       }
     }
-    dma_wait();  // this wave's part of tile kt+1 has landed
+  };
+
+  // ---- prologue: tile kt_lo in LDS, the scores of tile kt_lo, K and P of
+  // tile kt_lo+1 in flight.  The compiler-visible wait also retires the q and
+  // r loads, so no wait for them lands inside the tile loop.
+  issue_kp(kt_lo);
+  issue_v(kt_lo);
+  dma_wait();
+  __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0)
+  __syncthreads();
+  if (kt_lo < kt_hi) issue_kp(kt_lo + 1);
+  f32x16 s_cur = zero16();
+  {
+    const unsigned char* kt_b = smem + C::OFF_K + (kt_lo & 1) * C::TILEB;
+    const unsigned char* pt_b = smem + C::OFF_P + (kt_lo & 1) * C::TILEB;
+    if (band_of(kt_lo)) {
+      first_chunk(kt_lo);
+      f32x16 racc = zero16();
+#pragma unroll
+      for (int kk = 0; kk < D / 16; ++kk) {
+        mma32(frag_kp(kt_b, kk), qreg[kk], s_cur);
+        mma32(frag_kp(pt_b, kk), rreg[kk], racc);
+      }
+      put_chunk(kt_lo, racc);
+      shear_add(kt_lo, s_cur);
+    } else {
+#pragma unroll
+      for (int kk = 0; kk < D / 16; ++kk) mma32(frag_kp(kt_b, kk), qreg[kk], s_cur);
+#pragma unroll
+      for (int v = 0; v < 16; ++v) s_cur[v] *= qk_scale;
+    }
+    if (mask_of(kt_lo)) apply_mask(kt_lo, s_cur);
+  }
+  dma_wait();
+
+  // ---- tile loop.  Iteration kt runs the softmax and PV of tile kt and the
+  // scores of tile kt+1 in one straight-line block, so the matrix cores work
+  // on tile kt+1 while the VALU runs tile kt's exponentials, and the PV MFMAs
+  // overlap the next tile's shear.  LDS holds K and P of tile kt+1 and V of
+  // tile kt; the DMA fills K and P of tile kt+2 and V of tile kt+1.  Tiles
+  // with bias are a suffix of the range (the keys nearest the queries), so
+  // the loop runs in two parts; the last tile (no next scores) is peeled, and
+  // each part is unrolled by two so every LDS address is a lane offset plus a
+  // constant.
+  auto begin_tile = [&](int kt, f32x16& s) {
+    __syncthreads();  // K/P of tile kt+1 and V of tile kt are in LDS; all waves are past iteration kt-1
+    if (kt + 2 <= kt_hi) issue_kp(kt + 2);
+    if (kt + 1 <= kt_hi) issue_v(kt + 1);
+    if (kt > kt_lo && mask_of(kt)) apply_mask(kt, s);
+    // row maximum of tile kt and the (rare) lazy rescale
+    float mx = -INFINITY;
+#pragma unroll
+    for (int v = 0; v < 16; ++v) mx = fmaxf(mx, s[v]);
+    mx = pair_max32(mx);
+    if (__builtin_amdgcn_ballot_w64(mx > m_run + lazy) != 0) {
+      const float m_new = fmaxf(m_run, mx);
+      const float corr = fast_exp2(c2 * (m_run - m_new));
+      m_run = m_new;
+      l_run *= corr;
+#pragma unroll
+      for (int i = 0; i < D / 32; ++i)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) o[i][v] *= corr;
+    }
+    return -c2 * m_run;
+  };
+  // one iteration whose next tile has no bias; PAR = kt & 1
+  auto plain_step = [&](auto par, f32x16& s, f32x16& s_nx, int kt) {
+    constexpr int PAR = decltype(par)::value, NP = PAR ^ 1;
+    const float nm = begin_tile(kt, s);
+    const unsigned char* kt_b = smem + C::OFF_K + NP * C::TILEB;
+    const unsigned char* vt_b = smem + C::OFF_V + PAR * C::TILEB;
+    f32x16 s_odd = zero16();
+    s_nx = zero16();
+#pragma unroll
+    for (int kk = 0; kk < D / 16; ++kk) {
+      const bf16x8 kf = frag_kp(kt_b, kk);
+      if (kk & 1) mma32(kf, qreg[kk], s_odd);
+      else mma32(kf, qreg[kk], s_nx);
+    }
+    bf16x8 pb[2];
+    float psum;
+    exps(s, nm, pb, psum);
+    pv(vt_b, pb);
+#pragma unroll
+    for (int v = 0; v < 16; ++v) s_nx[v] = (s_nx[v] + s_odd[v]) * qk_scale;
+    l_run += psum;
+    dma_wait();  // this wave's parts of the next tiles have landed
+  };
+  // one iteration whose next tile has bias
+  auto band_step = [&](auto par, f32x16& s, f32x16& s_nx, int kt) {
+    constexpr int PAR = decltype(par)::value, NP = PAR ^ 1;
+    const float nm = begin_tile(kt, s);
+    const unsigned char* kt_b = smem + C::OFF_K + NP * C::TILEB;
+    const unsigned char* pt_b = smem + C::OFF_P + NP * C::TILEB;
+    const unsigned char* vt_b = smem + C::OFF_V + PAR * C::TILEB;
+    f32x16 racc = zero16();
+    s_nx = zero16();
+#pragma unroll
+    for (int kk = 0; kk < D / 16; ++kk) mma32(frag_kp(pt_b, kk), rreg[kk], racc);
+#pragma unroll
+    for (int kk = 0; kk < D / 16; ++kk) mma32(frag_kp(kt_b, kk), qreg[kk], s_nx);
+    bf16x8 pb[2];
+    float psum;
+    exps(s, nm, pb, psum);
+    put_chunk(NP, racc);
+    pv(vt_b, pb);
+    shear_add(NP, s_nx);
+    l_run += psum;
+    dma_wait();  // this wave's parts of the next tiles have landed
+  };
+  f32x16 s_b;
+  int kt = kt_lo;
+  // iterations kt .. kt_end-1, scores in s_cur at entry and exit
+  auto run = [&](auto step, int kt_end) {
+    if ((kt & 1) && kt < kt_end) {
+      step(IntC<1>{}, s_cur, s_b, kt);
+      s_cur = s_b;
+      ++kt;
+    }
+    for (; kt + 1 < kt_end; kt += 2) {
+      step(IntC<0>{}, s_cur, s_b, kt);
+      step(IntC<1>{}, s_b, s_cur, kt + 1);
+    }
+    if (kt < kt_end) {
+      step(IntC<0>{}, s_cur, s_b, kt);
+      s_cur = s_b;
+      ++kt;
+    }
+  };
+  const int kt_band = E > 0 ? max(kt_lo, (q0 - E + 1) / N) : kt_hi + 1;  // first tile with bias
+  run(plain_step, min(kt_hi, kt_band - 1));
+  if (kt < kt_hi && !band_of(kt_lo)) first_chunk(kt + 1);
+  run(band_step, kt_hi);
+  {
+    const float nm = begin_tile(kt, s_cur);
+    bf16x8 pb[2];
+    float psum;
+    exps(s_cur, nm, pb, psum);
+    pv(smem + C::OFF_V + (kt & 1) * C::TILEB, pb);
+    l_run += psum;
   }
 
   // ---- epilogue: normalise, stage the wave's 32 x D tile in LDS, write whole
