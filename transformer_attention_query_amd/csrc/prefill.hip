@@ -583,6 +583,18 @@ __device__ __forceinline__ void dma16(const void* src, unsigned lds_base) {
       : "v"(src), "s"(lds_base)
       : "memory");
 }
+// The same with a uniform 64-bit base and a 32-bit per-lane byte offset.
+__device__ __forceinline__ void dma16s(const void* base, unsigned off, unsigned lds_base) {
+  unsigned saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %3\n\t"
+      "global_load_lds_dwordx4 %1, %2\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "v"(off), "s"(base), "s"(lds_base)
+      : "memory");
+}
 __device__ __forceinline__ void dma_wait() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
 // A zero P row: DMA source for distances outside [0, E), so their relative
@@ -667,27 +679,32 @@ __global__ __launch_bounds__(512, 1) void prefill_dma_kernel(PrefillArgs p, int 
   const int dslot = lane & 15;
   const int qk_src = dslot ^ (drow & 7);        // K / P chunk landing in this slot
   const int qv_src = dslot ^ (2 * (drow & 3));  // V chunk landing in this slot
-  const size_t kv_row_stride = size_t(Hkv) * D;
-  const T* kbase = kg + (size_t(b) * T_ * Hkv + kvh) * D;
-  const T* vbase = vg + (size_t(b) * T_ * Hkv + kvh) * D;
-  const int pvec = d_r / 8;
+  // K and V rows of this sequence and kv head: a uniform base plus a 32-bit
+  // byte offset per lane (the host keeps T*Hkv*D*2 below 2^31).
+  const T* kseq = kg + (size_t(b) * T_ * Hkv + kvh) * D;
+  const T* vseq = vg + (size_t(b) * T_ * Hkv + kvh) * D;
+  const unsigned rowb = unsigned(Hkv) * D * 2;
+  const unsigned kcol = 16u * unsigned(qk_src), vcol = 16u * unsigned(qv_src);
+  const unsigned pcol = 16u * unsigned(min(qk_src, d_r / 8 - 1));
+  const T* const zrow = kZeroPRow + 8 * qk_src;
   const unsigned lds0 = unsigned(reinterpret_cast<size_t>(smem)) + 1024u * unsigned(w);
   auto chunk0 = [&](int kt) { return (q0 - kt * N) / N; };
+  auto kv_off = [&](int kt) { return unsigned(min(kt * N + drow, T_ - 1)) * rowb; };
   // K and the tile's new distance chunk of P rows (buffer kt & 1)
   auto issue_kp = [&](int kt) {
     const int buf = kt & 1;
-    const size_t j = size_t(min(kt * N + drow, T_ - 1)) * kv_row_stride;
-    dma16(kbase + j + 8 * qk_src, __builtin_amdgcn_readfirstlane(lds0 + C::OFF_K + buf * C::TILEB));
+    dma16s(kseq, kv_off(kt) + kcol, __builtin_amdgcn_readfirstlane(lds0 + C::OFF_K + buf * C::TILEB));
     if (E > 0) {
       const int d = (chunk0(kt) - 1) * N + drow;
-      const T* src = (d >= 0 && d < E) ? pcg + size_t(d) * d_r + 8 * min(qk_src, pvec - 1) : kZeroPRow + 8 * qk_src;
+      const T* src = unsigned(d) < unsigned(E)
+                         ? reinterpret_cast<const T*>(reinterpret_cast<const char*>(pcg) + unsigned(d) * unsigned(2 * d_r) + pcol)
+                         : zrow;
       dma16(src, __builtin_amdgcn_readfirstlane(lds0 + C::OFF_P + buf * C::TILEB));
     }
   };
   auto issue_v = [&](int kt) {
     const int buf = kt & 1;
-    const size_t j = size_t(min(kt * N + drow, T_ - 1)) * kv_row_stride;
-    dma16(vbase + j + 8 * qv_src, __builtin_amdgcn_readfirstlane(lds0 + C::OFF_V + buf * C::TILEB));
+    dma16s(vseq, kv_off(kt) + vcol, __builtin_amdgcn_readfirstlane(lds0 + C::OFF_V + buf * C::TILEB));
   };
   auto band_of = [&](int kt) { return E > 0 && max(0, q0 - (kt * N + N - 1)) < E; };
   auto mask_of = [&](int kt) {
@@ -985,7 +1002,11 @@ hipError_t launch_extend(int dtype, const PrefillArgs& a, hipStream_t stream) {
 
 hipError_t launch_prefill(int dtype, const PrefillArgs& a, hipStream_t stream) {
   if (dtype == 1) {
-    if ((a.Hq / a.Hkv) % 8 == 0) return launch_prefill_dma(a, stream);
+    // The DMA kernel addresses one sequence's K / V rows and P with 32-bit
+    // byte offsets.
+    const bool offsets32 = (long long)a.T * a.Hkv * kHeadDim * 2 < (1LL << 31) &&
+                           (long long)a.E * a.d_r * 2 < (1LL << 31);
+    if ((a.Hq / a.Hkv) % 8 == 0 && offsets32) return launch_prefill_dma(a, stream);
     return launch_prefill_tiles<__bf16, 8>(a, stream);
   }
   return launch_prefill_tiles<float, 2>(a, stream);
