@@ -16,3 +16,10 @@ from .relattn_oracle import (  # noqa: F401
     scale_factor,
     sheared_bias,
 )
+from .prologue_oracle import (  # noqa: F401
+    STATE_ROWS,
+    cache_positions,
+    prologue,
+    rms_norm,
+    short_conv,
+)
