@@ -112,6 +112,52 @@ int rel_attn_extend(const void* q, const void* k, const void* v, const void* r,
                     void* stream);
 
 /*
+ * Attention prologue: the step before the attention kernels on the new
+ * tokens' q, k and v projections (page "SGLang and Miles Add Day-0 Support
+ * for Inkling", section "ShortConv Optimization", paragraph "KV ShortConv +
+ * QK-norm + KV store"), in one kernel:
+ *   k' = RMSNorm_k(ShortConv_k(k))  -> k cache
+ *   v' = ShortConv_v(v)             -> v cache
+ *   q' = RMSNorm_q(q)               -> q_out
+ * ShortConv is the filter of section "Short Convolution (ShortConv)":
+ * y[t,c] = x[t,c] + sum_{d < conv_width} w[c,d] * x[t-d,c] over the Hkv*D
+ * channels of a K (V) row, accumulated in fp32 with the residual added last.
+ * RMSNorm is per head over D: x / sqrt(mean(x^2) + eps) * g, with one
+ * D-vector g for q and one for k shared by all heads.  r is not touched.
+ *   q_in [total_q, Hq, D], k_in and v_in [total_q, Hkv, D]: raw projections,
+ *     packed by sequence like extend (rows q_start[b] .. q_start[b+1]-1).
+ *   conv_k, conv_v [Hkv*D, conv_width]; q_norm_w, k_norm_w [D]: dtype.
+ *   q_out [total_q, Hq, D]: may be q_in itself (in place); no other output
+ *     may alias an input.
+ *   k_cache, v_cache: the caches of rel_attn_extend / rel_attn_decode_paged
+ *     (contiguous [B, cache_len, Hkv, D] when block_table is NULL, else pages
+ *     [num_pages, page_size, Hkv, D] with any positive page_size).  New row t
+ *     of sequence b goes to position kv_len[b] - n_b + t; rows whose position
+ *     falls outside the cache (or on a page id outside [0, num_pages)) are
+ *     not written.
+ *   state_in, state_out [B, 2, 3, Hkv*D] (dtype) or NULL: the raw K (index
+ *     0) and V (index 1) rows of the three positions before the chunk, oldest
+ *     first; NULL state_in means zeros (a fresh sequence).  state_out receives
+ *     the raw rows of each sequence's last three positions (state_in's rows
+ *     carried over for sequences with fewer than three new rows, or none);
+ *     state_out must not alias state_in.
+ *   q_start [B+1], kv_len [B], block_table [B, max_pages]: int32 device
+ *     arrays, 4-byte aligned.  Whatever they hold, every access stays in
+ *     bounds (offsets are clamped to [0, total_q]).
+ * conv_width in 1 .. 4 (4 in the pages' configurations), eps >= 0.
+ * B == 0, or total_q == 0 with state_out NULL, is a no-op that returns RA_OK.
+ */
+int rel_attn_prologue(const void* q_in, const void* k_in, const void* v_in,
+                      const void* conv_k, const void* conv_v,
+                      const void* q_norm_w, const void* k_norm_w, float eps,
+                      const void* state_in, void* state_out,
+                      void* q_out, void* k_cache, void* v_cache, int dtype,
+                      int B, int total_q, const int* q_start, const int* kv_len,
+                      int cache_len, const int* block_table, int max_pages,
+                      int num_pages, int page_size, int Hq, int Hkv, int D,
+                      int conv_width, void* stream);
+
+/*
  * Decode plan: a pure function of the shape.  Writes the number of KV splits
  * the decode call will use (num_splits_req > 0 asks for that many; the plan
  * may use fewer so that every split holds at least one 32-key step; 0 lets

@@ -36,7 +36,7 @@ def _declared_functions():
 def test_header_declares_the_boundary():
     names = _declared_functions()
     for n in ("rel_attn_prefill", "rel_attn_extend", "rel_attn_decode", "rel_attn_decode_paged",
-              "rel_attn_decode_plan", "rel_logits",
+              "rel_attn_decode_plan", "rel_logits", "rel_attn_prologue",
               "rel_attn_last_error", "rel_attn_version", "rel_attn_scale_factor"):
         assert n in names
 
@@ -268,3 +268,49 @@ def _decode_paged(lib, **kw):
 def test_decode_paged_rejects_bad_arguments(lib, kw, code, frag):
     assert _decode_paged(lib, **kw) == code
     assert frag in lib.rel_attn_last_error().decode()
+
+
+def _prologue(lib, **kw):
+    a = dict(q_in=FAKE, k_in=FAKE + 0x100, v_in=FAKE + 0x200, conv_k=FAKE + 0x300, conv_v=FAKE + 0x400,
+             qw=FAKE + 0x500, kw_=FAKE + 0x600, eps=1e-6, st_in=None, st_out=None, q_out=FAKE + 0x700,
+             k_cache=FAKE + 0x800, v_cache=FAKE + 0x900, dtype=RA_BF16, B=2, total_q=10, q_start=FAKE + 0xa00,
+             kv_len=FAKE + 0xb00, cache_len=64, block_table=None, max_pages=0, num_pages=0, page_size=0,
+             Hq=8, Hkv=1, D=128, W=4)
+    a.update(kw)
+    return lib.rel_attn_prologue(a["q_in"], a["k_in"], a["v_in"], a["conv_k"], a["conv_v"], a["qw"], a["kw_"],
+                                 a["eps"], a["st_in"], a["st_out"], a["q_out"], a["k_cache"], a["v_cache"],
+                                 a["dtype"], a["B"], a["total_q"], a["q_start"], a["kv_len"], a["cache_len"],
+                                 a["block_table"], a["max_pages"], a["num_pages"], a["page_size"], a["Hq"],
+                                 a["Hkv"], a["D"], a["W"], None)
+
+
+@pytest.mark.parametrize("kw,code,frag", [
+    (dict(W=5), RA_ERR_UNSUPPORTED, "conv_width"),
+    (dict(W=0), RA_ERR_UNSUPPORTED, "conv_width"),
+    (dict(D=64), RA_ERR_UNSUPPORTED, "head dim"),
+    (dict(eps=-1.0), RA_ERR_INVALID_ARG, "eps"),
+    (dict(eps=float("inf")), RA_ERR_INVALID_ARG, "eps"),
+    (dict(dtype=3), RA_ERR_INVALID_ARG, "dtype"),
+    (dict(q_start=None), RA_ERR_INVALID_ARG, "q_start"),
+    (dict(kv_len=FAKE + 2), RA_ERR_INVALID_ARG, "aligned"),
+    (dict(conv_k=FAKE + 1), RA_ERR_INVALID_ARG, "element size"),
+    (dict(k_cache=FAKE + 8), RA_ERR_INVALID_ARG, "16-byte"),
+    (dict(k_cache=FAKE + 0x900), RA_ERR_INVALID_ARG, "same buffer"),
+    (dict(v_cache=FAKE), RA_ERR_INVALID_ARG, "alias"),
+    (dict(q_out=FAKE + 0x100), RA_ERR_INVALID_ARG, "q_out"),
+    (dict(st_in=FAKE + 0xc00, st_out=FAKE + 0xc00), RA_ERR_INVALID_ARG, "state_out aliases"),
+    (dict(cache_len=0), RA_ERR_INVALID_ARG, "cache_len"),
+    (dict(block_table=FAKE + 0xd00, page_size=0, max_pages=4, num_pages=8), RA_ERR_INVALID_ARG, "page_size"),
+    (dict(block_table=FAKE + 0xd00, page_size=16, max_pages=0, num_pages=8), RA_ERR_INVALID_ARG, "max_pages"),
+    (dict(Hkv=0), RA_ERR_INVALID_ARG, "positive"),
+])
+def test_prologue_rejects_bad_arguments(lib, kw, code, frag):
+    assert _prologue(lib, **kw) == code
+    assert frag in lib.rel_attn_last_error().decode()
+
+
+def test_prologue_empty_is_a_noop(lib):
+    nulls = dict(q_in=None, k_in=None, v_in=None, q_out=None, k_cache=None, v_cache=None, conv_k=None,
+                 conv_v=None, qw=None, kw_=None, q_start=None, kv_len=None)
+    assert _prologue(lib, B=0, **nulls) == RA_OK
+    assert _prologue(lib, total_q=0, **nulls) == RA_OK

@@ -1,7 +1,8 @@
 """MI355X (gfx950) relative-attention forward: HIP kernels behind a C ABI.
 
-``prefill``, ``extend``, ``decode``, ``decode_paged``, ``decode_plan`` and ``rel_logits`` call the compiled
-library ``librelattn.so`` (built in-tree by ``__graft_entry__.build()`` or
+``prefill``, ``extend``, ``decode``, ``decode_paged``, ``decode_plan``,
+``prologue`` and ``rel_logits`` call the compiled library ``librelattn.so``
+(built in-tree by ``__graft_entry__.build()`` or
 ``python -m transformer_attention_query_amd.build``).  There is no fallback:
 if the library is missing the calls raise.
 """
@@ -15,6 +16,7 @@ from .binding import (  # noqa: F401
     library_path,
     load_library,
     prefill,
+    prologue,
     rel_logits,
     scale_factor,
     version,

@@ -58,6 +58,9 @@ def _declare(lib):
     lib.rel_attn_decode_paged.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, vp, vp, i32, i32, i32,
                                           i32, i32, i32, i32, f32, i32, i32, i32, i32, vp, sz, vp]
     lib.rel_attn_decode_paged.restype = i32
+    lib.rel_attn_prologue.argtypes = [vp, vp, vp, vp, vp, vp, vp, f32, vp, vp, vp, vp, vp, i32, i32, i32, vp, vp,
+                                      i32, vp, i32, i32, i32, i32, i32, i32, i32, vp]
+    lib.rel_attn_prologue.restype = i32
     lib.rel_logits.argtypes = [vp, vp, vp, i32, i64, i32, i32, i32, i32, i64, vp]
     lib.rel_logits.restype = i32
     lib.rel_attn_last_error.argtypes = []
@@ -363,3 +366,75 @@ def decode_paged(q: torch.Tensor, k_pages: torch.Tensor, v_pages: torch.Tensor, 
                                      int(rel_extent), int(window), 1 if log_scale else 0, ns, _ptr(workspace),
                                      workspace.numel() * workspace.element_size(), _stream(dev)))
     return out, lse
+
+
+def prologue(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, conv_k: torch.Tensor, conv_v: torch.Tensor,
+             q_norm_w: torch.Tensor, k_norm_w: torch.Tensor, eps: float, q_start: torch.Tensor,
+             kv_len: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
+             block_table: Optional[torch.Tensor] = None, state_in: Optional[torch.Tensor] = None,
+             state_out: Optional[torch.Tensor] = None, q_out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Attention prologue (rel_attn_prologue): K/V ShortConv, Q/K RMSNorm and the cache write.
+
+    q [total_q,Hq,D], k/v [total_q,Hkv,D] raw projections packed by ``q_start``
+    [B+1]; ``kv_len`` [B] (int32, device) sets each sequence's positions as in
+    ``extend``.  conv_k/conv_v [Hkv*D, W]; q_norm_w/k_norm_w [D].  k_cache and
+    v_cache are written in place (contiguous [B,cache_len,Hkv,D], or pages
+    [num_pages,page_size,Hkv,D] with ``block_table`` [B,max_pages]).
+    state_in/state_out [B,2,3,Hkv*D] carry the raw rows before / after the
+    chunk.  Returns q_out [total_q,Hq,D] (``q`` itself may be passed as
+    ``q_out``).
+    """
+    lib = load_library()
+    dev = q.device
+    dt = q.dtype
+    if dt not in _DTYPE_CODE:
+        raise TypeError(f"unsupported dtype {dt}")
+    _need(q, "q", dt, dev, 3)
+    _need(k, "k", dt, dev, 3)
+    _need(v, "v", dt, dev, 3)
+    _need(conv_k, "conv_k", dt, dev, 2)
+    _need(conv_v, "conv_v", dt, dev, 2)
+    _need(q_norm_w, "q_norm_w", dt, dev, 1)
+    _need(k_norm_w, "k_norm_w", dt, dev, 1)
+    _need(q_start, "q_start", torch.int32, dev, 1)
+    _need(kv_len, "kv_len", torch.int32, dev, 1)
+    _need(k_cache, "k_cache", dt, dev, 4)
+    _need(v_cache, "v_cache", dt, dev, 4)
+    total_q, Hq, D = q.shape
+    Hkv = k.shape[1]
+    B = kv_len.shape[0]
+    if q_start.shape[0] != B + 1:
+        raise ValueError(f"q_start must have B+1 = {B + 1} entries, got {q_start.shape[0]}")
+    if k.shape != (total_q, Hkv, D) or v.shape != k.shape:
+        raise ValueError(f"k and v must be [total_q={total_q}, Hkv, D={D}], got {tuple(k.shape)} and {tuple(v.shape)}")
+    W = conv_k.shape[1]
+    if conv_k.shape != (Hkv * D, W) or conv_v.shape != conv_k.shape:
+        raise ValueError(f"conv_k and conv_v must be [Hkv*D={Hkv * D}, W], got {tuple(conv_k.shape)}")
+    if q_norm_w.shape != (D,) or k_norm_w.shape != (D,):
+        raise ValueError(f"q_norm_w and k_norm_w must be [D={D}]")
+    if v_cache.shape != k_cache.shape:
+        raise ValueError("v_cache shape differs from k_cache")
+    if block_table is None:
+        cache_len, max_pages, num_pages, page_size = k_cache.shape[1], 0, 0, 0
+        if k_cache.shape[0] != B:
+            raise ValueError(f"contiguous caches must be [B={B}, cache_len, Hkv, D], got {tuple(k_cache.shape)}")
+    else:
+        _need(block_table, "block_table", torch.int32, dev, 2)
+        if block_table.shape[0] != B:
+            raise ValueError(f"block_table must be [B={B}, max_pages], got {tuple(block_table.shape)}")
+        cache_len, max_pages, num_pages, page_size = 0, block_table.shape[1], k_cache.shape[0], k_cache.shape[1]
+    for name, st in (("state_in", state_in), ("state_out", state_out)):
+        if st is not None:
+            _need(st, name, dt, dev, 4)
+            if st.shape != (B, 2, 3, Hkv * D):
+                raise ValueError(f"{name} must be [B={B}, 2, 3, Hkv*D={Hkv * D}], got {tuple(st.shape)}")
+    if q_out is None:
+        q_out = torch.empty_like(q)
+    else:
+        _need(q_out, "q_out", dt, dev, 3)
+    _check(lib.rel_attn_prologue(_ptr(q), _ptr(k), _ptr(v), _ptr(conv_k), _ptr(conv_v), _ptr(q_norm_w),
+                                 _ptr(k_norm_w), float(eps), _ptr(state_in), _ptr(state_out), _ptr(q_out),
+                                 _ptr(k_cache), _ptr(v_cache), _DTYPE_CODE[dt], B, total_q, _ptr(q_start),
+                                 _ptr(kv_len), cache_len, _ptr(block_table), max_pages, num_pages, page_size,
+                                 Hq, Hkv, D, W, _stream(dev)))
+    return q_out

@@ -146,6 +146,76 @@ int rel_attn_extend(const void* q, const void* k, const void* v, const void* r, 
   return ok();
 }
 
+int rel_attn_prologue(const void* q_in, const void* k_in, const void* v_in, const void* conv_k, const void* conv_v,
+                      const void* q_norm_w, const void* k_norm_w, float eps, const void* state_in, void* state_out,
+                      void* q_out, void* k_cache, void* v_cache, int dtype, int B, int total_q, const int* q_start,
+                      const int* kv_len, int cache_len, const int* block_table, int max_pages, int num_pages,
+                      int page_size, int Hq, int Hkv, int D, int conv_width, void* stream) {
+  if (dtype != RA_BF16 && dtype != RA_F32) return fail(RA_ERR_INVALID_ARG, "dtype %d is not RA_BF16 or RA_F32", dtype);
+  if (B < 0) return fail(RA_ERR_INVALID_ARG, "B = %d < 0", B);
+  if (total_q < 0) return fail(RA_ERR_INVALID_ARG, "total_q = %d < 0", total_q);
+  if (Hq <= 0 || Hkv <= 0) return fail(RA_ERR_INVALID_ARG, "Hq = %d and Hkv = %d must be positive", Hq, Hkv);
+  if (D != relattn::kHeadDim) return fail(RA_ERR_UNSUPPORTED, "head dim D = %d: only 128 is supported", D);
+  if (conv_width < 1 || conv_width > 4)
+    return fail(RA_ERR_UNSUPPORTED, "conv_width = %d: supported widths are 1 .. 4", conv_width);
+  if (!(eps >= 0.0f) || !std::isfinite(eps)) return fail(RA_ERR_INVALID_ARG, "eps must be finite and >= 0");
+  // With no new row the call only carries the states of the B sequences over.
+  if (B == 0 || (total_q == 0 && state_out == nullptr)) return ok();
+  const bool rows = total_q > 0;
+  int rc;
+  if ((rc = check_ptr(q_in, "q_in", rows)) || (rc = check_ptr(k_in, "k_in", rows)) ||
+      (rc = check_ptr(v_in, "v_in", rows)) || (rc = check_ptr(q_out, "q_out", rows)) ||
+      (rc = check_ptr(k_cache, "k_cache", rows)) || (rc = check_ptr(v_cache, "v_cache", rows)) ||
+      (rc = check_ptr(q_norm_w, "q_norm_w", rows)) || (rc = check_ptr(k_norm_w, "k_norm_w", rows)) ||
+      (rc = check_ptr(state_in, "state_in", false)) || (rc = check_ptr(state_out, "state_out", false)))
+    return rc;
+  if (rows && (conv_k == nullptr || conv_v == nullptr))
+    return fail(RA_ERR_INVALID_ARG, "conv_k and conv_v must not be NULL");
+  const size_t esz = dtype == RA_BF16 ? 2 : 4;
+  if ((reinterpret_cast<uintptr_t>(conv_k) | reinterpret_cast<uintptr_t>(conv_v)) & (esz - 1))
+    return fail(RA_ERR_INVALID_ARG, "conv_k and conv_v must be aligned to the element size");
+  if (q_start == nullptr || kv_len == nullptr) return fail(RA_ERR_INVALID_ARG, "q_start and kv_len must not be NULL");
+  if ((reinterpret_cast<uintptr_t>(q_start) | reinterpret_cast<uintptr_t>(kv_len) |
+       reinterpret_cast<uintptr_t>(block_table)) & 3u)
+    return fail(RA_ERR_INVALID_ARG, "q_start, kv_len and block_table must be 4-byte aligned");
+  if (state_out != nullptr && state_out == state_in)
+    return fail(RA_ERR_INVALID_ARG, "state_out aliases state_in (the new state would overwrite rows still to be read)");
+  if (rows && k_cache == v_cache) return fail(RA_ERR_INVALID_ARG, "k_cache and v_cache are the same buffer");
+  const void* outs[3] = {k_cache, v_cache, state_out};
+  const void* ins[5] = {q_in, k_in, v_in, state_in, q_norm_w};
+  for (const void* o : outs)
+    for (const void* i : ins)
+      if (o != nullptr && o == i) return fail(RA_ERR_INVALID_ARG, "an output buffer aliases an input");
+  if (rows && (q_out == k_in || q_out == v_in)) return fail(RA_ERR_INVALID_ARG, "q_out aliases k_in or v_in");
+  if (!rows) {
+    // only the state copies run; the cache geometry is not used
+  } else if (block_table == nullptr) {
+    if (cache_len <= 0) return fail(RA_ERR_INVALID_ARG, "cache_len = %d: contiguous caches need cache_len >= 1", cache_len);
+  } else {
+    if (page_size <= 0) return fail(RA_ERR_INVALID_ARG, "page_size = %d must be positive", page_size);
+    if (max_pages <= 0 || num_pages <= 0)
+      return fail(RA_ERR_INVALID_ARG, "max_pages = %d and num_pages = %d must be positive", max_pages, num_pages);
+    if ((long long)max_pages * page_size > 0x7fffffffLL)
+      return fail(RA_ERR_UNSUPPORTED, "max_pages * page_size too large");
+  }
+  if ((long long)total_q * (Hq + 2LL * Hkv) / 16 + (long long)B * 2 * Hkv > 0x7fffffffLL - 16)
+    return fail(RA_ERR_UNSUPPORTED, "total_q = %d too large for one launch", total_q);
+
+  relattn::PrologueArgs a;
+  a.q_in = q_in; a.k_in = k_in; a.v_in = v_in; a.conv_k = conv_k; a.conv_v = conv_v;
+  a.q_norm_w = q_norm_w; a.k_norm_w = k_norm_w; a.state_in = state_in; a.state_out = state_out;
+  a.q_out = q_out; a.k_cache = k_cache; a.v_cache = v_cache;
+  a.q_start = q_start; a.kv_len = kv_len; a.btab = block_table;
+  a.eps = eps; a.B = B; a.total_q = total_q; a.Hq = Hq; a.Hkv = Hkv; a.conv_w = conv_width;
+  a.cap = block_table == nullptr ? cache_len : 0;
+  a.max_pages = block_table == nullptr ? 0 : max_pages;
+  a.num_pages = block_table == nullptr ? 0 : num_pages;
+  a.page_size = block_table == nullptr ? 1 : page_size;
+  hipError_t e = relattn::launch_prologue(dtype, a, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(RA_ERR_HIP, "prologue launch failed: %s", hipGetErrorString(e));
+  return ok();
+}
+
 int rel_attn_decode_plan(int B, int L, int Hq, int Hkv, int D, int num_splits_req, int window, int rel_extent,
                          int* num_splits_out, size_t* workspace_bytes_out) {
   if (num_splits_out == nullptr || workspace_bytes_out == nullptr)

@@ -62,6 +62,28 @@ struct DecodeArgs {
   float alpha = 0.0f;
 };
 
+// Attention prologue (see rel_attn_prologue): device pointers and host bounds.
+struct PrologueArgs {
+  const void* q_in;
+  const void* k_in;
+  const void* v_in;
+  const void* conv_k;    // [Hkv*D, conv_w]
+  const void* conv_v;
+  const void* q_norm_w;  // [D]
+  const void* k_norm_w;  // [D]
+  const void* state_in;  // [B, 2, 3, Hkv*D] or null (zeros)
+  void* state_out;       // [B, 2, 3, Hkv*D] or null (not written)
+  void* q_out;
+  void* k_cache;
+  void* v_cache;
+  const int* q_start;    // [B+1]
+  const int* kv_len;     // [B]
+  const int* btab;       // [B, max_pages] or null (contiguous caches of cap rows)
+  float eps;
+  int B, total_q, Hq, Hkv, conv_w;
+  int cap, max_pages, num_pages, page_size;
+};
+
 // out[row * out_stride + oc] = s * r[row] . P_cols[d(oc)] for oc < out_cols,
 // with d(oc) = oc, or d(oc) = rev_base - 1 - oc when rev_base > 0; entries
 // whose d falls outside [0, E) are written as 0.
@@ -90,6 +112,7 @@ DecodePlan plan_decode(int B, int L, int Hq, int Hkv, int num_splits_req, int wi
 
 // Launchers: return hipSuccess or the launch error.  dtype: 1 = bf16, 2 = fp32.
 hipError_t launch_prefill(int dtype, const PrefillArgs& a, hipStream_t stream);
+hipError_t launch_prologue(int dtype, const PrologueArgs& a, hipStream_t stream);
 hipError_t launch_extend(int dtype, const PrefillArgs& a, hipStream_t stream);
 hipError_t launch_decode(int dtype, const DecodeArgs& a, hipStream_t stream);
 hipError_t launch_decode_paged(int dtype, const DecodeArgs& a, hipStream_t stream);

@@ -17,6 +17,14 @@ P ~ N(0, 0.02^2)); every tensor is then rounded to the workload dtype.
            seeded random permutation of page slots (a block table), when a
            page size is given.
 
+* prologue: q [N,Hq,D], k [N,Hkv,D], v [N,Hkv,D] (the raw projections of
+           N packed new tokens), conv_k, conv_v [Hkv*D,W] times ``conv_std``
+           (0.3), q_norm_w, k_norm_w [D] as 1 + 0.1 * normal, then (if asked)
+           the state [B,2,3,Hkv*D], then the caches' prior contents
+           [B,Lcap,Hkv,D] for k and v, cut into pages as for extend.  The
+           pages give no distribution for these weights; the recipe only keeps
+           the filter and norm outputs of order one.
+
 P is drawn in the orientation of the method's notation (column d holds the
 projection for distance d).  The library takes it distance-major, as
 ``P_cols`` [E, d_r] with ``P_cols[d] = P[:, d]``: the same numbers, stored so
@@ -32,7 +40,7 @@ from typing import Dict, Optional
 import torch
 
 __all__ = ["Workload", "WORKLOADS", "make_prefill_inputs", "make_decode_inputs", "make_extend_inputs",
-           "make_inputs", "torch_dtype"]
+           "make_prologue_inputs", "make_inputs", "torch_dtype"]
 
 
 def torch_dtype(name: str) -> torch.dtype:
@@ -43,7 +51,7 @@ def torch_dtype(name: str) -> torch.dtype:
 class Workload:
     """One named relative-attention workload (shapes, masks and dtype)."""
     name: str
-    kind: str            # "prefill", "decode" or "extend"
+    kind: str            # "prefill", "decode", "extend" or "prologue"
     dtype: str           # "bf16" or "fp32"
     B: int
     T: int               # prefill: sequence length; decode, extend: kv length L
@@ -56,8 +64,8 @@ class Workload:
     log_scale: bool = False
     alpha: float = 1.0 / math.sqrt(128.0)
     num_splits: int = 0  # decode only; 0 = library's choice
-    n_new: int = 0       # extend only: new query rows per sequence (the last n_new of its T)
-    page_size: int = 0   # extend only: rows per KV page; 0 = contiguous caches
+    n_new: int = 0       # extend, prologue: new rows per sequence (the last n_new of its T)
+    page_size: int = 0   # extend, prologue: rows per KV page; 0 = contiguous caches
     notes: str = field(default="", compare=False)
 
 
@@ -86,6 +94,12 @@ WORKLOADS: Dict[str, Workload] = {
         "extend_4x1k_8k_paged", "extend", "bf16", B=4, T=8192, Hq=16, Hkv=2, D=128, d_r=128, E=1024,
         n_new=1024, page_size=64,
         notes="chunked prefill: 4 sequences x 1024 new rows over 7168 cached ones, paged KV (64 rows)"),
+    "prologue_8k": Workload(
+        "prologue_8k", "prologue", "bf16", B=1, T=8192, Hq=16, Hkv=2, D=128, d_r=0, E=0, n_new=8192,
+        notes="attention prologue of an 8192-token prefill: K/V ShortConv (W=4), Q/K RMSNorm, cache write"),
+    "prologue_decode_64": Workload(
+        "prologue_decode_64", "prologue", "bf16", B=64, T=8192, Hq=16, Hkv=2, D=128, d_r=0, E=0, n_new=1,
+        page_size=64, notes="decode-step prologue: 64 sequences x 1 token with carried state, paged KV"),
 }
 
 
@@ -175,8 +189,61 @@ def make_extend_inputs(kv_lens, new_lens, Hq: int, Hkv: int, D: int, d_r: int, E
     return out
 
 
+def make_prologue_inputs(kv_lens, new_lens, Hq: int, Hkv: int, D: int, W: int = 4, dtype: str = "bf16",
+                         seed: int = 0, conv_std: float = 0.3, page_size: int = 0, with_state: bool = True,
+                         device: Optional[str] = None) -> Dict[str, torch.Tensor]:
+    """Seeded prologue inputs: sequence b's last new_lens[b] of kv_lens[b]
+    positions are new (packed in q, k, v).  Returns q, k, v, conv_k, conv_v,
+    q_norm_w, k_norm_w, q_start [B+1], kv_len [B] (int32), state_in
+    [B,2,3,Hkv*D] (with_state), k_cache, v_cache [B,Lcap,Hkv,D] holding prior
+    contents and, with a page size, k_pages, v_pages and block_table as for
+    extend."""
+    B = len(kv_lens)
+    assert len(new_lens) == B and all(0 <= n <= L for n, L in zip(new_lens, kv_lens))
+    gen = torch.Generator("cpu").manual_seed(seed)
+    dt = torch_dtype(dtype)
+    N = int(sum(new_lens))
+    Lcap = max(max(kv_lens), 1)
+    out = {"q": _draw(gen, (N, Hq, D)).to(dt), "k": _draw(gen, (N, Hkv, D)).to(dt),
+           "v": _draw(gen, (N, Hkv, D)).to(dt),
+           "conv_k": (_draw(gen, (Hkv * D, W)) * conv_std).to(dt), "conv_v": (_draw(gen, (Hkv * D, W)) * conv_std).to(dt),
+           "q_norm_w": (1.0 + 0.1 * _draw(gen, (D,))).to(dt), "k_norm_w": (1.0 + 0.1 * _draw(gen, (D,))).to(dt)}
+    if with_state:
+        out["state_in"] = _draw(gen, (B, 2, 3, Hkv * D)).to(dt)
+    kc = _draw(gen, (B, Lcap, Hkv, D)).to(dt)
+    vc = _draw(gen, (B, Lcap, Hkv, D)).to(dt)
+    out["k_cache"], out["v_cache"] = kc, vc
+    out["q_start"] = torch.tensor([0] + list(torch.cumsum(torch.tensor(list(new_lens)), 0).tolist()),
+                                  dtype=torch.int32)
+    out["kv_len"] = torch.tensor(list(kv_lens), dtype=torch.int32)
+    if page_size > 0:
+        pages = [(L + page_size - 1) // page_size for L in kv_lens]
+        max_pages = max(max(pages), 1)
+        n_pages = max(sum(pages), 1)
+        perm = torch.randperm(n_pages, generator=gen)
+        kp = torch.zeros(n_pages, page_size, Hkv, D, dtype=dt)
+        vp = torch.zeros(n_pages, page_size, Hkv, D, dtype=dt)
+        table = torch.zeros(B, max_pages, dtype=torch.int32)
+        slot = 0
+        for b, L in enumerate(kv_lens):
+            for pg in range(pages[b]):
+                dst = int(perm[slot])
+                slot += 1
+                table[b, pg] = dst
+                lo, hi = pg * page_size, min(L, (pg + 1) * page_size)
+                kp[dst, :hi - lo] = kc[b, lo:hi]
+                vp[dst, :hi - lo] = vc[b, lo:hi]
+        out.update(k_pages=kp, v_pages=vp, block_table=table)
+    if device is not None:
+        out = {n: t.to(device) for n, t in out.items()}
+    return out
+
+
 def make_inputs(w: Workload, seed: int = 0, device: Optional[str] = None) -> Dict[str, torch.Tensor]:
     """Inputs of a named workload."""
+    if w.kind == "prologue":
+        return make_prologue_inputs([w.T] * w.B, [w.n_new] * w.B, w.Hq, w.Hkv, w.D, 4, w.dtype, seed,
+                                    page_size=w.page_size, with_state=w.n_new < w.T, device=device)
     if w.kind == "extend":
         return make_extend_inputs([w.T] * w.B, [w.n_new] * w.B, w.Hq, w.Hkv, w.D, w.d_r, w.E, w.dtype, seed,
                                   page_size=w.page_size, device=device)
