@@ -5,7 +5,9 @@ online softmax, PV, epilogue) of the sliding-window layer (B=1, T=8192,
 Hq=16, Hkv=2, D=128, d_r=128, rel_extent=1024, window=1024, bf16) on inputs
 already resident in HBM.  The line also reports the split-KV decode of 64
 sequences x 8192 keys (KV GB/s), each against its roofline, and the fp64 CPU
-oracle timed on a bounded sample of the prefill workload.
+oracle timed on a bounded sample of the prefill workload; the paged decode,
+the extend (chunked prefill) and the attention prologue of an 8192-token
+prefill (K/V ShortConv, Q/K RMSNorm, cache write; HBM GB/s) ride along.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
        python bench.py --copy-calibration   (a plain 1 GiB device copy, for
@@ -31,6 +33,7 @@ PREFILL_WORKLOAD = "swa_prefill_8k"
 DECODE_WORKLOAD = "decode_64x8k"
 EXTEND_WORKLOAD = "extend_4x1k_8k_paged"
 PAGED_DECODE_WORKLOAD = "decode_paged_64x8k"
+PROLOGUE_WORKLOAD = "prologue_8k"
 PREFILL_KERNEL = "prefill_dma_kernel"  # the bf16 path for eight or more query heads per kv head
 DECODE_KERNEL = "decode_split_kernel"
 
@@ -203,6 +206,39 @@ def bench_decode_paged(steps: int, warmup: int):
     return w, nbytes, total_ms / steps, sum(per) / len(per), ns
 
 
+def prologue_bytes(N: int, B: int, Hq: int, Hkv: int, D: int, W: int, state: bool, elem: int = 2) -> int:
+    """Algorithmic bytes of one prologue call: every q, k and v row read once
+    and written once (q_out, the two caches), the filter and norm weights, and
+    the states (read if given, always written)."""
+    rows = 2 * N * (Hq + 2 * Hkv) * D * elem
+    weights = (2 * Hkv * D * W + 2 * D) * elem
+    st = B * 2 * 3 * Hkv * D * elem
+    return rows + weights + st * (2 if state else 1)
+
+
+def bench_prologue(steps: int, warmup: int):
+    """The attention prologue of an 8192-token prefill, caches written in place."""
+    import torch
+    import transformer_attention_query_amd as ra
+    from transformer_attention_query_amd import inputs as tinputs
+
+    w = tinputs.WORKLOADS[PROLOGUE_WORKLOAD]
+    x = {n: t.cuda() for n, t in tinputs.make_inputs(w, seed=0).items()}
+    st_in = x.get("state_in")
+    st_out = torch.empty(w.B, 2, 3, w.Hkv * w.D, dtype=x["q"].dtype, device="cuda")
+    q_out = torch.empty_like(x["q"])
+    stream = torch.cuda.current_stream()
+
+    def step(_i):
+        ra.prologue(x["q"], x["k"], x["v"], x["conv_k"], x["conv_v"], x["q_norm_w"], x["k_norm_w"], 1e-6,
+                    x["q_start"], x["kv_len"], x["k_cache"], x["v_cache"], state_in=st_in, state_out=st_out,
+                    q_out=q_out)
+
+    total_ms, per = _time_launches(step, steps, warmup, stream)
+    nbytes = prologue_bytes(w.B * w.n_new, w.B, w.Hq, w.Hkv, w.D, 4, st_in is not None)
+    return w, nbytes, total_ms / steps, sum(per) / len(per)
+
+
 def cpu_baseline(target_s: float = 15.0):
     """The fp64 oracle, as it stands, on query rows of the prefill workload."""
     import torch
@@ -252,6 +288,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-extend", action="store_true")
+    ap.add_argument("--no-prologue", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
@@ -333,6 +370,19 @@ def main():
                                        "traffic": _traffic("prefill_kernel_extend",
                                                            _src_hash("prefill.hip", "device_common.hpp")),
                                        "avg_launch_us": round(e_kernel_ms * 1e3, 2)}}
+    if not args.no_prologue:
+        gw, g_bytes, g_ms, g_kernel_ms = bench_prologue(args.steps, args.warmup)
+        print(f"# prologue {gw.name}: {g_ms * 1e3:.1f} us/step", file=sys.stderr, flush=True)
+        gk = g_bytes / (g_kernel_ms * 1e-3) / 1e9
+        line["prologue"] = {"workload": gw.name, "value": round(g_bytes / (g_ms * 1e-3) / 1e9, 1), "unit": "GB/s",
+                            "ms_per_step": round(g_ms, 5), "algorithmic_bytes": g_bytes,
+                            "config": {"B": gw.B, "tokens": gw.B * gw.n_new, "Hq": gw.Hq, "Hkv": gw.Hkv, "D": gw.D,
+                                       "conv_width": 4, "page_size": gw.page_size},
+                            "roofline": {"bound": "hbm", "kernel": "prologue_kernel", "achieved": round(gk, 1),
+                                         "peak": PEAK_HBM_GBPS, "unit": "GB/s", "frac": round(gk / PEAK_HBM_GBPS, 4),
+                                         "traffic": _traffic("prologue_kernel",
+                                                             _src_hash("prologue.hip", "device_common.hpp")),
+                                         "avg_launch_us": round(g_kernel_ms * 1e3, 2)}}
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline()
     print(json.dumps(line), flush=True)
