@@ -23,3 +23,14 @@ from .prologue_oracle import (  # noqa: F401
     rms_norm,
     short_conv,
 )
+from .mx_oracle import (  # noqa: F401
+    E4M3_MAX,
+    MX_BLOCK,
+    e4m3_decode,
+    e4m3_encode,
+    e4m3_round,
+    e8m0_value,
+    mx_dequantize,
+    mx_quantize,
+    mx_round,
+)
