@@ -214,6 +214,65 @@ int rel_attn_decode_paged(const void* q, const void* k_pages, const void* v_page
                           int num_splits, void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * MXFP8 K/V (page "SGLang and Miles Add Day-0 Support for Inkling", section
+ * "Relative Logits Optimization", paragraph "MXFP8 Support"): K and V stored
+ * as OCP MX blocks -- E4M3 codes (one byte per value) with one E8M0 scale
+ * byte per 32 values of D (four per 128-wide row), value = E4M3(code) *
+ * 2^(scale - 127).  Quantisation of a block: shared exponent =
+ * floor(log2(max |x|)) - 8, clamped to [-127, 127] (0 for an all-zero
+ * block); each element x * 2^-shared rounded to nearest E4M3, ties to even,
+ * magnitudes beyond 448 clamped to 448.
+ *
+ * rel_mx_quantize: rows of D = 128 values (dtype) -> codes [n_rows, 128]
+ * (uint8) and scales [n_rows, 4] (uint8).  x 16-byte aligned; the outputs
+ * must not alias x.  n_rows == 0 is a no-op.
+ */
+int rel_mx_quantize(const void* x, void* codes, void* scales, int dtype,
+                    long long n_rows, int D, void* stream);
+
+/*
+ * rel_attn_prologue_mx: rel_attn_prologue writing MXFP8 caches: the k and v
+ * rows are quantised (as rel_mx_quantize would quantise their fp32 values)
+ * into k_codes / v_codes [.., Hkv, D] (uint8, the layout of the dtype caches
+ * with one byte per value) and k_scales / v_scales [.., Hkv, D / 32]
+ * (uint8), contiguous ([B, cache_len, ...]) or paged ([num_pages,
+ * page_size, ...]).  q, k, v, weights, state and q_out are bf16.  The four
+ * cache buffers must be distinct.  Everything else as rel_attn_prologue.
+ */
+int rel_attn_prologue_mx(const void* q_in, const void* k_in, const void* v_in,
+                         const void* conv_k, const void* conv_v,
+                         const void* q_norm_w, const void* k_norm_w, float eps,
+                         const void* state_in, void* state_out, void* q_out,
+                         void* k_codes, void* k_scales, void* v_codes, void* v_scales,
+                         int B, int total_q, const int* q_start, const int* kv_len,
+                         int cache_len, const int* block_table, int max_pages,
+                         int num_pages, int page_size, int Hq, int Hkv, int D,
+                         int conv_width, void* stream);
+
+/*
+ * rel_attn_decode_mx: split-KV decode over MXFP8 caches.  The score product
+ * runs on MXFP8 operands: q is quantised like a K row (per (sequence, head)
+ * row, blocks of 32 along D) and Q.K^T is taken by the gfx950 MX-scaled
+ * fp8 MFMA with fp32 accumulation; V is dequantised to bf16 (exactly) for
+ * the bf16 P.V product.  q, r, P_cols, out: bf16; lse float32 or NULL.
+ *   Contiguous (block_table == NULL, kv_len == NULL): codes [B, L, Hkv, D],
+ *     scales [B, L, Hkv, D / 32]; the query at position L-1, as
+ *     rel_attn_decode.
+ *   Paged (block_table and kv_len given): codes [num_pages, page_size, Hkv,
+ *     D], scales [num_pages, page_size, Hkv, D / 32]; per-sequence lengths
+ *     kv_len[b] <= L, as rel_attn_decode_paged (page_size a multiple of 32).
+ * Workspace: as rel_attn_decode, sized by rel_attn_decode_plan(B, L, ...).
+ */
+int rel_attn_decode_mx(const void* q, const void* k_codes, const void* k_scales,
+                       const void* v_codes, const void* v_scales, const void* r,
+                       const void* P_cols, void* out, float* lse, int B, int L,
+                       const int* kv_len, const int* block_table, int max_pages,
+                       int num_pages, int page_size, int Hq, int Hkv, int D, int d_r,
+                       float alpha, int rel_extent, int window, int log_scale,
+                       int num_splits, void* workspace, size_t workspace_bytes,
+                       void* stream);
+
+/*
  * Dense relative logits (eq. for rel_logits in the same section):
  *   out[t, h, d] = s * sum_c r[t, h, c] * P_cols[d, c]   for every d < rel_extent
  *   r [n_tok, H, d_r] (dtype)   P_cols [E, d_r] (dtype)   out [n_tok, H, E] float32

@@ -36,7 +36,8 @@ def _declared_functions():
 def test_header_declares_the_boundary():
     names = _declared_functions()
     for n in ("rel_attn_prefill", "rel_attn_extend", "rel_attn_decode", "rel_attn_decode_paged",
-              "rel_attn_decode_plan", "rel_logits", "rel_attn_prologue",
+              "rel_attn_decode_plan", "rel_logits", "rel_attn_prologue", "rel_attn_prologue_mx",
+              "rel_attn_decode_mx", "rel_mx_quantize",
               "rel_attn_last_error", "rel_attn_version", "rel_attn_scale_factor"):
         assert n in names
 
@@ -314,3 +315,68 @@ def test_prologue_empty_is_a_noop(lib):
                  conv_v=None, qw=None, kw_=None, q_start=None, kv_len=None)
     assert _prologue(lib, B=0, **nulls) == RA_OK
     assert _prologue(lib, total_q=0, **nulls) == RA_OK
+
+
+def _decode_mx(lib, **kw):
+    a = dict(q=FAKE, kc=FAKE + 0x100, ks=FAKE + 0x200, vc=FAKE + 0x300, vs=FAKE + 0x400, r=FAKE + 0x500,
+             P=FAKE + 0x600, out=FAKE + 0x700, lse=None, B=2, L=100, kv_len=None, bt=None, max_pages=0, num_pages=0,
+             page_size=0, Hq=16, Hkv=2, D=128, d_r=64, alpha=0.1, E=32, W=0, ls=0, ns=0, ws=FAKE + 0x1000,
+             ws_bytes=1 << 30)
+    a.update(kw)
+    return lib.rel_attn_decode_mx(a["q"], a["kc"], a["ks"], a["vc"], a["vs"], a["r"], a["P"], a["out"], a["lse"],
+                                  a["B"], a["L"], a["kv_len"], a["bt"], a["max_pages"], a["num_pages"],
+                                  a["page_size"], a["Hq"], a["Hkv"], a["D"], a["d_r"], a["alpha"], a["E"], a["W"],
+                                  a["ls"], a["ns"], a["ws"], a["ws_bytes"], None)
+
+
+@pytest.mark.parametrize("kw,code,frag", [
+    (dict(ks=None), RA_ERR_INVALID_ARG, "scales"),
+    (dict(kv_len=FAKE + 0x800), RA_ERR_INVALID_ARG, "paged"),
+    (dict(bt=FAKE + 0x800), RA_ERR_INVALID_ARG, "kv_len"),
+    (dict(bt=FAKE + 0x800, kv_len=FAKE + 0x900, page_size=48, max_pages=4, num_pages=8), RA_ERR_UNSUPPORTED, "page_size"),
+    (dict(L=0), RA_ERR_INVALID_ARG, "L = 0"),
+    (dict(D=64), RA_ERR_UNSUPPORTED, "head dim"),
+    (dict(out=FAKE + 0x300), RA_ERR_INVALID_ARG, "alias"),
+    (dict(ws=None), RA_ERR_WORKSPACE, "workspace"),
+    (dict(ws_bytes=16), RA_ERR_WORKSPACE, "smaller"),
+    (dict(kc=FAKE + 8), RA_ERR_INVALID_ARG, "16-byte"),
+])
+def test_decode_mx_rejects_bad_arguments(lib, kw, code, frag):
+    assert _decode_mx(lib, **kw) == code
+    assert frag in lib.rel_attn_last_error().decode()
+
+
+def test_mx_quantize_rejects_and_noop(lib):
+    assert lib.rel_mx_quantize(FAKE, FAKE + 0x100, FAKE + 0x200, RA_BF16, 0, 128, None) == RA_OK
+    assert lib.rel_mx_quantize(FAKE, FAKE + 0x100, FAKE + 0x200, RA_BF16, 10, 64, None) == RA_ERR_UNSUPPORTED
+    assert lib.rel_mx_quantize(FAKE, FAKE, FAKE + 0x200, RA_BF16, 10, 128, None) == RA_ERR_INVALID_ARG
+    assert lib.rel_mx_quantize(FAKE, FAKE + 0x100, None, RA_BF16, 10, 128, None) == RA_ERR_INVALID_ARG
+    assert lib.rel_mx_quantize(FAKE, FAKE + 0x100, FAKE + 0x200, 7, 10, 128, None) == RA_ERR_INVALID_ARG
+    assert lib.rel_mx_quantize(FAKE, FAKE + 0x100, FAKE + 0x200, RA_BF16, -1, 128, None) == RA_ERR_INVALID_ARG
+
+
+def _prologue_mx(lib, **kw):
+    a = dict(q_in=FAKE, k_in=FAKE + 0x100, v_in=FAKE + 0x200, conv_k=FAKE + 0x300, conv_v=FAKE + 0x400,
+             qw=FAKE + 0x500, kw_=FAKE + 0x600, eps=1e-6, st_in=None, st_out=None, q_out=FAKE + 0x700,
+             kc=FAKE + 0x800, ks=FAKE + 0x900, vc=FAKE + 0xa00, vs=FAKE + 0xb00, B=2, total_q=10,
+             q_start=FAKE + 0xc00, kv_len=FAKE + 0xd00, cache_len=64, block_table=None, max_pages=0, num_pages=0,
+             page_size=0, Hq=8, Hkv=1, D=128, W=4)
+    a.update(kw)
+    return lib.rel_attn_prologue_mx(a["q_in"], a["k_in"], a["v_in"], a["conv_k"], a["conv_v"], a["qw"], a["kw_"],
+                                    a["eps"], a["st_in"], a["st_out"], a["q_out"], a["kc"], a["ks"], a["vc"], a["vs"],
+                                    a["B"], a["total_q"], a["q_start"], a["kv_len"], a["cache_len"],
+                                    a["block_table"], a["max_pages"], a["num_pages"], a["page_size"], a["Hq"],
+                                    a["Hkv"], a["D"], a["W"], None)
+
+
+@pytest.mark.parametrize("kw,code,frag", [
+    (dict(ks=None), RA_ERR_INVALID_ARG, "scales"),
+    (dict(vs=FAKE + 0x900), RA_ERR_INVALID_ARG, "overlap"),
+    (dict(ks=FAKE + 0x800), RA_ERR_INVALID_ARG, "overlap"),
+    (dict(vs=FAKE), RA_ERR_INVALID_ARG, "alias"),
+    (dict(W=5), RA_ERR_UNSUPPORTED, "conv_width"),
+    (dict(cache_len=0), RA_ERR_INVALID_ARG, "cache_len"),
+])
+def test_prologue_mx_rejects_bad_arguments(lib, kw, code, frag):
+    assert _prologue_mx(lib, **kw) == code
+    assert frag in lib.rel_attn_last_error().decode()

@@ -1,7 +1,8 @@
 """MI355X (gfx950) relative-attention forward: HIP kernels behind a C ABI.
 
-``prefill``, ``extend``, ``decode``, ``decode_paged``, ``decode_plan``,
-``prologue`` and ``rel_logits`` call the compiled library ``librelattn.so``
+``prefill``, ``extend``, ``decode``, ``decode_paged``, ``decode_mx``,
+``decode_plan``, ``prologue``, ``prologue_mx``, ``mx_quantize`` and
+``rel_logits`` call the compiled library ``librelattn.so``
 (built in-tree by ``__graft_entry__.build()`` or
 ``python -m transformer_attention_query_amd.build``).  There is no fallback:
 if the library is missing the calls raise.
@@ -10,13 +11,16 @@ if the library is missing the calls raise.
 from .binding import (  # noqa: F401
     RelAttnError,
     decode,
+    decode_mx,
     decode_paged,
     decode_plan,
     extend,
     library_path,
     load_library,
+    mx_quantize,
     prefill,
     prologue,
+    prologue_mx,
     rel_logits,
     scale_factor,
     version,

@@ -61,6 +61,14 @@ def _declare(lib):
     lib.rel_attn_prologue.argtypes = [vp, vp, vp, vp, vp, vp, vp, f32, vp, vp, vp, vp, vp, i32, i32, i32, vp, vp,
                                       i32, vp, i32, i32, i32, i32, i32, i32, i32, vp]
     lib.rel_attn_prologue.restype = i32
+    lib.rel_attn_prologue_mx.argtypes = [vp, vp, vp, vp, vp, vp, vp, f32, vp, vp, vp, vp, vp, vp, vp, i32, i32, vp,
+                                         vp, i32, vp, i32, i32, i32, i32, i32, i32, i32, vp]
+    lib.rel_attn_prologue_mx.restype = i32
+    lib.rel_attn_decode_mx.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i32, i32, vp, vp, i32, i32, i32, i32, i32,
+                                       i32, i32, f32, i32, i32, i32, i32, vp, sz, vp]
+    lib.rel_attn_decode_mx.restype = i32
+    lib.rel_mx_quantize.argtypes = [vp, vp, vp, i32, i64, i32, vp]
+    lib.rel_mx_quantize.restype = i32
     lib.rel_logits.argtypes = [vp, vp, vp, i32, i64, i32, i32, i32, i32, i64, vp]
     lib.rel_logits.restype = i32
     lib.rel_attn_last_error.argtypes = []
@@ -437,4 +445,117 @@ def prologue(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, conv_k: torch.Te
                                  _ptr(k_cache), _ptr(v_cache), _DTYPE_CODE[dt], B, total_q, _ptr(q_start),
                                  _ptr(kv_len), cache_len, _ptr(block_table), max_pages, num_pages, page_size,
                                  Hq, Hkv, D, W, _stream(dev)))
+    return q_out
+
+
+def mx_quantize(x: torch.Tensor) -> Tuple[torch.Tensor, torch.Tensor]:
+    """MXFP8 of rows of 128 values (rel_mx_quantize): returns (codes uint8
+    [..., 128], scales uint8 [..., 4])."""
+    lib = load_library()
+    dt = x.dtype
+    if dt not in _DTYPE_CODE:
+        raise TypeError(f"unsupported dtype {dt}")
+    if not x.is_contiguous() or x.shape[-1] != 128:
+        raise ValueError("x must be contiguous with a last dimension of 128")
+    n = x.numel() // 128
+    codes = torch.empty(x.shape, dtype=torch.uint8, device=x.device)
+    scales = torch.empty(x.shape[:-1] + (4,), dtype=torch.uint8, device=x.device)
+    _check(lib.rel_mx_quantize(_ptr(x), _ptr(codes), _ptr(scales), _DTYPE_CODE[dt], n, 128, _stream(x.device)))
+    return codes, scales
+
+
+def decode_mx(q: torch.Tensor, k_codes: torch.Tensor, k_scales: torch.Tensor, v_codes: torch.Tensor,
+              v_scales: torch.Tensor, r: Optional[torch.Tensor], P_cols: Optional[torch.Tensor], alpha: float,
+              rel_extent: int, window: int = 0, log_scale: bool = False, L: Optional[int] = None,
+              kv_len: Optional[torch.Tensor] = None, block_table: Optional[torch.Tensor] = None,
+              num_splits: int = 0, return_lse: bool = True, workspace: Optional[torch.Tensor] = None
+              ) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+    """Split-KV decode over MXFP8 caches (rel_attn_decode_mx).
+
+    q [B,Hq,D] bf16.  Contiguous: codes [B,L,Hkv,D], scales [B,L,Hkv,D/32]
+    (uint8).  Paged: codes [num_pages,page_size,Hkv,D], scales
+    [num_pages,page_size,Hkv,D/32], ``block_table`` [B,max_pages] and
+    ``kv_len`` [B] (int32, device), ``L`` the bound on kv_len.  Returns out
+    [B,Hq,D] bf16 and lse [B,Hq] fp32.
+    """
+    lib = load_library()
+    dev = q.device
+    _need(q, "q", torch.bfloat16, dev, 3)
+    for name, t in (("k_codes", k_codes), ("v_codes", v_codes), ("k_scales", k_scales), ("v_scales", v_scales)):
+        _need(t, name, torch.uint8, dev, 4)
+    B, Hq, D = q.shape
+    Hkv = k_codes.shape[2]
+    paged = block_table is not None
+    if paged:
+        _need(block_table, "block_table", torch.int32, dev, 2)
+        _need(kv_len, "kv_len", torch.int32, dev, 1)
+        if L is None:
+            raise ValueError("paged caches need L, the bound on kv_len")
+        max_pages, num_pages, page_size = block_table.shape[1], k_codes.shape[0], k_codes.shape[1]
+    else:
+        if kv_len is not None:
+            raise ValueError("kv_len is for paged caches")
+        L = k_codes.shape[1]
+        max_pages = num_pages = page_size = 0
+    if v_codes.shape != k_codes.shape or k_scales.shape != k_codes.shape[:3] + (D // 32,) or \
+            v_scales.shape != k_scales.shape:
+        raise ValueError("code and scale shapes do not match")
+    d_r = 0
+    if rel_extent > 0:
+        _need(r, "r", torch.bfloat16, dev, 3)
+        _need(P_cols, "P_cols", torch.bfloat16, dev, 2)
+        d_r = r.shape[2]
+    else:
+        r = None
+        P_cols = None
+    ns, ws_bytes = decode_plan(B, L, Hq, Hkv, D, num_splits, window, rel_extent)
+    if workspace is None:
+        workspace = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
+    out = torch.empty_like(q)
+    lse = torch.empty(B, Hq, dtype=torch.float32, device=dev) if return_lse else None
+    _check(lib.rel_attn_decode_mx(_ptr(q), _ptr(k_codes), _ptr(k_scales), _ptr(v_codes), _ptr(v_scales), _ptr(r),
+                                  _ptr(P_cols), _ptr(out), _ptr(lse), B, int(L), _ptr(kv_len), _ptr(block_table),
+                                  max_pages, num_pages, page_size, Hq, Hkv, D, d_r, float(alpha), int(rel_extent),
+                                  int(window), 1 if log_scale else 0, ns, _ptr(workspace), workspace.numel(),
+                                  _stream(dev)))
+    return out, lse
+
+
+def prologue_mx(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, conv_k: torch.Tensor, conv_v: torch.Tensor,
+                q_norm_w: torch.Tensor, k_norm_w: torch.Tensor, eps: float, q_start: torch.Tensor,
+                kv_len: torch.Tensor, k_codes: torch.Tensor, k_scales: torch.Tensor, v_codes: torch.Tensor,
+                v_scales: torch.Tensor, block_table: Optional[torch.Tensor] = None,
+                state_in: Optional[torch.Tensor] = None, state_out: Optional[torch.Tensor] = None,
+                q_out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """The attention prologue writing MXFP8 caches (rel_attn_prologue_mx); bf16
+    inputs; codes [..,Hkv,128] and scales [..,Hkv,4] uint8, written in place."""
+    lib = load_library()
+    dev = q.device
+    dt = torch.bfloat16
+    for name, t, nd in (("q", q, 3), ("k", k, 3), ("v", v, 3), ("conv_k", conv_k, 2), ("conv_v", conv_v, 2),
+                        ("q_norm_w", q_norm_w, 1), ("k_norm_w", k_norm_w, 1)):
+        _need(t, name, dt, dev, nd)
+    for name, t in (("k_codes", k_codes), ("v_codes", v_codes), ("k_scales", k_scales), ("v_scales", v_scales)):
+        _need(t, name, torch.uint8, dev, 4)
+    _need(q_start, "q_start", torch.int32, dev, 1)
+    _need(kv_len, "kv_len", torch.int32, dev, 1)
+    total_q, Hq, D = q.shape
+    Hkv = k.shape[1]
+    B = kv_len.shape[0]
+    W = conv_k.shape[1]
+    if block_table is None:
+        cache_len, max_pages, num_pages, page_size = k_codes.shape[1], 0, 0, 0
+    else:
+        _need(block_table, "block_table", torch.int32, dev, 2)
+        cache_len, max_pages, num_pages, page_size = 0, block_table.shape[1], k_codes.shape[0], k_codes.shape[1]
+    for name, st in (("state_in", state_in), ("state_out", state_out)):
+        if st is not None:
+            _need(st, name, dt, dev, 4)
+    if q_out is None:
+        q_out = torch.empty_like(q)
+    _check(lib.rel_attn_prologue_mx(_ptr(q), _ptr(k), _ptr(v), _ptr(conv_k), _ptr(conv_v), _ptr(q_norm_w),
+                                    _ptr(k_norm_w), float(eps), _ptr(state_in), _ptr(state_out), _ptr(q_out),
+                                    _ptr(k_codes), _ptr(k_scales), _ptr(v_codes), _ptr(v_scales), B, total_q,
+                                    _ptr(q_start), _ptr(kv_len), cache_len, _ptr(block_table), max_pages, num_pages,
+                                    page_size, Hq, Hkv, D, W, _stream(dev)))
     return q_out

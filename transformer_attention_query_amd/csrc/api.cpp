@@ -146,11 +146,18 @@ int rel_attn_extend(const void* q, const void* k, const void* v, const void* r, 
   return ok();
 }
 
-int rel_attn_prologue(const void* q_in, const void* k_in, const void* v_in, const void* conv_k, const void* conv_v,
-                      const void* q_norm_w, const void* k_norm_w, float eps, const void* state_in, void* state_out,
-                      void* q_out, void* k_cache, void* v_cache, int dtype, int B, int total_q, const int* q_start,
-                      const int* kv_len, int cache_len, const int* block_table, int max_pages, int num_pages,
-                      int page_size, int Hq, int Hkv, int D, int conv_width, void* stream) {
+}  // extern "C"
+
+namespace {
+
+// The prologue with caches in the input dtype (k_scale == v_scale == NULL) or
+// in MXFP8 (E4M3 codes in k_cache / v_cache and their E8M0 scales).
+int prologue_impl(const void* q_in, const void* k_in, const void* v_in, const void* conv_k, const void* conv_v,
+                  const void* q_norm_w, const void* k_norm_w, float eps, const void* state_in, void* state_out,
+                  void* q_out, void* k_cache, void* v_cache, bool mx, void* k_scale, void* v_scale, int dtype,
+                  int B, int total_q, const int* q_start, const int* kv_len, int cache_len, const int* block_table,
+                  int max_pages, int num_pages, int page_size, int Hq, int Hkv, int D, int conv_width,
+                  void* stream) {
   if (dtype != RA_BF16 && dtype != RA_F32) return fail(RA_ERR_INVALID_ARG, "dtype %d is not RA_BF16 or RA_F32", dtype);
   if (B < 0) return fail(RA_ERR_INVALID_ARG, "B = %d < 0", B);
   if (total_q < 0) return fail(RA_ERR_INVALID_ARG, "total_q = %d < 0", total_q);
@@ -187,6 +194,15 @@ int rel_attn_prologue(const void* q_in, const void* k_in, const void* v_in, cons
     for (const void* i : ins)
       if (o != nullptr && o == i) return fail(RA_ERR_INVALID_ARG, "an output buffer aliases an input");
   if (rows && (q_out == k_in || q_out == v_in)) return fail(RA_ERR_INVALID_ARG, "q_out aliases k_in or v_in");
+  if (mx && rows) {
+    if (k_scale == nullptr || v_scale == nullptr) return fail(RA_ERR_INVALID_ARG, "k_scales and v_scales must not be NULL");
+    const void* mouts[4] = {k_cache, v_cache, k_scale, v_scale};
+    for (int i = 0; i < 4; ++i)
+      for (int j = i + 1; j < 4; ++j)
+        if (mouts[i] == mouts[j]) return fail(RA_ERR_INVALID_ARG, "the MXFP8 code and scale buffers overlap");
+    for (const void* i : ins)
+      if (i == k_scale || i == v_scale) return fail(RA_ERR_INVALID_ARG, "an output buffer aliases an input");
+  }
   if (!rows) {
     // only the state copies run; the cache geometry is not used
   } else if (block_table == nullptr) {
@@ -211,9 +227,36 @@ int rel_attn_prologue(const void* q_in, const void* k_in, const void* v_in, cons
   a.max_pages = block_table == nullptr ? 0 : max_pages;
   a.num_pages = block_table == nullptr ? 0 : num_pages;
   a.page_size = block_table == nullptr ? 1 : page_size;
-  hipError_t e = relattn::launch_prologue(dtype, a, static_cast<hipStream_t>(stream));
+  a.k_scale = k_scale; a.v_scale = v_scale;
+  hipError_t e = mx ? relattn::launch_prologue_mx(a, static_cast<hipStream_t>(stream))
+                    : relattn::launch_prologue(dtype, a, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return fail(RA_ERR_HIP, "prologue launch failed: %s", hipGetErrorString(e));
   return ok();
+}
+
+}  // namespace
+
+extern "C" {
+
+int rel_attn_prologue(const void* q_in, const void* k_in, const void* v_in, const void* conv_k, const void* conv_v,
+                      const void* q_norm_w, const void* k_norm_w, float eps, const void* state_in, void* state_out,
+                      void* q_out, void* k_cache, void* v_cache, int dtype, int B, int total_q, const int* q_start,
+                      const int* kv_len, int cache_len, const int* block_table, int max_pages, int num_pages,
+                      int page_size, int Hq, int Hkv, int D, int conv_width, void* stream) {
+  return prologue_impl(q_in, k_in, v_in, conv_k, conv_v, q_norm_w, k_norm_w, eps, state_in, state_out, q_out,
+                       k_cache, v_cache, false, nullptr, nullptr, dtype, B, total_q, q_start, kv_len, cache_len,
+                       block_table, max_pages, num_pages, page_size, Hq, Hkv, D, conv_width, stream);
+}
+
+int rel_attn_prologue_mx(const void* q_in, const void* k_in, const void* v_in, const void* conv_k,
+                         const void* conv_v, const void* q_norm_w, const void* k_norm_w, float eps,
+                         const void* state_in, void* state_out, void* q_out, void* k_codes, void* k_scales,
+                         void* v_codes, void* v_scales, int B, int total_q, const int* q_start, const int* kv_len,
+                         int cache_len, const int* block_table, int max_pages, int num_pages, int page_size, int Hq,
+                         int Hkv, int D, int conv_width, void* stream) {
+  return prologue_impl(q_in, k_in, v_in, conv_k, conv_v, q_norm_w, k_norm_w, eps, state_in, state_out, q_out,
+                       k_codes, v_codes, true, k_scales, v_scales, RA_BF16, B, total_q, q_start, kv_len, cache_len,
+                       block_table, max_pages, num_pages, page_size, Hq, Hkv, D, conv_width, stream);
 }
 
 int rel_attn_decode_plan(int B, int L, int Hq, int Hkv, int D, int num_splits_req, int window, int rel_extent,
@@ -328,6 +371,88 @@ int rel_attn_decode_paged(const void* q, const void* k_pages, const void* v_page
   a.log_scale = log_scale; a.alpha = alpha;
   hipError_t e = relattn::launch_decode_paged(dtype, a, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return fail(RA_ERR_HIP, "decode launch failed: %s", hipGetErrorString(e));
+  return ok();
+}
+
+int rel_attn_decode_mx(const void* q, const void* k_codes, const void* k_scales, const void* v_codes,
+                       const void* v_scales, const void* r, const void* P_cols, void* out, float* lse, int B, int L,
+                       const int* kv_len, const int* block_table, int max_pages, int num_pages, int page_size, int Hq,
+                       int Hkv, int D, int d_r, float alpha, int rel_extent, int window, int log_scale,
+                       int num_splits, void* workspace, size_t workspace_bytes, void* stream) {
+  int rc = check_common(RA_BF16, B, L, Hq, Hkv, D, d_r, alpha, rel_extent, window, log_scale, "L");
+  if (rc) return rc;
+  if (L == 0) return fail(RA_ERR_INVALID_ARG, "L = 0: a cache holds at least the query's own token");
+  if ((rc = check_ptr(q, "q", true)) || (rc = check_ptr(k_codes, "k_codes", true)) ||
+      (rc = check_ptr(v_codes, "v_codes", true)) || (rc = check_ptr(out, "out", true)) ||
+      (rc = check_ptr(lse, "lse", false)) || (rc = check_ptr(r, "r", rel_extent > 0)) ||
+      (rc = check_ptr(P_cols, "P_cols", rel_extent > 0)))
+    return rc;
+  if (k_scales == nullptr || v_scales == nullptr) return fail(RA_ERR_INVALID_ARG, "k_scales and v_scales must not be NULL");
+  const bool paged = block_table != nullptr;
+  if (paged) {
+    if (kv_len == nullptr) return fail(RA_ERR_INVALID_ARG, "a paged cache needs kv_len");
+    if ((reinterpret_cast<uintptr_t>(kv_len) | reinterpret_cast<uintptr_t>(block_table)) & 3u)
+      return fail(RA_ERR_INVALID_ARG, "kv_len and block_table must be 4-byte aligned");
+    if (page_size <= 0 || page_size % 32 != 0)
+      return fail(RA_ERR_UNSUPPORTED, "page_size = %d: supported values are positive multiples of 32", page_size);
+    if (max_pages <= 0 || num_pages <= 0)
+      return fail(RA_ERR_INVALID_ARG, "max_pages = %d and num_pages = %d must be positive", max_pages, num_pages);
+    if ((long long)max_pages * page_size > 0x7fffffffLL)
+      return fail(RA_ERR_UNSUPPORTED, "max_pages * page_size too large");
+  } else if (kv_len != nullptr) {
+    return fail(RA_ERR_INVALID_ARG, "kv_len is for paged caches; a contiguous cache holds L keys per sequence");
+  }
+  const void* ins[7] = {q, k_codes, k_scales, v_codes, v_scales, r, P_cols};
+  for (const void* i : ins)
+    if (i != nullptr && (i == out || i == lse)) return fail(RA_ERR_INVALID_ARG, "out or lse aliases an input");
+  if (num_splits < 0) return fail(RA_ERR_INVALID_ARG, "num_splits = %d < 0", num_splits);
+  relattn::DecodePlan pl = relattn::plan_decode(B, L, Hq, Hkv, num_splits, window, rel_extent);
+  if (B == 0) return ok();
+  if (workspace == nullptr) return fail(RA_ERR_WORKSPACE, "workspace is NULL (need %zu bytes)", pl.ws_bytes);
+  if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0)
+    return fail(RA_ERR_WORKSPACE, "workspace is not 256-byte aligned");
+  if (workspace_bytes < pl.ws_bytes)
+    return fail(RA_ERR_WORKSPACE, "workspace of %zu bytes is smaller than the %zu the plan needs", workspace_bytes,
+                pl.ws_bytes);
+  if (!paged && (long long)B * L > 0x7fffffffLL) return fail(RA_ERR_UNSUPPORTED, "B * L = %lld too large", (long long)B * L);
+
+  relattn::DecodeArgs a;
+  a.q = q; a.k = k_codes; a.v = v_codes; a.r = r; a.pc = P_cols; a.out = out; a.lse = lse;
+  a.k_scale = k_scales; a.v_scale = v_scales;
+  a.ws = static_cast<float*>(workspace);
+  a.B = B; a.L = L; a.Hq = Hq; a.Hkv = Hkv; a.d_r = rel_extent > 0 ? d_r : 16; a.E = rel_extent; a.W = window;
+  const double s = paged ? 1.0 : scale_of(log_scale, L);  // paged: s per sequence on the device
+  a.c1 = (float)(s * (double)alpha * 1.4426950408889634);
+  a.c2 = (float)(s * 1.4426950408889634);
+  a.n_split = pl.n_split;
+  a.chunk = pl.chunk;
+  a.kv_lo = pl.kv_lo;
+  a.n_hg = pl.n_hg;
+  a.rl_base = pl.rl_base;
+  a.rl_stride = pl.rl_stride;
+  a.rl = reinterpret_cast<const float*>(static_cast<char*>(workspace) + pl.ws_partial_bytes);
+  if (paged) {
+    a.kv_len = kv_len; a.btab = block_table;
+    a.max_pages = max_pages; a.num_pages = num_pages; a.page_size = page_size;
+    a.log_scale = log_scale; a.alpha = alpha;
+  }
+  hipError_t e = relattn::launch_decode_mx(a, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(RA_ERR_HIP, "decode launch failed: %s", hipGetErrorString(e));
+  return ok();
+}
+
+int rel_mx_quantize(const void* x, void* codes, void* scales, int dtype, long long n_rows, int D, void* stream) {
+  if (dtype != RA_BF16 && dtype != RA_F32) return fail(RA_ERR_INVALID_ARG, "dtype %d is not RA_BF16 or RA_F32", dtype);
+  if (n_rows < 0) return fail(RA_ERR_INVALID_ARG, "n_rows = %lld < 0", n_rows);
+  if (D != relattn::kHeadDim) return fail(RA_ERR_UNSUPPORTED, "row length D = %d: only 128 is supported", D);
+  if (n_rows == 0) return ok();
+  int rc;
+  if ((rc = check_ptr(x, "x", true)) || (rc = check_ptr(codes, "codes", true))) return rc;
+  if (scales == nullptr) return fail(RA_ERR_INVALID_ARG, "scales is NULL");
+  if (codes == x || scales == x) return fail(RA_ERR_INVALID_ARG, "an output aliases x");
+  if (n_rows > 0x7fffffffLL * 16) return fail(RA_ERR_UNSUPPORTED, "n_rows = %lld too large", n_rows);
+  hipError_t e = relattn::launch_mx_quantize(dtype, x, codes, scales, n_rows, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(RA_ERR_HIP, "quantize launch failed: %s", hipGetErrorString(e));
   return ok();
 }
 

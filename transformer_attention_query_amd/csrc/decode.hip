@@ -29,6 +29,7 @@
 //      (ds_read_b64_tr_b16); fp32 tiles are stored transposed.
 //   3. decode_merge_kernel: log-sum-exp merge of the split partials.
 #include "device_common.hpp"
+#include "mx_common.hpp"
 #include "relattn_internal.hpp"
 
 namespace relattn {
@@ -112,6 +113,24 @@ struct Chunk {
   f32x4 rl[2];                  // bias of keys 16*blk + 4*g .. +3 (log2 units)
 };
 
+// The same step from MXFP8 caches: E4M3 codes with one E8M0 scale per 32
+// values of D.  The score MFMA (v_mfma_scale_f32_16x16x128_f8f6f4) takes all
+// of D at once: lane (g, c) supplies bytes d = 16g .. 16g+15 and
+// 64+16g .. 64+16g+15 of its key and the scale of d-block g (the operand
+// layout, checked on the device: lane 16*blk + r carries the scale of row r,
+// d-block blk).  V codes are dequantised to bf16 before the LDS tile.
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+struct ChunkMX {
+  i32x8 k[2];        // key 16*blk + c: d 16g .. 16g+15, then 64+16g .. 64+16g+15
+  unsigned ks[2];    // E8M0 scale of that key's d-block g
+  uint2 v[8];        // key 8g + i: codes of d 8c .. 8c+7
+  unsigned vs[8];    // E8M0 scale of key 8g + i, d-block c/4
+  f32x4 rl[2];
+};
+
+template <bool C, typename A, typename B> struct Pick { typedef A type; };
+template <typename A, typename B> struct Pick<false, A, B> { typedef B type; };
+
 // Per-workgroup reduction of the four waves' partial states (reuses the V tiles' LDS).
 struct DecReduce {
   float m[kDecWaves][16];
@@ -123,8 +142,12 @@ struct DecReduce {
 // kv_len[b] (at most L), pages of page_size keys (a multiple of 32) through a
 // block table, steps aligned to 32 keys so each lies in one page, and bias
 // rows in distance order scaled by log2(e) only (s applied here per sequence).
-template <typename T, bool PAGED>
+// MX: MXFP8 caches (rel_attn_decode_mx); q is quantised to MXFP8 the same way
+// for the score product, V is dequantised to bf16 for PV.
+template <typename T, bool PAGED, bool MX = false>
 __global__ __launch_bounds__(kDecWaves * 64, sizeof(T) == 2 ? 2 : 1) void decode_split_kernel(DecodeArgs p) {
+  static_assert(!MX || sizeof(T) == 2, "MXFP8 caches come with bf16 queries");
+  using CH = typename Pick<MX, ChunkMX, Chunk<T>>::type;
   using VS = DecV<T>;
   constexpr int D = kHeadDim;
   constexpr size_t SMEM = kDecWaves * VS::BYTES > sizeof(DecReduce) ? kDecWaves * VS::BYTES : sizeof(DecReduce);
@@ -175,9 +198,47 @@ __global__ __launch_bounds__(kDecWaves * 64, sizeof(T) == 2 ? 2 : 1) void decode
   const T* vg = static_cast<const T*>(p.v);
   // query (B operand of S^T = K Q^T): k-slot 8g+t of step st is d = 32*st + 8*g + t
   v8_t<T> qreg[D / 32];
+  i32x8 qx;          // MX: the query in MXFP8, bytes as the scaled MFMA takes them
+  unsigned qs = 127; // MX: E8M0 scale of d-block g of head c
+  if constexpr (!MX) {
 #pragma unroll
-  for (int st = 0; st < D / 32; ++st)
-    qreg[st] = ld8_or_zero<T>(qg + (size_t(b) * Hq + h) * D + 32 * st + 8 * g, hvalid);
+    for (int st = 0; st < D / 32; ++st)
+      qreg[st] = ld8_or_zero<T>(qg + (size_t(b) * Hq + h) * D + 32 * st + 8 * g, hvalid);
+  } else {
+    // every lane of head c reads the whole row, finds the four block maxima
+    // and encodes its own 32 values (d 16g .. +15 and 64+16g .. +15)
+    float qv[D];
+#pragma unroll
+    for (int v8 = 0; v8 < D / 8; ++v8) {
+      const v8_t<T> x = ld8_or_zero<T>(qg + (size_t(b) * Hq + h) * D + 8 * v8, hvalid);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) qv[8 * v8 + e] = float(x[e]);
+    }
+    int sh[D / kMxBlock];
+#pragma unroll
+    for (int blk = 0; blk < D / kMxBlock; ++blk) {
+      float amax = 0.0f;
+#pragma unroll
+      for (int e = 0; e < kMxBlock; ++e) amax = fmaxf(amax, fabsf(qv[kMxBlock * blk + e]));
+      sh[blk] = mx_shared_exp(amax);
+    }
+    // g selects among compile-time offsets with a branch-free pick
+    int shg = sh[0], lo_sh = sh[0], hi_sh = sh[2];
+    if (g == 1) { shg = sh[1]; }
+    if (g == 2) { shg = sh[2]; lo_sh = sh[1]; hi_sh = sh[3]; }
+    if (g == 3) { shg = sh[3]; lo_sh = sh[1]; hi_sh = sh[3]; }
+    qs = unsigned(shg + 127);
+#pragma unroll
+    for (int gg = 0; gg < 4; ++gg) {
+      if (gg != g) continue;
+#pragma unroll
+      for (int w4 = 0; w4 < 4; ++w4) {
+        const int d0 = 16 * gg + 4 * w4, d1 = 64 + 16 * gg + 4 * w4;
+        qx[w4] = int(e4m3_pack4(qv[d0], qv[d0 + 1], qv[d0 + 2], qv[d0 + 3], lo_sh));
+        qx[4 + w4] = int(e4m3_pack4(qv[d1], qv[d1 + 1], qv[d1 + 2], qv[d1 + 3], hi_sh));
+      }
+    }
+  }
   // bias rows (log2-scaled s * r.P, reversed): key j reads entry j - L + rl_base
   const float* rlrow = p.rl + (size_t(b) * Hq + h) * p.rl_stride;
 
@@ -192,36 +253,68 @@ __global__ __launch_bounds__(kDecWaves * 64, sizeof(T) == 2 ? 2 : 1) void decode
   const size_t row_stride = size_t(Hkv) * D;
   const T* kbase = kg + (size_t(b) * L * Hkv + kvh) * D;
   const T* vbase = vg + (size_t(b) * L * Hkv + kvh) * D;
+  // MX: codes (one byte per value) and scales (D / 32 bytes per row)
+  typedef unsigned char u8;
+  constexpr int NSC = D / kMxBlock;
+  const size_t mrow = size_t(Hkv) * D, srow = size_t(Hkv) * NSC;
+  const u8* kc = static_cast<const u8*>(p.k);
+  const u8* vc = static_cast<const u8*>(p.v);
+  const u8* ksc = static_cast<const u8*>(p.k_scale);
+  const u8* vsc = static_cast<const u8*>(p.v_scale);
 
   // Every load of a step is unconditional, so the compiler's wait before a
   // step covers only that step's loads and later steps' stay in flight: rows
   // past the split end are clamped to its last key (masked later, weight
   // exactly 0 against finite data).
-  auto fetch = [&](int j0, Chunk<T>& ch) {
+  auto fetch = [&](int j0, CH& ch) {
     // rows past the split end are clamped to its last key; in the paged form
     // the clamped rows of a step share one page: the page of min(j0, ke-1)
     const T* kb = kbase;
     const T* vb = vbase;
-    int jp = 0;  // first key of that page
+    int jp = 0;                   // first key of that page
+    size_t r0 = size_t(b) * L;    // cache row of key jp
     if constexpr (PAGED) {
       const int jsel = max(min(j0, ke - 1), 0);
       const int pi = min(jsel / p.page_size, p.max_pages - 1);
       const int pg = min(max(p.btab[size_t(b) * p.max_pages + pi], 0), p.num_pages - 1);
       jp = pi * p.page_size;
-      kb = kg + (size_t(pg) * p.page_size * Hkv + kvh) * D;
-      vb = vg + (size_t(pg) * p.page_size * Hkv + kvh) * D;
+      r0 = size_t(pg) * p.page_size;
+      kb = kg + (r0 * Hkv + kvh) * D;
+      vb = vg + (r0 * Hkv + kvh) * D;
     }
+    if constexpr (MX) {
+      // rows of sequence b (or of the page) of kv head kvh
+      const u8* kcb = kc + r0 * mrow + size_t(kvh) * D;
+      const u8* vcb = vc + r0 * mrow + size_t(kvh) * D;
+      const u8* ksb = ksc + r0 * srow + size_t(kvh) * NSC;
+      const u8* vsb = vsc + r0 * srow + size_t(kvh) * NSC;
 #pragma unroll
-    for (int blk = 0; blk < 2; ++blk) {
-      const int j = min(j0 + 16 * blk + c, ke - 1);
-      const T* src = kb + size_t(j - jp) * row_stride + 8 * g;
+      for (int blk = 0; blk < 2; ++blk) {
+        const int j = min(j0 + 16 * blk + c, ke - 1) - jp;
+        const uint4 lo = *reinterpret_cast<const uint4*>(kcb + size_t(j) * mrow + 16 * g);
+        const uint4 hi = *reinterpret_cast<const uint4*>(kcb + size_t(j) * mrow + 64 + 16 * g);
+        ch.k[blk] = i32x8{int(lo.x), int(lo.y), int(lo.z), int(lo.w), int(hi.x), int(hi.y), int(hi.z), int(hi.w)};
+        ch.ks[blk] = ksb[size_t(j) * srow + g];
+      }
 #pragma unroll
-      for (int st = 0; st < D / 32; ++st) ch.k[blk][st] = ld8<T>(src + 32 * st);
-    }
+      for (int i = 0; i < 8; ++i) {
+        const int j = min(j0 + 8 * g + i, ke - 1) - jp;
+        ch.v[i] = *reinterpret_cast<const uint2*>(vcb + size_t(j) * mrow + 8 * c);
+        ch.vs[i] = vsb[size_t(j) * srow + (c >> 2)];
+      }
+    } else {
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int j = min(j0 + 8 * g + i, ke - 1);
-      ch.v[i] = ld8<T>(vb + size_t(j - jp) * row_stride + 8 * c);
+      for (int blk = 0; blk < 2; ++blk) {
+        const int j = min(j0 + 16 * blk + c, ke - 1);
+        const T* src = kb + size_t(j - jp) * row_stride + 8 * g;
+#pragma unroll
+        for (int st = 0; st < D / 32; ++st) ch.k[blk][st] = ld8<T>(src + 32 * st);
+      }
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const int j = min(j0 + 8 * g + i, ke - 1);
+        ch.v[i] = ld8<T>(vb + size_t(j - jp) * row_stride + 8 * c);
+      }
     }
     if constexpr (PAGED) {
       // bias of key j at entry d = Lb-1-j of the distance-ordered row (0 past E)
@@ -245,16 +338,36 @@ __global__ __launch_bounds__(kDecWaves * 64, sizeof(T) == 2 ? 2 : 1) void decode
     }
   };
 
-  auto process = [&](int j0, Chunk<T>& ch) {
-    VS::stage(vbuf, ch.v, g, c);
-
-    // scores in log2 units: accumulator (blk, v) of lane (g, c) = key j0 + 16*blk + 4*g + v, head c
+  auto process = [&](int j0, CH& ch) {
     f32x4 x[2];
+    if constexpr (MX) {
+      // V codes -> bf16 (exact: a 4-bit significand times a power of two)
+      v8_t<T> vd[8];
 #pragma unroll
-    for (int blk = 0; blk < 2; ++blk) {
-      x[blk] = zero4();
+      for (int i = 0; i < 8; ++i) {
+        const float sc = e8m0_float(ch.vs[i]);
+        typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+        const bf16x2 a0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(ch.v[i].x, sc, false);
+        const bf16x2 a1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(ch.v[i].x, sc, true);
+        const bf16x2 a2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(ch.v[i].y, sc, false);
+        const bf16x2 a3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(ch.v[i].y, sc, true);
+        vd[i] = v8_t<T>{a0[0], a0[1], a1[0], a1[1], a2[0], a2[1], a3[0], a3[1]};
+      }
+      VS::stage(vbuf, vd, g, c);
+      // scores: one MXFP8 MFMA per 16 keys covers all of D
 #pragma unroll
-      for (int st = 0; st < D / 32; ++st) mma16(ch.k[blk][st], qreg[st], x[blk]);
+      for (int blk = 0; blk < 2; ++blk)
+        x[blk] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(ch.k[blk], qx, zero4(), 0, 0, 0, int(ch.ks[blk]), 0,
+                                                                 int(qs));
+    } else {
+      VS::stage(vbuf, ch.v, g, c);
+      // scores in log2 units: accumulator (blk, v) of lane (g, c) = key j0 + 16*blk + 4*g + v, head c
+#pragma unroll
+      for (int blk = 0; blk < 2; ++blk) {
+        x[blk] = zero4();
+#pragma unroll
+        for (int st = 0; st < D / 32; ++st) mma16(ch.k[blk][st], qreg[st], x[blk]);
+      }
     }
 #pragma unroll
     for (int blk = 0; blk < 2; ++blk)
@@ -311,7 +424,7 @@ __global__ __launch_bounds__(kDecWaves * 64, sizeof(T) == 2 ? 2 : 1) void decode
   // process below is unconditional and the waits stay partial.
   constexpr int NB = kDecDepth;
   constexpr int STRIDE = kDecWaves * kDecKeys;
-  Chunk<T> ring[NB];
+  CH ring[NB];
   // steps of this split: the plan's chunk, or (paged) up to the sequence's
   // end in whole ring turns; none for an empty split
   int j_end = ks + p.chunk;
@@ -476,7 +589,7 @@ __global__ __launch_bounds__(256) void decode_merge_small_kernel(DecodeArgs p) {
   if (p.lse != nullptr && d4 == 0) p.lse[bh] = (M + log2f(den)) * kLn2;
 }
 
-template <typename T, bool PAGED>
+template <typename T, bool PAGED, bool MX = false>
 hipError_t launch_decode_t(const DecodeArgs& a, hipStream_t stream) {
   {
     // bias rows of every (sequence, head): s * log2(e) * r.P[:, d], stored
@@ -501,7 +614,7 @@ hipError_t launch_decode_t(const DecodeArgs& a, hipStream_t stream) {
   }
   const long long grid = (long long)a.B * a.Hkv * a.n_hg * a.n_split;
   if (grid > 0x7fffffffLL) return hipErrorInvalidConfiguration;
-  hipLaunchKernelGGL((decode_split_kernel<T, PAGED>), dim3((unsigned)grid), dim3(kDecWaves * 64), 0, stream, a);
+  hipLaunchKernelGGL((decode_split_kernel<T, PAGED, MX>), dim3((unsigned)grid), dim3(kDecWaves * 64), 0, stream, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   if (a.n_split <= kMergeSmallSplits) {
@@ -565,6 +678,11 @@ hipError_t launch_decode(int dtype, const DecodeArgs& a, hipStream_t stream) {
 hipError_t launch_decode_paged(int dtype, const DecodeArgs& a, hipStream_t stream) {
   if (dtype == 1) return launch_decode_t<__bf16, true>(a, stream);
   return launch_decode_t<float, true>(a, stream);
+}
+
+hipError_t launch_decode_mx(const DecodeArgs& a, hipStream_t stream) {
+  if (a.btab != nullptr) return launch_decode_t<__bf16, true, true>(a, stream);
+  return launch_decode_t<__bf16, false, true>(a, stream);
 }
 
 }  // namespace relattn

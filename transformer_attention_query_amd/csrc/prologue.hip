@@ -25,6 +25,7 @@
 // three previous k / v rows hit the caches) and one write of every output
 // row -- the kernels are bound by HBM bandwidth.
 #include "device_common.hpp"
+#include "mx_common.hpp"
 #include "relattn_internal.hpp"
 
 namespace relattn {
@@ -99,7 +100,7 @@ __device__ __forceinline__ void q_rows(const PrologueArgs& p, int wg, long long 
 // block's rows; rows before a sequence's chunk come from the state.
 constexpr int kTB = 4;
 
-template <typename T>
+template <typename T, bool MX>
 __device__ __forceinline__ void kv_rows(const PrologueArgs& p, int wg, int n_row_units, int n_units) {
   __shared__ int s_qs[kSeqLds];
   __shared__ int s_kv[kSeqLds];
@@ -189,7 +190,6 @@ __device__ __forceinline__ void kv_rows(const PrologueArgs& p, int wg, int n_row
     b = lo;
   }
   int sb = qs(b), se = qs(b + 1);
-  T* cache = static_cast<T*>(is_k ? p.k_cache : p.v_cache);
 #pragma unroll
   for (int k = 0; k < kTB; ++k) {
     const int t = t0 + k;
@@ -242,7 +242,26 @@ __device__ __forceinline__ void kv_rows(const PrologueArgs& p, int wg, int n_row
       const int pg = p.btab[size_t(b) * p.max_pages + pos / p.page_size];
       if (pg >= 0 && pg < p.num_pages) row = (long long)pg * p.page_size + pos % p.page_size;
     }
-    if (row >= 0) store8f<T>(cache + size_t(row) * rs + size_t(hk) * kHeadDim + c0, y);
+    if constexpr (MX) {
+      // E4M3 codes with the scale of the 32-channel block (the lane's quad)
+      float amax = 0.0f;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) amax = fmaxf(amax, fabsf(y[e]));
+      const int sh = mx_shared_exp(quad_max(amax));
+      uint2 cw;
+      cw.x = e4m3_pack4(y[0], y[1], y[2], y[3], sh);
+      cw.y = e4m3_pack4(y[4], y[5], y[6], y[7], sh);
+      if (row >= 0) {
+        unsigned char* cc = static_cast<unsigned char*>(is_k ? p.k_cache : p.v_cache);
+        unsigned char* sc = static_cast<unsigned char*>(is_k ? p.k_scale : p.v_scale);
+        *reinterpret_cast<uint2*>(cc + (size_t(row) * Hkv + hk) * kHeadDim + c0) = cw;
+        if ((lane16 & 3) == 0)
+          sc[(size_t(row) * Hkv + hk) * (kHeadDim / kMxBlock) + (lane16 >> 2)] = (unsigned char)(sh + 127);
+      }
+    } else {
+      T* cache = static_cast<T*>(is_k ? p.k_cache : p.v_cache);
+      if (row >= 0) store8f<T>(cache + size_t(row) * rs + size_t(hk) * kHeadDim + c0, y);
+    }
     if (t == se - 1 && p.state_out != nullptr) {  // last new token: its three last raw rows are the new state
       T* so = static_cast<T*>(p.state_out) + (size_t(b) * 2 + s) * kStateRows * C + hk * kHeadDim + c0;
       store8f<T>(so, x[2]);
@@ -254,14 +273,14 @@ __device__ __forceinline__ void kv_rows(const PrologueArgs& p, int wg, int n_row
 
 // One launch for both jobs: the k / v workgroups come first (they start
 // first and their latency-bound work overlaps the q rows' streaming).
-template <typename T>
+template <typename T, bool MX = false>
 __global__ __launch_bounds__(256) void prologue_kernel(PrologueArgs p, int n_kv_wg, int n_row_units, int n_units,
                                                        long long n_q) {
-  if ((int)blockIdx.x < n_kv_wg) kv_rows<T>(p, blockIdx.x, n_row_units, n_units);
+  if ((int)blockIdx.x < n_kv_wg) kv_rows<T, MX>(p, blockIdx.x, n_row_units, n_units);
   else q_rows<T>(p, blockIdx.x - n_kv_wg, n_q);
 }
 
-template <typename T>
+template <typename T, bool MX = false>
 hipError_t launch_t(const PrologueArgs& a, hipStream_t stream) {
   const long long n_q = (long long)a.total_q * a.Hq;
   const long long q_wg = (n_q + 16 * kQRows - 1) / (16 * kQRows);
@@ -269,12 +288,14 @@ hipError_t launch_t(const PrologueArgs& a, hipStream_t stream) {
   const long long n_units = n_rows + (long long)a.B * 2 * a.Hkv;
   const long long kv_wg = (n_units + 15) / 16;
   if (n_units > 0x7fffffffLL - 16 || q_wg + kv_wg > 0x7fffffffLL) return hipErrorInvalidConfiguration;
-  hipLaunchKernelGGL(prologue_kernel<T>, dim3((unsigned)(q_wg + kv_wg)), dim3(256), 0, stream, a, (int)kv_wg,
+  hipLaunchKernelGGL((prologue_kernel<T, MX>), dim3((unsigned)(q_wg + kv_wg)), dim3(256), 0, stream, a, (int)kv_wg,
                      (int)n_rows, (int)n_units, n_q);
   return hipGetLastError();
 }
 
 }  // namespace
+
+hipError_t launch_prologue_mx(const PrologueArgs& a, hipStream_t stream) { return launch_t<__bf16, true>(a, stream); }
 
 hipError_t launch_prologue(int dtype, const PrologueArgs& a, hipStream_t stream) {
   if (dtype == 1) return launch_t<__bf16>(a, stream);

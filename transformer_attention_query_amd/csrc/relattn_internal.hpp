@@ -60,6 +60,10 @@ struct DecodeArgs {
   int max_pages = 0, num_pages = 0, page_size = 0;
   int log_scale = 0;            // s per sequence from kv_len
   float alpha = 0.0f;
+  // MXFP8 caches only (see rel_attn_decode_mx): k and v then hold E4M3 codes
+  // [.., Hkv, D] and these their E8M0 block scales [.., Hkv, D / 32]
+  const void* k_scale = nullptr;
+  const void* v_scale = nullptr;
 };
 
 // Attention prologue (see rel_attn_prologue): device pointers and host bounds.
@@ -82,6 +86,10 @@ struct PrologueArgs {
   float eps;
   int B, total_q, Hq, Hkv, conv_w;
   int cap, max_pages, num_pages, page_size;
+  // MXFP8 caches (rel_attn_prologue_mx): k_cache / v_cache hold E4M3 codes
+  // and these the E8M0 scales [.., Hkv, D / 32]
+  void* k_scale = nullptr;
+  void* v_scale = nullptr;
 };
 
 // out[row * out_stride + oc] = s * r[row] . P_cols[d(oc)] for oc < out_cols,
@@ -113,9 +121,15 @@ DecodePlan plan_decode(int B, int L, int Hq, int Hkv, int num_splits_req, int wi
 // Launchers: return hipSuccess or the launch error.  dtype: 1 = bf16, 2 = fp32.
 hipError_t launch_prefill(int dtype, const PrefillArgs& a, hipStream_t stream);
 hipError_t launch_prologue(int dtype, const PrologueArgs& a, hipStream_t stream);
+// bf16 inputs, MXFP8 caches
+hipError_t launch_prologue_mx(const PrologueArgs& a, hipStream_t stream);
 hipError_t launch_extend(int dtype, const PrefillArgs& a, hipStream_t stream);
 hipError_t launch_decode(int dtype, const DecodeArgs& a, hipStream_t stream);
 hipError_t launch_decode_paged(int dtype, const DecodeArgs& a, hipStream_t stream);
+// MXFP8 K/V caches, bf16 q / r / P / out; paged when a.btab is set
+hipError_t launch_decode_mx(const DecodeArgs& a, hipStream_t stream);
+// rows of D = 128 values (dtype) -> E4M3 codes [n_rows, 128] and E8M0 scales [n_rows, 4]
+hipError_t launch_mx_quantize(int dtype, const void* x, void* codes, void* scales, long long n_rows, hipStream_t stream);
 hipError_t launch_rel_logits(int dtype, const RelLogitsArgs& a, hipStream_t stream);
 
 }  // namespace relattn
