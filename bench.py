@@ -175,6 +175,43 @@ def bench_decode(steps: int, warmup: int):
     return w, nbytes, kv, total_ms / steps, sum(per) / len(per), ns
 
 
+def decode_bytes_mx(B: int, L: int, Hq: int, Hkv: int, D: int, d_r: int, E: int, W: int) -> int:
+    """Algorithmic bytes of one decode call over MXFP8 caches: per visible key
+    and kv head the K and V codes (D bytes each) and scales (D/32 bytes
+    each); q, r and out per sequence (bf16) and P once, as for bf16."""
+    vis = min(L, W) if W > 0 else L
+    kv = B * vis * Hkv * 2 * (D + D // 32)
+    per_seq = B * (Hq * D * 2 + Hq * d_r * 2 + Hq * D * 2)
+    return kv + per_seq + E * d_r * 2
+
+
+def bench_decode_mx(steps: int, warmup: int):
+    """decode_64x8k over MXFP8 caches (quantised once from the bf16 ones)."""
+    import torch
+    import transformer_attention_query_amd as ra
+    from transformer_attention_query_amd import inputs as tinputs
+
+    w = tinputs.WORKLOADS[DECODE_WORKLOAD]
+    x = {n: t.cuda() for n, t in tinputs.make_inputs(w, seed=0).items()}
+    kc, ks = ra.mx_quantize(x["k"])
+    vc, vs = ra.mx_quantize(x["v"])
+    del x["k"], x["v"]
+    # two copies, used alternately: a launch reads ~277 MB, past the 256 MB MALL
+    caches = [(kc, ks, vc, vs), (kc.clone(), ks.clone(), vc.clone(), vs.clone())]
+    ns, ws_bytes = ra.decode_plan(w.B, w.T, w.Hq, w.Hkv, w.D, 0, w.W, w.E)
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device="cuda")
+    stream = torch.cuda.current_stream()
+
+    def step(i):
+        c = caches[i % 2]
+        ra.decode_mx(x["q"], c[0], c[1], c[2], c[3], x["r"], x["P_cols"], w.alpha, w.E, w.W, w.log_scale,
+                     num_splits=ns, workspace=ws)
+
+    total_ms, per = _time_launches(step, steps, warmup, stream)
+    nbytes = decode_bytes_mx(w.B, w.T, w.Hq, w.Hkv, w.D, w.d_r, w.E, w.W)
+    return w, nbytes, total_ms / steps, sum(per) / len(per), ns
+
+
 def bench_extend(steps: int, warmup: int):
     """Chunked prefill over a paged cache: the new rows of every sequence."""
     import torch
@@ -377,7 +414,7 @@ def main():
                           "roofline": {"bound": "hbm", "kernel": DECODE_KERNEL + "+merge", "achieved": round(kgbps, 1),
                                        "peak": PEAK_HBM_GBPS, "unit": "GB/s",
                                        "frac": round(kgbps / PEAK_HBM_GBPS, 4),
-                                       "traffic": _traffic(DECODE_KERNEL, _src_hash("decode.hip", "device_common.hpp")),
+                                       "traffic": _traffic(DECODE_KERNEL, _src_hash("decode.hip", "device_common.hpp", "mx_common.hpp")),
                                        "avg_launch_us": round(d_kernel_ms * 1e3, 2)}}
     if not args.no_decode:
         pw, p_bytes, p_ms, p_kernel_ms, p_ns = bench_decode_paged(args.steps, args.warmup)
@@ -389,8 +426,21 @@ def main():
                                              "achieved": round(pk, 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
                                              "frac": round(pk / PEAK_HBM_GBPS, 4),
                                              "traffic": _traffic(DECODE_KERNEL + "_paged",
-                                                                 _src_hash("decode.hip", "device_common.hpp")),
+                                                                 _src_hash("decode.hip", "device_common.hpp", "mx_common.hpp")),
                                              "avg_launch_us": round(p_kernel_ms * 1e3, 2)}}
+    if not args.no_decode:
+        mw, m_bytes, m_ms, m_kernel_ms, m_ns = bench_decode_mx(args.steps, args.warmup)
+        print(f"# decode {mw.name} (MXFP8 K/V): {m_ms * 1e3:.1f} us/step ({m_ns} splits)", file=sys.stderr, flush=True)
+        mk = m_bytes / (m_kernel_ms * 1e-3) / 1e9
+        line["decode_mx"] = {"workload": mw.name + " (MXFP8 K/V)", "value": round(m_bytes / (m_ms * 1e-3) / 1e9, 1),
+                             "unit": "GB/s", "ms_per_step": round(m_ms, 5), "num_splits": m_ns,
+                             "algorithmic_bytes": m_bytes, "dtype": "mxfp8 K/V, bf16 q/out",
+                             "roofline": {"bound": "hbm", "kernel": DECODE_KERNEL + " (MXFP8)+merge",
+                                          "achieved": round(mk, 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
+                                          "frac": round(mk / PEAK_HBM_GBPS, 4),
+                                          "traffic": _traffic(DECODE_KERNEL + "_mx",
+                                                              _src_hash("decode.hip", "device_common.hpp", "mx_common.hpp")),
+                                          "avg_launch_us": round(m_kernel_ms * 1e3, 2)}}
     if not args.no_extend:
         ew, e_flops, e_ms, e_kernel_ms = bench_extend(args.steps, args.warmup)
         print(f"# extend {ew.name}: {e_ms * 1e3:.1f} us/step", file=sys.stderr, flush=True)
@@ -416,7 +466,7 @@ def main():
                             "roofline": {"bound": "hbm", "kernel": "prologue_kernel", "achieved": round(gk, 1),
                                          "peak": PEAK_HBM_GBPS, "unit": "GB/s", "frac": round(gk / PEAK_HBM_GBPS, 4),
                                          "traffic": _traffic("prologue_kernel",
-                                                             _src_hash("prologue.hip", "device_common.hpp")),
+                                                             _src_hash("prologue.hip", "device_common.hpp", "mx_common.hpp")),
                                          "avg_launch_us": round(g_kernel_ms * 1e3, 2)}}
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline()
