@@ -34,3 +34,6 @@ from .mx_oracle import (  # noqa: F401
     mx_quantize,
     mx_round,
 )
+from .backward_oracle import (  # noqa: F401
+    prefill_backward,
+)

@@ -36,3 +36,15 @@ def test_workload_table_matches_spec():
     assert W["decode_1x1m_log"].T == 1048576 and W["decode_64x8k"].B == 64
     for w in W.values():
         assert w.D == 128 and w.Hq % w.Hkv == 0
+
+
+def test_backward_inputs_extend_the_prefill_draws():
+    """The backward recipe draws the prefill tensors first, so they equal the
+    prefill inputs of the same seed; dout comes last."""
+    a = tinputs.make_prefill_inputs(1, 40, 4, 2, 128, 32, 16, "bf16", seed=3)
+    b = tinputs.make_backward_inputs(1, 40, 4, 2, 128, 32, 16, "bf16", seed=3)
+    for n in a:
+        assert torch.equal(a[n].float(), b[n].float())
+    assert b["dout"].shape == (1, 40, 4, 128) and b["dout"].dtype == torch.bfloat16
+    w = tinputs.WORKLOADS["swa_backward_8k"]
+    assert (w.kind, w.T, w.W, w.E, w.d_r) == ("backward", 8192, 1024, 1024, 128)

@@ -17,6 +17,8 @@ P ~ N(0, 0.02^2)); every tensor is then rounded to the workload dtype.
            seeded random permutation of page slots (a block table), when a
            page size is given.
 
+* backward: the prefill tensors, then dout [B,T,Hq,D] (the gradient of the
+           loss w.r.t. the attention output), drawn after P.
 * prologue: q [N,Hq,D], k [N,Hkv,D], v [N,Hkv,D] (the raw projections of
            N packed new tokens), conv_k, conv_v [Hkv*D,W] times ``conv_std``
            (0.3), q_norm_w, k_norm_w [D] as 1 + 0.1 * normal, then (if asked)
@@ -39,8 +41,8 @@ from typing import Dict, Optional
 
 import torch
 
-__all__ = ["Workload", "WORKLOADS", "make_prefill_inputs", "make_decode_inputs", "make_extend_inputs",
-           "make_prologue_inputs", "make_inputs", "torch_dtype"]
+__all__ = ["Workload", "WORKLOADS", "make_prefill_inputs", "make_backward_inputs", "make_decode_inputs",
+           "make_extend_inputs", "make_prologue_inputs", "make_inputs", "torch_dtype"]
 
 
 def torch_dtype(name: str) -> torch.dtype:
@@ -51,7 +53,7 @@ def torch_dtype(name: str) -> torch.dtype:
 class Workload:
     """One named relative-attention workload (shapes, masks and dtype)."""
     name: str
-    kind: str            # "prefill", "decode", "extend" or "prologue"
+    kind: str            # "prefill", "backward", "decode", "extend" or "prologue"
     dtype: str           # "bf16" or "fp32"
     B: int
     T: int               # prefill: sequence length; decode, extend: kv length L
@@ -77,6 +79,9 @@ WORKLOADS: Dict[str, Workload] = {
     "swa_prefill_8k": Workload(
         "swa_prefill_8k", "prefill", "bf16", B=1, T=8192, Hq=16, Hkv=2, D=128, d_r=128, E=1024, W=1024,
         notes="sliding-window layer, 1024 keys incl. self, GQA 8:1"),
+    "swa_backward_8k": Workload(
+        "swa_backward_8k", "backward", "bf16", B=1, T=8192, Hq=16, Hkv=2, D=128, d_r=128, E=1024, W=1024,
+        notes="backward of the sliding-window layer: dq, dk, dv, dr at an 8K packed sequence, E = 1024"),
     "full_prefill_32k_log": Workload(
         "full_prefill_32k_log", "prefill", "bf16", B=2, T=32768, Hq=16, Hkv=2, D=128, d_r=128, E=1024,
         log_scale=True, notes="full causal layer with the length log-scale (s = 1.25)"),
@@ -119,6 +124,24 @@ def make_prefill_inputs(B: int, T: int, Hq: int, Hkv: int, D: int, d_r: int, E: 
     r = _draw(gen, (B, T, Hq, d_r)).to(dt)
     P = (_draw(gen, (d_r, E)) * p_std).to(dt)
     out = {"q": q, "k": k, "v": v, "r": r, "P": P, "P_cols": P.t().contiguous()}
+    if device is not None:
+        out = {n: t.to(device) for n, t in out.items()}
+    return out
+
+
+def make_backward_inputs(B: int, T: int, Hq: int, Hkv: int, D: int, d_r: int, E: int,
+                         dtype: str = "bf16", seed: int = 0, p_std: float = 0.02,
+                         device: Optional[str] = None) -> Dict[str, torch.Tensor]:
+    """Seeded backward inputs: the prefill inputs of the same seed, then dout."""
+    gen = torch.Generator("cpu").manual_seed(seed)
+    dt = torch_dtype(dtype)
+    q = _draw(gen, (B, T, Hq, D)).to(dt)
+    k = _draw(gen, (B, T, Hkv, D)).to(dt)
+    v = _draw(gen, (B, T, Hkv, D)).to(dt)
+    r = _draw(gen, (B, T, Hq, d_r)).to(dt)
+    P = (_draw(gen, (d_r, E)) * p_std).to(dt)
+    dout = _draw(gen, (B, T, Hq, D)).to(dt)
+    out = {"q": q, "k": k, "v": v, "r": r, "P": P, "P_cols": P.t().contiguous(), "dout": dout}
     if device is not None:
         out = {n: t.to(device) for n, t in out.items()}
     return out
@@ -247,6 +270,8 @@ def make_inputs(w: Workload, seed: int = 0, device: Optional[str] = None) -> Dic
     if w.kind == "extend":
         return make_extend_inputs([w.T] * w.B, [w.n_new] * w.B, w.Hq, w.Hkv, w.D, w.d_r, w.E, w.dtype, seed,
                                   page_size=w.page_size, device=device)
+    if w.kind == "backward":
+        return make_backward_inputs(w.B, w.T, w.Hq, w.Hkv, w.D, w.d_r, w.E, w.dtype, seed, device=device)
     if w.kind == "prefill":
         return make_prefill_inputs(w.B, w.T, w.Hq, w.Hkv, w.D, w.d_r, w.E, w.dtype, seed, device=device)
     return make_decode_inputs(w.B, w.T, w.Hq, w.Hkv, w.D, w.d_r, w.E, w.dtype, seed, device=device)
