@@ -273,6 +273,48 @@ int rel_attn_decode_mx(const void* q, const void* k_codes, const void* k_scales,
                        void* stream);
 
 /*
+ * Backward plan: a pure function of the shape.  Writes the number of
+ * workgroups each kv head's query heads are split over in the dk / dv kernel
+ * (head_splits_req > 0 asks for that many and must divide Hq / Hkv; 0 lets
+ * the library choose, from the 128-key blocks and B * Hkv, so that the launch
+ * fills the GPU) and the workspace size in bytes: delta_i = dout_i . out_i per
+ * (sequence, head, row) as float32, plus, when the heads are split, float32
+ * partial dk and dv per split.
+ */
+int rel_attn_backward_plan(int B, int T, int Hq, int Hkv, int D, int head_splits_req,
+                           int* head_splits_out, size_t* workspace_bytes_out);
+
+/*
+ * Backward of rel_attn_prefill (page "SGLang and Miles Add Day-0 Support for
+ * Inkling", section "Customized Efficient Kernels for Train-Inference
+ * Consistency", paragraph "Relative attention": gradients through the scores
+ * and through r, the relative projection P held fixed).  For the loss
+ * sum(dout * out):
+ *   dq_i = s alpha sum_j ds_ij k_j        dk_j = s alpha sum_i ds_ij q_i
+ *   dv_j = sum_i p_ij dout_i              dr_i = s sum_{d < E} ds_{i,i-d} P[:, d]
+ * with p the attention weights, ds_ij = p_ij (dout_i . v_j - dout_i . out_i),
+ * and the sums for dk and dv also over the query heads of the kv head.
+ *   q, dq, dout, out [B, T, Hq, D]   k, v, dk, dv [B, T, Hkv, D]
+ *   r, dr [B, T, Hq, d_r]   P_cols [E, d_r]   lse [B, Hq, T] float32
+ * out and lse are what rel_attn_prefill returned for the same inputs and
+ * arguments (lse is required).  dtype: RA_BF16 only (RA_F32 returns
+ * RA_ERR_UNSUPPORTED); gradients are accumulated in float32 and written in
+ * bf16.  rel_extent == 0: r, P_cols and dr may be NULL (a non-NULL dr is left
+ * untouched).  head_splits and the workspace come from rel_attn_backward_plan
+ * (workspace: device memory, 256-byte aligned, contents ignored on entry and
+ * unspecified on return).  Gradient outputs must not alias the inputs, the
+ * workspace or each other; they are fully overwritten.  Four kernels on
+ * `stream`: delta, dq and dr, dk and dv, and (head_splits > 1) the sum of the
+ * partials.  B == 0 or T == 0 is a no-op that returns RA_OK.
+ */
+int rel_attn_backward(const void* q, const void* k, const void* v, const void* r,
+                      const void* P_cols, const void* out, const void* dout, const float* lse,
+                      void* dq, void* dk, void* dv, void* dr, int dtype,
+                      int B, int T, int Hq, int Hkv, int D, int d_r,
+                      float alpha, int rel_extent, int window, int log_scale,
+                      int head_splits, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * Dense relative logits (eq. for rel_logits in the same section):
  *   out[t, h, d] = s * sum_c r[t, h, c] * P_cols[d, c]   for every d < rel_extent
  *   r [n_tok, H, d_r] (dtype)   P_cols [E, d_r] (dtype)   out [n_tok, H, E] float32

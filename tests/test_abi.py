@@ -37,7 +37,7 @@ def test_header_declares_the_boundary():
     names = _declared_functions()
     for n in ("rel_attn_prefill", "rel_attn_extend", "rel_attn_decode", "rel_attn_decode_paged",
               "rel_attn_decode_plan", "rel_logits", "rel_attn_prologue", "rel_attn_prologue_mx",
-              "rel_attn_decode_mx", "rel_mx_quantize",
+              "rel_attn_decode_mx", "rel_mx_quantize", "rel_attn_backward", "rel_attn_backward_plan",
               "rel_attn_last_error", "rel_attn_version", "rel_attn_scale_factor"):
         assert n in names
 
@@ -380,3 +380,74 @@ def _prologue_mx(lib, **kw):
 def test_prologue_mx_rejects_bad_arguments(lib, kw, code, frag):
     assert _prologue_mx(lib, **kw) == code
     assert frag in lib.rel_attn_last_error().decode()
+
+
+# ---------------------------------------------------------------- backward
+
+def _bplan(lib, B, T, Hq, Hkv, D=128, req=0):
+    ns, wb = ctypes.c_int(-7), ctypes.c_size_t(0)
+    rc = lib.rel_attn_backward_plan(B, T, Hq, Hkv, D, req, ctypes.byref(ns), ctypes.byref(wb))
+    return rc, ns.value, wb.value
+
+
+def test_backward_plan_is_pure_and_sized(lib):
+    rc, ns, wb = _bplan(lib, 1, 8192, 16, 2)
+    # 64 blocks of 128 keys x 2 kv heads = 128 workgroups: the 8 heads of a group split in 2
+    assert rc == RA_OK and ns == 2
+    assert wb == 16 * 8192 * 4 + 2 * 2 * 8192 * 2 * 128 * 4
+    assert _bplan(lib, 1, 8192, 16, 2) == (rc, ns, wb)
+    rc, ns, wb = _bplan(lib, 2, 32768, 16, 2)
+    assert rc == RA_OK and ns == 1 and wb == 2 * 16 * 32768 * 4  # enough blocks: no split, no partials
+    assert _bplan(lib, 1, 100, 16, 2, req=4)[:2] == (RA_OK, 4)
+    rc, ns, wb = _bplan(lib, 1, 5, 3, 3)  # one head per kv head: nothing to split
+    assert rc == RA_OK and ns == 1 and wb == 256
+
+
+@pytest.mark.parametrize("args,code", [
+    ((1, 100, 16, 2, 128, 3), RA_ERR_INVALID_ARG),
+    ((1, 100, 16, 2, 128, -1), RA_ERR_INVALID_ARG),
+    ((1, 100, 6, 4, 128, 0), RA_ERR_INVALID_ARG),
+    ((-1, 100, 16, 2, 128, 0), RA_ERR_INVALID_ARG),
+    ((1, 100, 16, 2, 64, 0), RA_ERR_UNSUPPORTED),
+])
+def test_backward_plan_rejects(lib, args, code):
+    assert _bplan(lib, *args)[0] == code
+
+
+def _backward(lib, **kw):
+    a = dict(q=FAKE, k=FAKE + 16, v=FAKE + 32, r=FAKE + 48, P=FAKE + 64, out=FAKE + 80, dout=FAKE + 96,
+             lse=FAKE + 112, dq=FAKE + 128, dk=FAKE + 144, dv=FAKE + 160, dr=FAKE + 176, dtype=RA_BF16,
+             B=1, T=100, Hq=16, Hkv=2, D=128, d_r=128, alpha=0.1, E=64, W=0, ls=0, ns=1, ws=FAKE * 16,
+             wsb=1 << 30)
+    a.update(kw)
+    return lib.rel_attn_backward(a["q"], a["k"], a["v"], a["r"], a["P"], a["out"], a["dout"], a["lse"], a["dq"],
+                                 a["dk"], a["dv"], a["dr"], a["dtype"], a["B"], a["T"], a["Hq"], a["Hkv"], a["D"],
+                                 a["d_r"], a["alpha"], a["E"], a["W"], a["ls"], a["ns"], a["ws"], a["wsb"], None)
+
+
+@pytest.mark.parametrize("kw,code,frag", [
+    (dict(dtype=RA_F32), RA_ERR_UNSUPPORTED, "RA_BF16"),
+    (dict(dtype=5), RA_ERR_INVALID_ARG, "dtype"),
+    (dict(lse=None), RA_ERR_INVALID_ARG, "lse is NULL"),
+    (dict(dout=None), RA_ERR_INVALID_ARG, "dout is NULL"),
+    (dict(dr=None), RA_ERR_INVALID_ARG, "dr is NULL"),
+    (dict(dq=FAKE), RA_ERR_INVALID_ARG, "alias"),
+    (dict(dv=FAKE + 144), RA_ERR_INVALID_ARG, "alias"),
+    (dict(dk=FAKE * 16), RA_ERR_INVALID_ARG, "alias"),
+    (dict(ns=3), RA_ERR_INVALID_ARG, "head_splits"),
+    (dict(ns=0), RA_ERR_INVALID_ARG, "head_splits"),
+    (dict(ws=None), RA_ERR_WORKSPACE, "NULL"),
+    (dict(ws=FAKE * 16 + 16), RA_ERR_WORKSPACE, "256-byte"),
+    (dict(wsb=100), RA_ERR_WORKSPACE, "smaller"),
+    (dict(d_r=24), RA_ERR_UNSUPPORTED, "d_r"),
+    (dict(D=96), RA_ERR_UNSUPPORTED, "head dim"),
+])
+def test_backward_rejects_bad_arguments(lib, kw, code, frag):
+    assert _backward(lib, **kw) == code
+    assert frag in _err(lib)
+
+
+def test_backward_without_bias_needs_no_r_P_or_dr_and_empty_is_a_noop(lib):
+    assert _backward(lib, B=0, ws=None, wsb=0) == RA_OK
+    assert _backward(lib, T=0, ws=None, wsb=0) == RA_OK
+    assert _backward(lib, E=0, r=None, P=None, dr=None, B=0) == RA_OK

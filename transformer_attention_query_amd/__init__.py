@@ -1,8 +1,8 @@
-"""MI355X (gfx950) relative-attention forward: HIP kernels behind a C ABI.
+"""MI355X (gfx950) relative attention: HIP kernels behind a C ABI.
 
 ``prefill``, ``extend``, ``decode``, ``decode_paged``, ``decode_mx``,
-``decode_plan``, ``prologue``, ``prologue_mx``, ``mx_quantize`` and
-``rel_logits`` call the compiled library ``librelattn.so``
+``decode_plan``, ``prologue``, ``prologue_mx``, ``mx_quantize``,
+``rel_logits``, ``backward`` and ``backward_plan`` call the compiled library ``librelattn.so``
 (built in-tree by ``__graft_entry__.build()`` or
 ``python -m transformer_attention_query_amd.build``).  There is no fallback:
 if the library is missing the calls raise.
@@ -10,6 +10,8 @@ if the library is missing the calls raise.
 
 from .binding import (  # noqa: F401
     RelAttnError,
+    backward,
+    backward_plan,
     decode,
     decode_mx,
     decode_paged,

@@ -67,6 +67,12 @@ def _declare(lib):
     lib.rel_attn_decode_mx.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i32, i32, vp, vp, i32, i32, i32, i32, i32,
                                        i32, i32, f32, i32, i32, i32, i32, vp, sz, vp]
     lib.rel_attn_decode_mx.restype = i32
+    lib.rel_attn_backward_plan.argtypes = [i32, i32, i32, i32, i32, i32, ctypes.POINTER(ctypes.c_int),
+                                           ctypes.POINTER(ctypes.c_size_t)]
+    lib.rel_attn_backward_plan.restype = i32
+    lib.rel_attn_backward.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32,
+                                      i32, f32, i32, i32, i32, i32, vp, ctypes.c_size_t, vp]
+    lib.rel_attn_backward.restype = i32
     lib.rel_mx_quantize.argtypes = [vp, vp, vp, i32, i64, i32, vp]
     lib.rel_mx_quantize.restype = i32
     lib.rel_logits.argtypes = [vp, vp, vp, i32, i64, i32, i32, i32, i32, i64, vp]
@@ -559,3 +565,64 @@ def prologue_mx(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, conv_k: torch
                                     _ptr(q_start), _ptr(kv_len), cache_len, _ptr(block_table), max_pages, num_pages,
                                     page_size, Hq, Hkv, D, W, _stream(dev)))
     return q_out
+
+
+def backward_plan(B: int, T: int, Hq: int, Hkv: int, D: int = 128, head_splits: int = 0) -> Tuple[int, int]:
+    """(head_splits, workspace bytes) of a backward call of this shape."""
+    lib = load_library()
+    ns = ctypes.c_int(0)
+    wb = ctypes.c_size_t(0)
+    _check(lib.rel_attn_backward_plan(B, T, Hq, Hkv, D, head_splits, ctypes.byref(ns), ctypes.byref(wb)))
+    return ns.value, wb.value
+
+
+def backward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, r: Optional[torch.Tensor],
+             P_cols: Optional[torch.Tensor], out: torch.Tensor, dout: torch.Tensor, lse: torch.Tensor,
+             alpha: float, rel_extent: int, window: int = 0, log_scale: bool = False, head_splits: int = 0,
+             workspace: Optional[torch.Tensor] = None):
+    """Gradients (dq, dk, dv, dr) of sum(dout * out) for a bf16 prefill call.
+
+    q, out, dout [B,T,Hq,D]; k, v [B,T,Hkv,D]; r [B,T,Hq,d_r]; P_cols [E,d_r];
+    lse [B,Hq,T] fp32 from the forward.  dr is None when rel_extent == 0.
+    """
+    lib = load_library()
+    dev = q.device
+    dt = q.dtype
+    if dt != torch.bfloat16:
+        raise TypeError(f"backward supports bfloat16 only, got {dt}")
+    _need(q, "q", dt, dev, 4)
+    _need(k, "k", dt, dev, 4)
+    _need(v, "v", dt, dev, 4)
+    _need(out, "out", dt, dev, 4)
+    _need(dout, "dout", dt, dev, 4)
+    _need(lse, "lse", torch.float32, dev, 3)
+    B, T, Hq, D = q.shape
+    Hkv = k.shape[2]
+    if k.shape != (B, T, Hkv, D) or v.shape != k.shape or out.shape != q.shape or dout.shape != q.shape:
+        raise ValueError("q/k/v/out/dout shapes do not agree")
+    if lse.shape != (B, Hq, T):
+        raise ValueError(f"lse must be [B, Hq, T] = {(B, Hq, T)}, got {tuple(lse.shape)}")
+    d_r = 0
+    if rel_extent > 0:
+        _need(r, "r", dt, dev, 4)
+        _need(P_cols, "P_cols", dt, dev, 2)
+        d_r = r.shape[3]
+        if r.shape[:3] != (B, T, Hq):
+            raise ValueError(f"r shape {tuple(r.shape)} does not match q")
+        if P_cols.shape != (rel_extent, d_r):
+            raise ValueError(f"P_cols must be [rel_extent={rel_extent}, d_r={d_r}], got {tuple(P_cols.shape)}")
+    else:
+        r = None
+        P_cols = None
+    ns, ws_bytes = backward_plan(B, T, Hq, Hkv, D, head_splits)
+    if workspace is None:
+        workspace = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
+    dq = torch.empty_like(q)
+    dk = torch.empty_like(k)
+    dv = torch.empty_like(v)
+    dr = torch.empty(B, T, Hq, d_r, dtype=dt, device=dev) if rel_extent > 0 else None
+    _check(lib.rel_attn_backward(_ptr(q), _ptr(k), _ptr(v), _ptr(r), _ptr(P_cols), _ptr(out), _ptr(dout), _ptr(lse),
+                                 _ptr(dq), _ptr(dk), _ptr(dv), _ptr(dr), _DTYPE_CODE[dt], B, T, Hq, Hkv, D, d_r,
+                                 float(alpha), int(rel_extent), int(window), 1 if log_scale else 0, ns,
+                                 _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(dev)))
+    return dq, dk, dv, dr

@@ -21,7 +21,7 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD_DIR = os.path.join(ROOT, "_build")
 LIB = os.path.join(HERE, "librelattn.so")
 
-SOURCES = ["api.cpp", "prefill.hip", "decode.hip", "rel_logits.hip", "prologue.hip", "mx.hip"]
+SOURCES = ["api.cpp", "prefill.hip", "decode.hip", "rel_logits.hip", "prologue.hip", "mx.hip", "backward.hip"]
 ARCH = "gfx950"
 
 # Packed fp32 VALU ops are switched off for every device pass (the compiler

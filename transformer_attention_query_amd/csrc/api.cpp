@@ -259,6 +259,95 @@ int rel_attn_prologue_mx(const void* q_in, const void* k_in, const void* v_in, c
                        block_table, max_pages, num_pages, page_size, Hq, Hkv, D, conv_width, stream);
 }
 
+namespace {
+// Backward planning: the dk / dv kernel runs one workgroup per 128-key block,
+// kv head and split of the group's query heads; the split doubles until the
+// launch has a workgroup for every compute unit (or the group is exhausted).
+constexpr size_t kBwdAlign = 256;
+int bwd_splits(int B, int T, int Hq, int Hkv, int req) {
+  const int G = Hq / Hkv;
+  if (req > 0) return req;
+  const long long n_kb = (T + 127) / 128;
+  int n = 1;
+  while (n_kb * B * Hkv * n < 256 && G % (n * 2) == 0) n *= 2;
+  return n;
+}
+size_t bwd_delta_bytes(int B, int T, int Hq) {
+  return ((size_t)B * Hq * T * sizeof(float) + kBwdAlign - 1) / kBwdAlign * kBwdAlign;
+}
+size_t bwd_ws_bytes(int B, int T, int Hq, int Hkv, int n_split) {
+  const size_t part = n_split > 1 ? (size_t)n_split * 2 * B * T * Hkv * relattn::kHeadDim * sizeof(float) : 0;
+  return bwd_delta_bytes(B, T, Hq) + part;
+}
+}  // namespace
+
+int rel_attn_backward_plan(int B, int T, int Hq, int Hkv, int D, int head_splits_req, int* head_splits_out,
+                           size_t* workspace_bytes_out) {
+  if (head_splits_out == nullptr || workspace_bytes_out == nullptr)
+    return fail(RA_ERR_INVALID_ARG, "head_splits_out and workspace_bytes_out must not be NULL");
+  if (B < 0 || T < 0) return fail(RA_ERR_INVALID_ARG, "B = %d, T = %d must not be negative", B, T);
+  if (Hq <= 0 || Hkv <= 0 || Hq % Hkv != 0)
+    return fail(RA_ERR_INVALID_ARG, "Hq = %d, Hkv = %d: need positive Hq multiple of Hkv", Hq, Hkv);
+  if (D != relattn::kHeadDim) return fail(RA_ERR_UNSUPPORTED, "head dim D = %d: only 128 is supported", D);
+  if (head_splits_req < 0 || (head_splits_req > 0 && (Hq / Hkv) % head_splits_req != 0))
+    return fail(RA_ERR_INVALID_ARG, "head_splits = %d must be 0 or divide Hq / Hkv = %d", head_splits_req, Hq / Hkv);
+  const int n = bwd_splits(B, T, Hq, Hkv, head_splits_req);
+  *head_splits_out = n;
+  *workspace_bytes_out = bwd_ws_bytes(B, T, Hq, Hkv, n);
+  return ok();
+}
+
+int rel_attn_backward(const void* q, const void* k, const void* v, const void* r, const void* P_cols,
+                      const void* out, const void* dout, const float* lse, void* dq, void* dk, void* dv, void* dr,
+                      int dtype, int B, int T, int Hq, int Hkv, int D, int d_r, float alpha, int rel_extent,
+                      int window, int log_scale, int head_splits, void* workspace, size_t workspace_bytes,
+                      void* stream) {
+  int rc = check_common(dtype, B, T, Hq, Hkv, D, d_r, alpha, rel_extent, window, log_scale, "T");
+  if (rc) return rc;
+  if (dtype != RA_BF16) return fail(RA_ERR_UNSUPPORTED, "backward: only RA_BF16 is supported");
+  if ((rc = check_ptr(q, "q", true)) || (rc = check_ptr(k, "k", true)) || (rc = check_ptr(v, "v", true)) ||
+      (rc = check_ptr(out, "out", true)) || (rc = check_ptr(dout, "dout", true)) ||
+      (rc = check_ptr(lse, "lse", true)) || (rc = check_ptr(dq, "dq", true)) || (rc = check_ptr(dk, "dk", true)) ||
+      (rc = check_ptr(dv, "dv", true)) || (rc = check_ptr(r, "r", rel_extent > 0)) ||
+      (rc = check_ptr(P_cols, "P_cols", rel_extent > 0)) || (rc = check_ptr(dr, "dr", rel_extent > 0)))
+    return rc;
+  const void* ins[] = {q, k, v, r, P_cols, out, dout, lse, workspace};
+  const void* outs[] = {dq, dk, dv, dr};
+  for (const void* o : outs)
+    for (const void* i : ins)
+      if (o != nullptr && o == i) return fail(RA_ERR_INVALID_ARG, "a gradient output aliases an input or the workspace");
+  if (dq == dk || dq == dv || dk == dv || (dr != nullptr && (dr == dq || dr == dk || dr == dv)))
+    return fail(RA_ERR_INVALID_ARG, "gradient outputs alias each other");
+  if ((long long)T * Hq > 0x7fffffffLL / relattn::kHeadDim)
+    return fail(RA_ERR_UNSUPPORTED, "T * Hq = %lld too large for one launch", (long long)T * Hq);
+  if (head_splits <= 0 || (Hq / Hkv) % head_splits != 0)
+    return fail(RA_ERR_INVALID_ARG, "head_splits = %d must divide Hq / Hkv = %d (see rel_attn_backward_plan)",
+                head_splits, Hq / Hkv);
+  if (B == 0 || T == 0) return ok();
+  const size_t need = bwd_ws_bytes(B, T, Hq, Hkv, head_splits);
+  if (workspace == nullptr) return fail(RA_ERR_WORKSPACE, "workspace is NULL");
+  if ((reinterpret_cast<uintptr_t>(workspace) & (kBwdAlign - 1)) != 0)
+    return fail(RA_ERR_WORKSPACE, "workspace is not 256-byte aligned");
+  if (workspace_bytes < need)
+    return fail(RA_ERR_WORKSPACE, "workspace of %zu bytes is smaller than the %zu needed", workspace_bytes, need);
+
+  const double s = scale_of(log_scale, T);
+  relattn::BackwardArgs a;
+  a.q = q; a.k = k; a.v = v; a.r = r; a.pc = P_cols; a.out = out; a.dout = dout; a.lse = lse;
+  a.dq = dq; a.dk = dk; a.dv = dv; a.dr = rel_extent > 0 ? dr : nullptr;
+  a.delta = static_cast<float*>(workspace);
+  a.part = reinterpret_cast<float*>(static_cast<char*>(workspace) + bwd_delta_bytes(B, T, Hq));
+  a.B = B; a.T = T; a.Hq = Hq; a.Hkv = Hkv; a.d_r = rel_extent > 0 ? d_r : 0; a.E = rel_extent; a.W = window;
+  a.c1 = (float)(s * (double)alpha * 1.4426950408889634);
+  a.c2 = (float)(s * 1.4426950408889634);
+  a.sa = (float)(s * (double)alpha);
+  a.s = (float)s;
+  a.n_split = head_splits;
+  hipError_t e = relattn::launch_backward(a, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(RA_ERR_HIP, "backward launch failed: %s", hipGetErrorString(e));
+  return ok();
+}
+
 int rel_attn_decode_plan(int B, int L, int Hq, int Hkv, int D, int num_splits_req, int window, int rel_extent,
                          int* num_splits_out, size_t* workspace_bytes_out) {
   if (num_splits_out == nullptr || workspace_bytes_out == nullptr)

@@ -105,6 +105,28 @@ struct RelLogitsArgs {
   int out_cols, out_stride, rev_base;
 };
 
+// Backward launch description (bf16; see rel_attn_backward).  c1 and c2 as
+// in PrefillArgs; sa = s * alpha scales dq and dk, s scales dr.
+struct BackwardArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  const void* r;
+  const void* pc;    // P_cols [E, d_r]
+  const void* out;
+  const void* dout;
+  const float* lse;  // [B, Hq, T], natural log
+  void* dq;
+  void* dk;
+  void* dv;
+  void* dr;          // may be null
+  float* delta;      // workspace [B, Hq, T]
+  float* part;       // workspace [n_split][2][B, T, Hkv, D] when n_split > 1
+  int B, T, Hq, Hkv, d_r, E, W;
+  float c1, c2, sa, s;
+  int n_split;       // the dk / dv kernel's split of each group's query heads
+};
+
 // Decode planning shared by rel_attn_decode_plan and rel_attn_decode.
 struct DecodePlan {
   int n_split;
@@ -130,6 +152,7 @@ hipError_t launch_decode_paged(int dtype, const DecodeArgs& a, hipStream_t strea
 hipError_t launch_decode_mx(const DecodeArgs& a, hipStream_t stream);
 // rows of D = 128 values (dtype) -> E4M3 codes [n_rows, 128] and E8M0 scales [n_rows, 4]
 hipError_t launch_mx_quantize(int dtype, const void* x, void* codes, void* scales, long long n_rows, hipStream_t stream);
+hipError_t launch_backward(const BackwardArgs& a, hipStream_t stream);
 hipError_t launch_rel_logits(int dtype, const RelLogitsArgs& a, hipStream_t stream);
 
 }  // namespace relattn
