@@ -34,6 +34,7 @@ DECODE_WORKLOAD = "decode_64x8k"
 EXTEND_WORKLOAD = "extend_4x1k_8k_paged"
 PAGED_DECODE_WORKLOAD = "decode_paged_64x8k"
 PROLOGUE_WORKLOAD = "prologue_8k"
+BACKWARD_WORKLOAD = "swa_backward_8k"
 PREFILL_KERNEL = "prefill_dma_kernel"  # the bf16 path for eight or more query heads per kv head
 DECODE_KERNEL = "decode_split_kernel"
 
@@ -52,6 +53,15 @@ def prefill_work(T: int, Hq: int, D: int, d_r: int, E: int, W: int, rows=None):
         pairs += vis
         rel += min(vis, E)
     return Hq * (pairs * 4 * D + rel * 2 * d_r), Hq * pairs, Hq * rel
+
+
+def backward_work(T: int, Hq: int, D: int, d_r: int, E: int, W: int):
+    """Algorithmic flops of a backward: 10*D per visible (i, j, h) pair (q.k
+    recomputed, dout.v, and the dq, dk and dv products) plus 4*d_r per needed
+    relative-logit entry (r.P recomputed, and dr).  The forward's convention
+    otherwise: masked pairs, skipped tiles and the softmax are not counted."""
+    _, pairs, rel = prefill_work(T, Hq, D, d_r, E, W)
+    return pairs * 10 * D + rel * 4 * d_r
 
 
 def decode_bytes(B: int, L: int, Hq: int, Hkv: int, D: int, d_r: int, E: int, W: int, elem: int = 2):
@@ -311,6 +321,38 @@ def bench_prologue(steps: int, warmup: int):
     return w, nbytes, total_ms / steps, kernel_ms
 
 
+def bench_backward(steps: int, warmup: int):
+    """The backward of the 8K sliding-window layer: dq, dk, dv and dr from the
+    forward's out and lse (computed once, outside the timed region)."""
+    import torch
+    import transformer_attention_query_amd as ra
+    from transformer_attention_query_amd import inputs as tinputs
+
+    w = tinputs.WORKLOADS[BACKWARD_WORKLOAD]
+    x = {n: t.cuda() for n, t in tinputs.make_inputs(w, seed=0).items()}
+    out, lse = ra.prefill(x["q"], x["k"], x["v"], x["r"], x["P_cols"], w.alpha, w.E, w.W, w.log_scale)
+    ns, ws_bytes = ra.backward_plan(w.B, w.T, w.Hq, w.Hkv, w.D)
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device="cuda")
+    dq, dk, dv = torch.empty_like(x["q"]), torch.empty_like(x["k"]), torch.empty_like(x["v"])
+    dr = torch.empty_like(x["r"])
+    stream = torch.cuda.current_stream()
+    lib = ra.load_library()
+    args = (x["q"].data_ptr(), x["k"].data_ptr(), x["v"].data_ptr(), x["r"].data_ptr(), x["P_cols"].data_ptr(),
+            out.data_ptr(), x["dout"].data_ptr(), lse.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(),
+            dr.data_ptr(), 1, w.B, w.T, w.Hq, w.Hkv, w.D, w.d_r, w.alpha, w.E, w.W, 1 if w.log_scale else 0, ns,
+            ws.data_ptr(), ws_bytes, stream.cuda_stream)
+    fn = lib.rel_attn_backward
+
+    def step(_i):
+        fn(*args)
+
+    total_ms, per = _time_launches(step, steps, warmup, stream)
+    if fn(*args) != 0:
+        raise RuntimeError("backward call failed: " + lib.rel_attn_last_error().decode())
+    flops = backward_work(w.T, w.Hq, w.D, w.d_r, w.E, w.W) * w.B
+    return w, flops, total_ms / steps, sum(per) / len(per), ns
+
+
 def cpu_baseline(target_s: float = 15.0):
     """The fp64 oracle, as it stands, on query rows of the prefill workload."""
     import torch
@@ -361,6 +403,7 @@ def main():
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-extend", action="store_true")
     ap.add_argument("--no-prologue", action="store_true")
+    ap.add_argument("--no-backward", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
@@ -468,6 +511,19 @@ def main():
                                          "traffic": _traffic("prologue_kernel",
                                                              _src_hash("prologue.hip", "device_common.hpp", "mx_common.hpp")),
                                          "avg_launch_us": round(g_kernel_ms * 1e3, 2)}}
+    if not args.no_backward:
+        bw, b_flops, b_ms, b_kernel_ms, b_ns = bench_backward(args.steps, args.warmup)
+        print(f"# backward {bw.name}: {b_ms * 1e3:.1f} us/step ({b_ns} head splits)", file=sys.stderr, flush=True)
+        b_ach = b_flops / (b_kernel_ms * 1e-3) / 1e12
+        line["backward"] = {"workload": bw.name, "value": round(b_flops / (b_ms * 1e-3) / 1e12, 2),
+                            "unit": "TFLOP/s", "ms_per_step": round(b_ms, 5), "algorithmic_flops": b_flops,
+                            "head_splits": b_ns,
+                            "config": {"B": bw.B, "T": bw.T, "Hq": bw.Hq, "Hkv": bw.Hkv, "D": bw.D, "d_r": bw.d_r,
+                                       "rel_extent": bw.E, "window": bw.W, "log_scale": bw.log_scale},
+                            "roofline": {"bound": "mfma", "kernel": "bwd_dq_kernel+bwd_dkdv_kernel (+delta, reduce)",
+                                         "achieved": round(b_ach, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                                         "frac": round(b_ach / PEAK_BF16_TFLOPS, 4), "traffic": None,
+                                         "avg_launch_us": round(b_kernel_ms * 1e3, 2)}}
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline()
     print(json.dumps(line), flush=True)
