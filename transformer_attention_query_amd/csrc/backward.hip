@@ -250,6 +250,22 @@ __global__ __launch_bounds__(THREADS, 1) void bwd_dq_kernel(BackwardArgs p, int 
   float* rs = Rs + w * N * LS;
   f32x16 rprev = zero16();
   int rlast = INT_MIN;
+  // dr runs one distance chunk per tile: chunk c of a tile takes its entries
+  // with offset delta <= a from this tile's dS and those with delta > a from
+  // the previous tile's (where it was chunk c-1), carried here as bf16
+  // operands; glast names the chunk the carry belongs to.
+  bf16x8 gcar[2];
+  gcar[0] = zero8<__bf16>();
+  gcar[1] = zero8<__bf16>();
+  int glast = INT_MIN;
+  auto dr_chunk = [&](int k, const bf16x8* g) {
+    const __bf16* ps = slot(k);
+#pragma unroll
+    for (int c16 = 0; c16 < 2; ++c16)
+#pragma unroll
+      for (int cb = 0; cb < kMaxDr / 32; ++cb)
+        if (cb < (d_r + 31) / 32) mma32(frag_tr<XS>(ps, c16, cb, lane), g[c16], dr[cb]);
+  };
 
   for (int kt = kt_lo; kt <= kt_hi; ++kt) {
     const int j0 = kt * N;
@@ -261,8 +277,15 @@ __global__ __launch_bounds__(THREADS, 1) void bwd_dq_kernel(BackwardArgs p, int 
     pch.fetch(pcg, knew, E, d_r, tid);
 
     const bool wdead = qw0 >= T || j0 > qw0 + 31 || (W > 0 && qw0 - (j0 + N - 1) >= W);
+    const bool wband = !wdead && E > 0 && max(0, qw0 - (j0 + N - 1)) < E;
+    if (!wband && glast != INT_MIN) {
+      // the carried chunk's other entries fall on this tile, which adds none
+      // (tiles after a band tile are band tiles or entirely masked); the ring
+      // still holds the chunk (it is this tile's chunk c)
+      dr_chunk(glast, gcar);
+      glast = INT_MIN;
+    }
     if (!wdead) {
-      const bool wband = E > 0 && max(0, qw0 - (j0 + N - 1)) < E;
       const bool wmask = (j0 + N - 1 > qw0) || (W > 0 && qw0 + 31 - j0 >= W);
       const int c = c0 + qb;
 
@@ -351,27 +374,27 @@ __global__ __launch_bounds__(THREADS, 1) void bwd_dq_kernel(BackwardArgs p, int 
             *reinterpret_cast<f32x2*>(gs + 8 * g4 + 4 * h2 + e) = x;
           }
         wave_lds_fence();
-        // dr^T += P_cols^T G^T over chunks c-1 (cl = 0) and c (cl = 1): k-slot
-        // t of step c16 is distance 32(c-1+cl) + 16 c16 + 8(t/4) + 4 h2 + t%4,
-        // which is key b = a + 32(1-cl) - (16 c16 + 8(t/4) + 4 h2 + t%4)
+        // dr^T += P_cols^T G^T, G[a][32k + o] = dS[a][key a + 32(c - k) - o]:
+        // k-slot t of step c16 is offset o = 16 c16 + 8(t/4) + 4 h2 + t%4 of a
+        // chunk.  Offsets o <= a of chunk c read key a - o of this tile;
+        // offsets o > a read key a + 32 - o, which belongs to chunk c-1 here
+        // (chunk c's are in the carry).  Both are key (a - o) mod 32.
+        const bool carry_ok = glast == c;
+        bf16x8 gb[2], gn[2];
 #pragma unroll
-        for (int cl = 0; cl < 2; ++cl) {
-          const __bf16* ps = slot(c - 1 + cl);
+        for (int c16 = 0; c16 < 2; ++c16)
 #pragma unroll
-          for (int c16 = 0; c16 < 2; ++c16) {
-            bf16x8 gb;
-#pragma unroll
-            for (int t = 0; t < 8; ++t) {
-              const int bk = a + 32 * (1 - cl) - (16 * c16 + 8 * (t >> 2) + 4 * h2 + (t & 3));
-              const bool ok = bk >= 0 && bk < N;
-              const float x = gs[min(max(bk, 0), N - 1)];
-              gb[t] = __bf16(ok ? x : 0.0f);
-            }
-#pragma unroll
-            for (int cb = 0; cb < kMaxDr / 32; ++cb)
-              if (cb < (d_r + 31) / 32) mma32(frag_tr<XS>(ps, c16, cb, lane), gb, dr[cb]);
+          for (int t = 0; t < 8; ++t) {
+            const int o = 16 * c16 + 8 * (t >> 2) + 4 * h2 + (t & 3);
+            const __bf16 x = __bf16(gs[(a - o) & (N - 1)]);
+            const bool low = o <= a;
+            gb[c16][t] = low ? x : (carry_ok ? gcar[c16][t] : __bf16(0.0f));
+            gn[c16][t] = low ? __bf16(0.0f) : x;
           }
-        }
+        dr_chunk(c, gb);
+        gcar[0] = gn[0];
+        gcar[1] = gn[1];
+        glast = c - 1;
         wave_lds_fence();
       }
     }
@@ -382,6 +405,8 @@ __global__ __launch_bounds__(THREADS, 1) void bwd_dq_kernel(BackwardArgs p, int 
       pch.store<XS>(slot(knew), tid);
     }
   }
+
+  if (glast != INT_MIN) dr_chunk(glast, gcar);  // the last carry (no further tile adds to it)
 
   // ---- epilogue: dq = s alpha dq^T^T, dr = s dr^T^T through a per-wave LDS
   // staging tile, written back as whole rows
