@@ -522,7 +522,8 @@ def main():
                                        "rel_extent": bw.E, "window": bw.W, "log_scale": bw.log_scale},
                             "roofline": {"bound": "mfma", "kernel": "bwd_dq_kernel+bwd_dkdv_kernel (+delta, reduce)",
                                          "achieved": round(b_ach, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                                         "frac": round(b_ach / PEAK_BF16_TFLOPS, 4), "traffic": None,
+                                         "frac": round(b_ach / PEAK_BF16_TFLOPS, 4),
+                                         "traffic": _traffic("backward", _src_hash("backward.hip", "device_common.hpp")),
                                          "avg_launch_us": round(b_kernel_ms * 1e3, 2)}}
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline()

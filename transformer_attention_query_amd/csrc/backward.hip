@@ -471,14 +471,25 @@ __global__ __launch_bounds__(THREADS, 1) void bwd_dkdv_kernel(BackwardArgs p, in
   const int n_split = p.n_split, hps = G / n_split;
   const int item = blockIdx.x;
   if (item >= n_items) return;
+  // Under the causal mask the blocks run longest first (block 0 sees every
+  // query).  In a sliding-window layer every block has the same work, and
+  // consecutive blocks of one (batch, kv head, split) go to one XCD
+  // (workgroup i runs on XCD i % 8), so the query tiles they share meet in
+  // that XCD's L2.
   const int per_kb = p.B * Hkv * n_split;
-  const int kb = item / per_kb;  // most queries first under the causal mask
-  int rest = item % per_kb;
+  int kb, rest;
+  if (W > 0 && n_items % 8 == 0) {
+    const int lin = (item % 8) * (n_items / 8) + item / 8;
+    kb = lin % n_kb;
+    rest = lin / n_kb;
+  } else {
+    kb = item / per_kb;
+    rest = item % per_kb;
+  }
   const int hs = rest % n_split;
   rest /= n_split;
   const int kvh = rest % Hkv;
   const int b = rest / Hkv;
-  (void)n_kb;
 
   const int tid = threadIdx.x;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -551,26 +562,44 @@ __global__ __launch_bounds__(THREADS, 1) void bwd_dkdv_kernel(BackwardArgs p, in
   auto slot = [&](int k) { return Pr + size_t(k & (DkvLds::RING - 1)) * N * RS; };
   PChunk pch;
 
-  {
-    fetch_step(it_lo, h_first);
-    const int cb = it_lo - j0 / N;
+  auto fill_ring = [&](int it) {  // the WAVES + 1 chunks of query tile it
+    const int cb = it - j0 / N;
     for (int k = cb - WAVES; k <= cb; ++k) {
       pch.fetch(pcg, k, E, d_r, tid);
       pch.store<RS>(slot(k), tid);
     }
-    store_step();
-  }
+  };
+
+  // Order of the query tiles.  In a sliding-window layer a full block sees
+  // n_rot tiles; step sg takes the block's tile congruent to sg modulo n_rot,
+  // so at any step all the blocks that share a tile take it together (and
+  // its rows are read from L2 once for them).  A block cut short by the end of
+  // the sequence skips the steps whose tile lies past it.  Causal: ascending.
+  const int n_rot = W > 0 ? (N * WAVES - 2 + W) / N + 1 : it_hi - it_lo + 1;
+  auto tile_at = [&](int sg) { return W > 0 ? it_lo + pos_mod(sg - it_lo, n_rot) : it_lo + sg; };
+  auto next_valid = [&](int sg) {
+    while (sg < n_rot && tile_at(sg) > it_hi) ++sg;
+    return sg;
+  };
+  int sg = next_valid(0);
+  int it = tile_at(sg);
+  fetch_step(it, h_first);
+  fill_ring(it);
+  store_step();
 
   float* rs = Rs + w * N * LS;
-  for (int it = it_lo; it <= it_hi; ++it) {
+  while (sg < n_rot) {
     const int i0 = it * N;
+    const int sg_next = next_valid(sg + 1);
+    const int it_next = sg_next < n_rot ? tile_at(sg_next) : -1;
+    const bool adjacent = it_next == it + 1;  // the ring then takes one new chunk
     for (int hh = 0; hh < hps; ++hh) {
       __syncthreads();
       const bool last_h = hh + 1 == hps;
-      const bool more = !(last_h && it == it_hi);
-      if (more) fetch_step(last_h ? it + 1 : it, h_first + (last_h ? 0 : hh + 1));
-      const int knew = it + 1 - j0 / N;  // chunk the next query tile adds
-      if (last_h && more) pch.fetch(pcg, knew, E, d_r, tid);
+      const bool more = !(last_h && it_next < 0);
+      if (more) fetch_step(last_h ? it_next : it, h_first + (last_h ? 0 : hh + 1));
+      const int knew = it_next - j0 / N;  // chunk the next query tile adds
+      if (last_h && more && adjacent) pch.fetch(pcg, knew, E, d_r, tid);
 
       const bool wdead = j0w >= T || i0 + 31 < j0w || (W > 0 && i0 - (j0w + N - 1) >= W);
       if (!wdead) {
@@ -667,8 +696,13 @@ __global__ __launch_bounds__(THREADS, 1) void bwd_dkdv_kernel(BackwardArgs p, in
 
       __syncthreads();
       if (more) store_step();
-      if (last_h && more) pch.store<RS>(slot(knew), tid);
+      if (last_h && more) {
+        if (adjacent) pch.store<RS>(slot(knew), tid);
+        else fill_ring(it_next);
+      }
     }
+    sg = sg_next;
+    it = it_next;
   }
 
   // ---- epilogue: rows of dk (scaled by s alpha) and dv, bf16 or fp32 partials
