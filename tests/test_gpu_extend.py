@@ -94,6 +94,7 @@ DECODE_CASES = [
     ("g8_forced_splits_short_seq", "bf16", [2050, 40], 16, 2, 128, 1024, 0, False, 128, 8),
     ("mha_E0", "bf16", [129, 257], 2, 2, 16, 0, 0, False, 32, 0),
     ("fp32_paged", "fp32", [257, 1, 90], 4, 2, 32, 40, 0, False, 32, 0),
+    ("g8_one_split_mixed", "bf16", [1, 900, 2000], 16, 2, 128, 256, 0, False, 64, 1),
 ]
 
 

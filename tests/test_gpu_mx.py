@@ -64,6 +64,7 @@ CASES = [
     ("g8_log_scale", 1, 5000, 8, 1, 32, 100, 0, True, 0),
     ("mha_E0", 2, 333, 4, 4, 32, 0, 0, False, 3),
     ("g16_short", 4, 65, 16, 1, 64, 64, 0, False, 0),
+    ("g8_one_split", 2, 1500, 16, 2, 128, 512, 0, False, 1),
 ]
 
 

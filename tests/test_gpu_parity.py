@@ -135,6 +135,9 @@ DECODE_CASES = [
     ("E_beyond_L", "bf16", 1, 300, 16, 2, 128, 1024, 0, False, 2),
     ("fp32", "fp32", 2, 513, 8, 2, 32, 64, 0, False, 0),
     ("fp32_W50_s5", "fp32", 1, 777, 4, 1, 48, 100, 50, False, 5),
+    # one split: the split kernel normalises and writes the output itself
+    ("L2000_s1", "bf16", 2, 2000, 16, 2, 128, 1024, 0, False, 1),
+    ("fp32_L600_W200_s1", "fp32", 1, 600, 8, 2, 32, 64, 200, False, 1),
 ]
 
 

@@ -11,7 +11,8 @@
 // interleaved 32-key steps, and it streams its chunk of K and V exactly once
 // for every query head of the group.  The
 // partial softmax states (unnormalised o, running max m, sum l) go to the
-// caller's workspace and a second kernel merges them by log-sum-exp.
+// caller's workspace and a second kernel merges them by log-sum-exp (with
+// a single split the workgroup normalises and writes the output itself).
 //
 // Three launches on the caller's stream:
 //   1. rel_logits_kernel writes, per (sequence, query head), the bias row
@@ -476,6 +477,14 @@ __global__ __launch_bounds__(kDecWaves * 64, sizeof(T) == 2 ? 2 : 1) void decode
   }
   const size_t n_bh = size_t(p.B) * Hq;
   const size_t bh = size_t(b) * Hq + kvh * G + hin2;
+  if (p.n_split == 1) {  // the only split: normalise and write the output here
+    const float inv = 1.0f / wsum_l;
+    T* const out_row = static_cast<T*>(p.out) + bh * D + d0;
+    st4_f32<T>(out_row, acc[0] * inv, acc[1] * inv, acc[2] * inv, acc[3] * inv);
+    st4_f32<T>(out_row + 4, acc[4] * inv, acc[5] * inv, acc[6] * inv, acc[7] * inv);
+    if (p.lse != nullptr && d0 == 0) p.lse[bh] = (M + log2f(wsum_l)) * kLn2;
+    return;
+  }
   float* ws_o = p.ws + (size_t(split) * n_bh + bh) * D;
   float* ws_m = p.ws + size_t(p.n_split) * n_bh * D;
   float* ws_l = ws_m + size_t(p.n_split) * n_bh;
@@ -616,7 +625,7 @@ hipError_t launch_decode_t(const DecodeArgs& a, hipStream_t stream) {
   if (grid > 0x7fffffffLL) return hipErrorInvalidConfiguration;
   hipLaunchKernelGGL((decode_split_kernel<T, PAGED, MX>), dim3((unsigned)grid), dim3(kDecWaves * 64), 0, stream, a);
   hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
+  if (e != hipSuccess || a.n_split == 1) return e;
   if (a.n_split <= kMergeSmallSplits) {
     const long long threads = (long long)a.B * a.Hq * (kHeadDim / 4);
     hipLaunchKernelGGL(decode_merge_small_kernel<T>, dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, stream, a);
