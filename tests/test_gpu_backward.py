@@ -140,3 +140,17 @@ def test_backward_swa_8k_workload_sampled():
     rows = [0, 1, 33, 1023, 1024, 1025, 4000, 8190, 8191]
     keys = [0, 31, 32, 1000, 4096, 7168, 8191]
     _check("swa_backward_8k", x, got, w.alpha, w.E, w.W, w.log_scale, rows=rows, keys=keys)
+
+
+def test_backward_full_causal_32k_log_sampled():
+    """The 32K full-causal log-scale shape (B = 2, s = 1.25; the dk/dv kernel
+    then runs without head splits, longest blocks first), on sampled query
+    rows and on keys near the end, which few queries see."""
+    B, T, Hq, Hkv, d_r, E = 2, 32768, 16, 2, 128, 1024
+    x = tinputs.make_backward_inputs(B, T, Hq, Hkv, 128, d_r, E, "bf16", seed=41)
+    ns, _ = ra.backward_plan(B, T, Hq, Hkv)
+    assert ns == 1
+    got = _gpu_backward(x, ALPHA, E, 0, True)
+    rows = [0, 1, 1023, 1024, 20000, 32766, 32767]
+    keys = [32700, 32735, 32767]
+    _check("causal_32k_log", x, got, ALPHA, E, 0, True, rows=rows, keys=keys)
