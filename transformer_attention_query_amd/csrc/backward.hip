@@ -531,21 +531,29 @@ __global__ __launch_bounds__(THREADS, 1) void bwd_dkdv_kernel(BackwardArgs p, in
   // staged step (query tile it, head h): q, dout and r rows, lse2 and delta
   bf16x8 qpre[VECS], dpre[VECS], rpre[VECS];
   float lpre = 0.0f;
+  // Every load is issued unconditionally from a clamped address inside its
+  // tensor (rows past T read row T-1, columns past d_r the row's last piece,
+  // r without bias reads q); rows past T and columns past d_r are zeroed when
+  // stored, so no load sits behind a branch.
+  unsigned pre_ok = 0;  // bit i: vector i's row is a query; bit 8 + i: its r piece is needed
+  const float* lsrc = tid < N ? p.lse : p.delta;
   auto fetch_step = [&](int it, int h) {
+    pre_ok = 0;
 #pragma unroll
     for (int i = 0; i < VECS; ++i) {
       const int vid = tid + i * THREADS;
       const int qi = it * N + (vid >> 4), c8 = vid & 15;
       const bool ok = qi < T;
-      const size_t row = (size_t(b) * T + (ok ? qi : T - 1)) * Hq + h;
-      qpre[i] = ld8_or_zero<__bf16>(qg + row * D + 8 * c8, ok);
-      dpre[i] = ld8_or_zero<__bf16>(dog + row * D + 8 * c8, ok);
-      rpre[i] = ld8_or_zero<__bf16>(rg + row * d_r + 8 * min(c8, max(d_r / 8 - 1, 0)), ok && E > 0 && c8 < d_r / 8);
+      pre_ok |= (unsigned(ok) << i) | (unsigned(ok && E > 0 && c8 < d_r / 8) << (8 + i));
+      const size_t row = (size_t(b) * T + min(qi, T - 1)) * Hq + h;
+      qpre[i] = ld8<__bf16>(qg + row * D + 8 * c8);
+      dpre[i] = ld8<__bf16>(dog + row * D + 8 * c8);
+      rpre[i] = ld8<__bf16>(rg + (E > 0 ? row * d_r + 8 * min(c8, max(d_r / 8 - 1, 0)) : row * D + 8 * c8));
     }
     if (tid < 2 * N) {
       const int qi = it * N + (tid & (N - 1));
-      const size_t li = (size_t(b) * Hq + h) * T + min(qi, T - 1);
-      lpre = qi < T ? (tid < N ? p.lse[li] * kLog2e : p.delta[li]) : 0.0f;
+      lpre = lsrc[(size_t(b) * Hq + h) * T + min(qi, T - 1)];
+      pre_ok |= unsigned(qi < T) << 16;
     }
   };
   auto store_step = [&]() {
@@ -553,11 +561,12 @@ __global__ __launch_bounds__(THREADS, 1) void bwd_dkdv_kernel(BackwardArgs p, in
     for (int i = 0; i < VECS; ++i) {
       const int vid = tid + i * THREADS;
       const int row = vid >> 4, c8 = vid & 15;
-      st8<__bf16>(Qs + row * XS + c8 * 8, qpre[i]);
-      st8<__bf16>(Ds + row * XS + c8 * 8, dpre[i]);
-      st8<__bf16>(Rr + row * RS + c8 * 8, rpre[i]);
+      const bool ok = (pre_ok >> i) & 1u, rok = (pre_ok >> (8 + i)) & 1u;
+      st8<__bf16>(Qs + row * XS + c8 * 8, ok ? qpre[i] : zero8<__bf16>());
+      st8<__bf16>(Ds + row * XS + c8 * 8, ok ? dpre[i] : zero8<__bf16>());
+      st8<__bf16>(Rr + row * RS + c8 * 8, rok ? rpre[i] : zero8<__bf16>());
     }
-    if (tid < 2 * N) Ls[tid] = lpre;
+    if (tid < 2 * N) Ls[tid] = ((pre_ok >> 16) & 1u) ? (tid < N ? lpre * kLog2e : lpre) : 0.0f;
   };
   auto slot = [&](int k) { return Pr + size_t(k & (DkvLds::RING - 1)) * N * RS; };
   PChunk pch;
