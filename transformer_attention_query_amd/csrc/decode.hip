@@ -142,7 +142,8 @@ struct DecReduce {
 // PAGED: the paged form (rel_attn_decode_paged): per-sequence cache lengths
 // kv_len[b] (at most L), pages of page_size keys (a multiple of 32) through a
 // block table, steps aligned to 32 keys so each lies in one page, and bias
-// rows in distance order scaled by log2(e) only (s applied here per sequence).
+// rows in distance order scaled by log2(e) only (s applied here per sequence),
+// shifted per sequence so that each step's 4-key groups are aligned vectors.
 // MX: MXFP8 caches (rel_attn_decode_mx); q is quantised to MXFP8 the same way
 // for the score product, V is dequantised to bf16 for PV.
 template <typename T, bool PAGED, bool MX = false>
@@ -318,15 +319,25 @@ __global__ __launch_bounds__(kDecWaves * 64, sizeof(T) == 2 ? 2 : 1) void decode
       }
     }
     if constexpr (PAGED) {
-      // bias of key j at entry d = Lb-1-j of the distance-ordered row (0 past E)
+      // Bias of key j at distance d = Lb-1-j: the row is in distance order
+      // from entry sh = (4 - Lb % 4) % 4 on (zeros from distance E to the row's
+      // end), so keys j0+16*blk+4g .. +3 are the four entries from
+      // Lb-4-(j0+16*blk+4g)+sh, 16-byte aligned, in reverse order.  Clamping
+      // keeps the read inside the row: a group clamped to the end is at
+      // distances >= E (zeros); one clamped to the start holds only keys past
+      // Lb-1, which are masked.
+      if (p.E > 0) {
+        const int sh = (4 - (Lb & 3)) & 3;
 #pragma unroll
-      for (int blk = 0; blk < 2; ++blk)
-#pragma unroll
-        for (int v = 0; v < 4; ++v) {
-          const int d = Lb - 1 - (j0 + 16 * blk + 4 * g + v);
-          const float x = rlrow[min(max(d, 0), max(p.E - 1, 0))];
-          ch.rl[blk][v] = (d >= 0 && d < p.E) ? x : 0.0f;
+        for (int blk = 0; blk < 2; ++blk) {
+          const int idx = min(max(Lb - 4 - (j0 + 16 * blk + 4 * g) + sh, 0), p.rl_stride - 4);
+          const f32x4 t = *reinterpret_cast<const f32x4*>(rlrow + idx);
+          ch.rl[blk] = f32x4{t[3], t[2], t[1], t[0]};
         }
+      } else {
+        ch.rl[0] = zero4();
+        ch.rl[1] = zero4();
+      }
     } else {
       // Bias of keys j0+16*blk+4g .. +3: entries j - L + rl_base.  Clamping
       // keeps the read inside the row; a clamped key is at distance >= E, whose
@@ -604,7 +615,9 @@ hipError_t launch_decode_t(const DecodeArgs& a, hipStream_t stream) {
     // bias rows of every (sequence, head): s * log2(e) * r.P[:, d], stored
     // reversed so that key j finds its distance L-1-j at entry j - L + rl_base
     // (all zeros when E == 0).  Paged form: log2(e) * r.P[:, d] in distance
-    // order (the lengths, hence s, are per sequence and known on the device).
+    // order from entry (4 - Lb % 4) % 4 of each row, zeros past E (the
+    // lengths, hence s and that shift, are per sequence and known on the
+    // device).
     RelLogitsArgs ra;
     ra.r = a.r;
     ra.pc = a.pc;
@@ -613,7 +626,12 @@ hipError_t launch_decode_t(const DecodeArgs& a, hipStream_t stream) {
     ra.d_r = a.d_r;
     ra.E = a.E;
     ra.s = PAGED ? 1.4426950408889634f : a.c2;
-    ra.out_cols = PAGED ? a.E : a.rl_stride;
+    ra.out_cols = a.rl_stride;
+    if (PAGED) {
+      ra.shift_len = a.kv_len;
+      ra.shift_hq = a.Hq;
+      ra.shift_lmax = a.L < a.max_pages * a.page_size ? a.L : a.max_pages * a.page_size;
+    }
     ra.out_stride = a.rl_stride;
     ra.rev_base = PAGED ? 0 : a.rl_base;
     if (!PAGED || a.E > 0) {

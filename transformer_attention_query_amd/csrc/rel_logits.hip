@@ -60,7 +60,12 @@ __global__ __launch_bounds__(kRlWaves * 64) void rel_logits_kernel(RelLogitsArgs
 #pragma unroll
     for (int v = 0; v < 16; ++v) {
       const long long row = row0 + 8 * (v >> 2) + 4 * h2 + (v & 3);
-      if (row < p.n_rows) p.out[row * p.out_stride + col] = acc[v] * p.s;
+      if (row < p.n_rows) {
+        const int sh = p.shift_len != nullptr
+                           ? (4 - (min(max(p.shift_len[row / p.shift_hq], 1), p.shift_lmax) & 3)) & 3
+                           : 0;
+        if (col + sh < p.out_stride) p.out[row * p.out_stride + col + sh] = acc[v] * p.s;
+      }
     }
   }
 }

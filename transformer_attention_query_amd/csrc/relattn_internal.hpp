@@ -103,6 +103,12 @@ struct RelLogitsArgs {
   int d_r, E;
   float s;
   int out_cols, out_stride, rev_base;
+  // optional per-row shift of the output columns: row r is written from
+  // column sh = (4 - Lb % 4) % 4 on, Lb = clamp(shift_len[r / shift_hq], 1,
+  // shift_lmax), columns shifted past out_stride dropped (paged decode:
+  // aligns each sequence's bias groups)
+  const int* shift_len = nullptr;
+  int shift_hq = 1, shift_lmax = 1;
 };
 
 // Backward launch description (bf16; see rel_attn_backward).  c1 and c2 as
