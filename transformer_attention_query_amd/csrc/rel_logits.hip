@@ -57,14 +57,25 @@ __global__ __launch_bounds__(kRlWaves * 64) void rel_logits_kernel(RelLogitsArgs
   }
   // accumulator v of lane (h2, a): row 8*(v/4) + 4*h2 + v%4, column a
   if (col < p.out_cols) {
+    // Per-row shift: rows 4k .. 4k+3 belong to one sequence when shift_hq is
+    // a multiple of 4, so a lane looks its shift up once per group of four.
+    const bool grouped = p.shift_hq % 4 == 0;
+    auto shift_of = [&](long long row) {
+      if (p.shift_len == nullptr) return 0;
+      const long long rr = min(row, p.n_rows - 1);
+      return (4 - (min(max(p.shift_len[rr / p.shift_hq], 1), p.shift_lmax) & 3)) & 3;
+    };
 #pragma unroll
-    for (int v = 0; v < 16; ++v) {
-      const long long row = row0 + 8 * (v >> 2) + 4 * h2 + (v & 3);
-      if (row < p.n_rows) {
-        const int sh = p.shift_len != nullptr
-                           ? (4 - (min(max(p.shift_len[row / p.shift_hq], 1), p.shift_lmax) & 3)) & 3
-                           : 0;
-        if (col + sh < p.out_stride) p.out[row * p.out_stride + col + sh] = acc[v] * p.s;
+    for (int g4 = 0; g4 < 4; ++g4) {
+      const long long rg = row0 + 8 * g4 + 4 * h2;
+      const int sh_g = grouped ? shift_of(rg) : 0;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const long long row = rg + e;
+        if (row < p.n_rows) {
+          const int sh = grouped ? sh_g : shift_of(row);
+          if (col + sh < p.out_stride) p.out[row * p.out_stride + col + sh] = acc[4 * g4 + e] * p.s;
+        }
       }
     }
   }
