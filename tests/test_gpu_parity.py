@@ -138,6 +138,11 @@ DECODE_CASES = [
     # one split: the split kernel normalises and writes the output itself
     ("L2000_s1", "bf16", 2, 2000, 16, 2, 128, 1024, 0, False, 1),
     ("fp32_L600_W200_s1", "fp32", 1, 600, 8, 2, 32, 64, 200, False, 1),
+    # bias keys [2800, 3000) begin 12 keys before the end of the middle split
+    ("L3000_W700_E200_s3", "bf16", 2, 3000, 16, 2, 128, 200, 700, False, 3),
+    # 16 heads per kv head and E = 2048: the in-kernel bias region would not
+    # fit the LDS budget, so the bias rows come from the pre-pass
+    ("G16_E2048_prepass", "bf16", 1, 3000, 16, 1, 128, 2048, 0, False, 1),
 ]
 
 

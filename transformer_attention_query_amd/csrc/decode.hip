@@ -139,6 +139,11 @@ struct DecReduce {
   float o[kDecWaves][16][kHeadDim];
 };
 
+template <typename T>
+constexpr size_t dec_static_lds() {
+  return kDecWaves * DecV<T>::BYTES > sizeof(DecReduce) ? kDecWaves * DecV<T>::BYTES : sizeof(DecReduce);
+}
+
 // PAGED: the paged form (rel_attn_decode_paged): per-sequence cache lengths
 // kv_len[b] (at most L), pages of page_size keys (a multiple of 32) through a
 // block table, steps aligned to 32 keys so each lies in one page, and bias
@@ -146,14 +151,22 @@ struct DecReduce {
 // shifted per sequence so that each step's 4-key groups are aligned vectors.
 // MX: MXFP8 caches (rel_attn_decode_mx); q is quantised to MXFP8 the same way
 // for the score product, V is dequantised to bf16 for PV.
-template <typename T, bool PAGED, bool MX = false>
+// BL: the bias is made in the kernel.  A workgroup whose split holds keys
+// within E of the query computes s * log2(e) * r.P[:, Lb-1-j] for those keys
+// and its query heads once, before its loop (16-key blocks, one MFMA chain
+// per block over d_r), into a dynamic LDS region [heads][bias_ld]; its steps
+// read the bias from there.  Workgroups of other splits load no bias at all
+// and no pre-pass launch is needed.  Without BL the bias comes from the
+// pre-pass rows in the workspace.
+template <typename T, bool PAGED, bool MX = false, bool BL = false>
 __global__ __launch_bounds__(kDecWaves * 64, sizeof(T) == 2 ? 2 : 1) void decode_split_kernel(DecodeArgs p) {
   static_assert(!MX || sizeof(T) == 2, "MXFP8 caches come with bf16 queries");
   using CH = typename Pick<MX, ChunkMX, Chunk<T>>::type;
   using VS = DecV<T>;
   constexpr int D = kHeadDim;
-  constexpr size_t SMEM = kDecWaves * VS::BYTES > sizeof(DecReduce) ? kDecWaves * VS::BYTES : sizeof(DecReduce);
+  constexpr size_t SMEM = dec_static_lds<T>();
   __shared__ __attribute__((aligned(16))) unsigned char smem[SMEM];
+  extern __shared__ __attribute__((aligned(16))) float bias_lds[];  // BL: [bias_rows][bias_ld]
 
   const int tid = threadIdx.x;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -194,6 +207,12 @@ __global__ __launch_bounds__(kDecWaves * 64, sizeof(T) == 2 ? 2 : 1) void decode
   const int hin = hg * 16 + c;  // head within the kv group
   const bool hvalid = hin < G;
   const int h = kvh * G + (hvalid ? hin : 0);
+
+  // BL: keys [jb, ke) carry bias; sb is the first step holding one of them
+  const int jb = max(ks_lo, Lb - p.E);
+  const bool has_bias = BL && p.E > 0 && jb < ke;
+  const int sb = ks + ((max(jb, ks) - ks) & ~31);
+  const float c2s = PAGED ? bscale * p.c2 : p.c2;
 
   const T* qg = static_cast<const T*>(p.q);
   const T* kg = static_cast<const T*>(p.k);
@@ -318,7 +337,9 @@ __global__ __launch_bounds__(kDecWaves * 64, sizeof(T) == 2 ? 2 : 1) void decode
         ch.v[i] = ld8<T>(vb + size_t(j - jp) * row_stride + 8 * c);
       }
     }
-    if constexpr (PAGED) {
+    if constexpr (BL) {
+      // bias from LDS in process()
+    } else if constexpr (PAGED) {
       // Bias of key j at distance d = Lb-1-j: the row is in distance order
       // from entry sh = (4 - Lb % 4) % 4 on (zeros from distance E to the row's
       // end), so keys j0+16*blk+4g .. +3 are the four entries from
@@ -381,10 +402,24 @@ __global__ __launch_bounds__(kDecWaves * 64, sizeof(T) == 2 ? 2 : 1) void decode
         for (int st = 0; st < D / 32; ++st) mma16(ch.k[blk][st], qreg[st], x[blk]);
       }
     }
+    if constexpr (BL) {
+      f32x4 bb[2] = {zero4(), zero4()};
+      if (has_bias && j0 >= sb) {  // steps are 32-key aligned to sb
+        const float* brow = bias_lds + min(c, p.bias_rows - 1) * p.bias_ld;
 #pragma unroll
-    for (int blk = 0; blk < 2; ++blk)
+        for (int blk = 0; blk < 2; ++blk)
+          bb[blk] = *reinterpret_cast<const f32x4*>(brow + min(j0 + 16 * blk + 4 * g - sb, p.bias_cols - 4));
+      }
 #pragma unroll
-      for (int v = 0; v < 4; ++v) x[blk][v] = fmaf(x[blk][v], c1, PAGED ? bscale * ch.rl[blk][v] : ch.rl[blk][v]);
+      for (int blk = 0; blk < 2; ++blk)
+#pragma unroll
+        for (int v = 0; v < 4; ++v) x[blk][v] = fmaf(x[blk][v], c1, bb[blk][v]);
+    } else {
+#pragma unroll
+      for (int blk = 0; blk < 2; ++blk)
+#pragma unroll
+        for (int v = 0; v < 4; ++v) x[blk][v] = fmaf(x[blk][v], c1, PAGED ? bscale * ch.rl[blk][v] : ch.rl[blk][v]);
+    }
     if (j0 + kDecKeys > ke || (PAGED && j0 < ks_lo)) {  // ragged end (or aligned start) of the split
 #pragma unroll
       for (int blk = 0; blk < 2; ++blk)
@@ -446,6 +481,58 @@ __global__ __launch_bounds__(kDecWaves * 64, sizeof(T) == 2 ? 2 : 1) void decode
   }
 #pragma unroll
   for (int bfi = 0; bfi < NB - 1; ++bfi) fetch(ks + w * kDecKeys + bfi * STRIDE, ring[bfi]);
+  if constexpr (BL) {
+    if (has_bias) {
+      // keys sb + 16*bi + c (A rows: P row of distance Lb-1-j, clamped into
+      // [0, E) and zeroed below by the distance of each output key), heads c
+      // (B columns: r of head c); accumulator v of lane (g, c) is key
+      // sb + 16*bi + 4*g + v, head c, as in the score product
+      // d_r is a multiple of 16: in a last half step the lane groups past
+      // d_r read clamped slots against a zero r fragment
+      const int nst = (p.d_r + 31) / 32;
+      const T* rrow = static_cast<const T*>(p.r) + (size_t(b) * Hq + h) * p.d_r;
+      const T* pcg = static_cast<const T*>(p.pc);
+      v8_t<T> rf[kMaxDr / 32];
+#pragma unroll
+      for (int st = 0; st < kMaxDr / 32; ++st) {
+        const int off = 32 * st + 8 * g;
+        rf[st] = ld8_or_zero<T>(rrow + min(off, p.d_r - 8), off < p.d_r);
+      }
+      const int nblk = min((ke - sb + 15) / 16, p.bias_cols / 16);
+      // The P rows of kBiasBatch blocks are loaded together (blocks past the
+      // last are clamped to it and not stored), so a wave waits for the
+      // memory once per batch rather than once per block.
+      constexpr int kBiasBatch = 4;
+      for (int bi0 = w; bi0 < nblk; bi0 += kBiasBatch * kDecWaves) {
+        v8_t<T> pf[kBiasBatch][kMaxDr / 32];
+#pragma unroll
+        for (int u = 0; u < kBiasBatch; ++u) {
+          const int bi = min(bi0 + u * kDecWaves, nblk - 1);
+          const int d = Lb - 1 - (sb + 16 * bi + c);
+          const T* prow = pcg + size_t(min(max(d, 0), p.E - 1)) * p.d_r;
+#pragma unroll
+          for (int st = 0; st < kMaxDr / 32; ++st) pf[u][st] = ld8<T>(prow + min(32 * st + 8 * g, p.d_r - 8));
+        }
+#pragma unroll
+        for (int u = 0; u < kBiasBatch; ++u) {
+          const int bi = bi0 + u * kDecWaves;
+          f32x4 acc = zero4();
+#pragma unroll
+          for (int st = 0; st < kMaxDr / 32; ++st)
+            if (st < nst) mma16(pf[u][st], rf[st], acc);
+          f32x4 y;
+#pragma unroll
+          for (int v = 0; v < 4; ++v) {
+            const int dv = Lb - 1 - (sb + 16 * bi + 4 * g + v);
+            y[v] = (dv >= 0 && dv < p.E) ? acc[v] * c2s : 0.0f;
+          }
+          if (bi < nblk && c < p.bias_rows)
+            *reinterpret_cast<f32x4*>(bias_lds + c * p.bias_ld + 16 * bi + 4 * g) = y;
+        }
+      }
+      __syncthreads();
+    }
+  }
   for (int j0 = ks + w * kDecKeys; j0 < j_end; j0 += NB * STRIDE) {
 #pragma unroll
     for (int bfi = 0; bfi < NB; ++bfi) {
@@ -609,8 +696,36 @@ __global__ __launch_bounds__(256) void decode_merge_small_kernel(DecodeArgs p) {
   if (p.lse != nullptr && d4 == 0) p.lse[bh] = (M + log2f(den)) * kLn2;
 }
 
+template <typename T>
+hipError_t launch_decode_merge(const DecodeArgs& a, hipStream_t stream);
+
 template <typename T, bool PAGED, bool MX = false>
-hipError_t launch_decode_t(const DecodeArgs& a, hipStream_t stream) {
+hipError_t launch_decode_t(const DecodeArgs& a_in, hipStream_t stream) {
+  DecodeArgs a = a_in;
+  const long long grid = (long long)a.B * a.Hkv * a.n_hg * a.n_split;
+  if (grid > 0x7fffffffLL) return hipErrorInvalidConfiguration;
+  // Bias made in the split kernel when its LDS region leaves room for the
+  // kernel's occupancy (two workgroups per CU for bf16, one for fp32): a
+  // split's keys with bias span at most min(E, chunk) + 31 entries from its
+  // first biased step.
+  if (a.E > 0) {
+    constexpr size_t kLdsPerCu = 160 * 1024;
+    const size_t budget = kLdsPerCu / (sizeof(T) == 2 ? 2 : 1) - dec_static_lds<T>();
+    const int span = (a.E < a.chunk ? a.E : a.chunk) + 31;
+    const int cols = (span + 15) / 16 * 16;
+    const int ld = cols + 4;
+    const int G = a.Hq / a.Hkv;
+    const int rows = G < 16 ? G : 16;
+    const size_t bytes = size_t(rows) * ld * sizeof(float);
+    if (bytes <= budget) {
+      a.bias_cols = cols;
+      a.bias_ld = ld;
+      a.bias_rows = rows;
+      hipLaunchKernelGGL((decode_split_kernel<T, PAGED, MX, true>), dim3((unsigned)grid), dim3(kDecWaves * 64),
+                         (unsigned)bytes, stream, a);
+      return launch_decode_merge<T>(a, stream);
+    }
+  }
   {
     // bias rows of every (sequence, head): s * log2(e) * r.P[:, d], stored
     // reversed so that key j finds its distance L-1-j at entry j - L + rl_base
@@ -639,9 +754,13 @@ hipError_t launch_decode_t(const DecodeArgs& a, hipStream_t stream) {
       if (e != hipSuccess) return e;
     }
   }
-  const long long grid = (long long)a.B * a.Hkv * a.n_hg * a.n_split;
-  if (grid > 0x7fffffffLL) return hipErrorInvalidConfiguration;
   hipLaunchKernelGGL((decode_split_kernel<T, PAGED, MX>), dim3((unsigned)grid), dim3(kDecWaves * 64), 0, stream, a);
+  return launch_decode_merge<T>(a, stream);
+}
+
+// The merge launch after the split kernel (none for a single split).
+template <typename T>
+hipError_t launch_decode_merge(const DecodeArgs& a, hipStream_t stream) {
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || a.n_split == 1) return e;
   if (a.n_split <= kMergeSmallSplits) {

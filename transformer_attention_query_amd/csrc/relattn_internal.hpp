@@ -54,6 +54,8 @@ struct DecodeArgs {
   int n_hg;         // groups of 16 query heads per kv head
   int rl_base;      // key j reads bias row entry j - L + rl_base
   int rl_stride;    // floats per bias row
+  // bias made in the split kernel (set by the launcher; 0 = pre-pass rows)
+  int bias_cols = 0, bias_ld = 0, bias_rows = 0;
   // paged form only (see rel_attn_decode_paged): L is then the bound on kv_len
   const int* kv_len = nullptr;  // [B] cached tokens per sequence
   const int* btab = nullptr;    // [B, max_pages] page ids
