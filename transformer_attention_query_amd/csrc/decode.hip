@@ -180,11 +180,16 @@ __global__ __launch_bounds__(kDecWaves * 64, sizeof(T) == 2 ? 2 : 1) void decode
   // interleaved 32-key steps of the split, so the workgroup streams one
   // contiguous window of the cache; neighbouring workgroups take the kv heads
   // of the same key range ([L, Hkv, D] interleaves the heads of a position).
-  const long long wg = blockIdx.x;
-  const int hg = (int)(wg % p.n_hg);
-  long long rest = wg / p.n_hg;
-  const int kvh = (int)(rest % Hkv);
-  rest /= Hkv;
+  // Workgroup ids go round the 8 XCDs; the kv heads of one (sequence,
+  // split, head group) t take ids 8 apart, so one XCD reads the whole
+  // [Hkv, D] rows of its key range, each at about the same time.
+  const long long x = blockIdx.x;
+  const long long grp = 8LL * Hkv;
+  const int kvh = (int)((x % grp) / 8);
+  const long long t = (x / grp) * 8 + (x % 8);
+  if (t >= (long long)p.B * p.n_split * p.n_hg) return;  // padding of the last group of 8
+  const int hg = (int)(t % p.n_hg);
+  long long rest = t / p.n_hg;
   const int split = (int)(rest % p.n_split);
   const int b = (int)(rest / p.n_split);
 
@@ -702,7 +707,7 @@ hipError_t launch_decode_merge(const DecodeArgs& a, hipStream_t stream);
 template <typename T, bool PAGED, bool MX = false>
 hipError_t launch_decode_t(const DecodeArgs& a_in, hipStream_t stream) {
   DecodeArgs a = a_in;
-  const long long grid = (long long)a.B * a.Hkv * a.n_hg * a.n_split;
+  const long long grid = ((long long)a.B * a.n_hg * a.n_split + 7) / 8 * 8 * a.Hkv;
   if (grid > 0x7fffffffLL) return hipErrorInvalidConfiguration;
   // Bias made in the split kernel when its LDS region leaves room for the
   // kernel's occupancy (two workgroups per CU for bf16, one for fp32): a
@@ -786,10 +791,13 @@ DecodePlan plan_decode(int B, int L, int Hq, int Hkv, int num_splits_req, int wi
   if (num_splits_req > 0) {
     ns = num_splits_req;
   } else {
-    // Aim for ~512 workgroups (two per CU of a 256-CU part), each streaming
-    // at least two quanta so its prologue latency is amortised.
+    // Aim for ~256 workgroups (one per CU of a 256-CU part), each streaming
+    // at least two quanta so its prologue latency is amortised.  Measured on
+    // 64 sequences x 8192 keys: 256 workgroups (2 splits) beat 512 (4) by
+    // about 3 us of ~113; counts that do not divide over the CUs (3, 6
+    // splits) are slower than either.
     const long long wgs_per_split = (long long)B * Hkv * pl.n_hg;
-    long long want = (512 + wgs_per_split - 1) / wgs_per_split;
+    long long want = (256 + wgs_per_split - 1) / wgs_per_split;
     const long long cap = (vis + 2 * kDecSplitQuantum - 1) / (2 * kDecSplitQuantum);
     if (want > cap) want = cap;
     ns = (int)(want < 1 ? 1 : want);
