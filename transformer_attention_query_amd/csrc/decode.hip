@@ -14,21 +14,26 @@
 // caller's workspace and a second kernel merges them by log-sum-exp (with
 // a single split the workgroup normalises and writes the output itself).
 //
-// Three launches on the caller's stream:
-//   1. rel_logits_kernel writes, per (sequence, query head), the bias row
-//      s * log2(e) * r.P[:, d] for the last E distances into the workspace,
-//      stored reversed so that key j reads entry j - L + rl_base and entries
-//      beyond E (and the padding) are zero: a single query needs no shear.
-//   2. decode_split_kernel: per 32-key step a wave computes S^T = K Q^T with
+// Two launches on the caller's stream (three when the bias takes the
+// pre-pass):
+//   1. decode_split_kernel: the workgroups whose split holds keys within E
+//      of the query first make the bias s * log2(e) * r.P[:, L-1-j] of those
+//      keys and their query heads with MFMAs into LDS (a single query needs
+//      no shear).  Per 32-key step a wave computes S^T = K Q^T with
 //      16x16x32 MFMAs (rows = keys, columns = query heads, padded to 16),
-//      adds the bias entries of its keys (clamped 16-byte loads, no branch),
-//      applies the online softmax and accumulates O^T = V^T P^T.  The wave
-//      keeps two 32-key steps of K and V in flight in registers (ping-pong,
-//      no copies), so HBM latency overlaps the previous step's work.  V goes
-//      through a wave-private LDS tile: bf16 tiles are stored row-major and
-//      read as MFMA fragments with the gfx950 transpose read
+//      adds the bias of its keys from LDS, applies the online softmax and
+//      accumulates O^T = V^T P^T.  The
+//      wave keeps two 32-key steps of K and V in flight in registers
+//      (ping-pong, no copies), so HBM latency overlaps the previous step's
+//      work.  V goes through a wave-private LDS tile: bf16 tiles are stored
+//      row-major and read as MFMA fragments with the gfx950 transpose read
 //      (ds_read_b64_tr_b16); fp32 tiles are stored transposed.
-//   3. decode_merge_kernel: log-sum-exp merge of the split partials.
+//      Pre-pass form, when the bias region would not fit the LDS budget:
+//      rel_logits_kernel first writes, per (sequence, query head), the bias
+//      row for the last E distances into the workspace, stored reversed so
+//      that key j reads entry j - L + rl_base and entries beyond E are zero,
+//      and the split kernel loads its keys' entries with each step.
+//   2. decode_merge_kernel: log-sum-exp merge of the split partials.
 #include "device_common.hpp"
 #include "mx_common.hpp"
 #include "relattn_internal.hpp"
