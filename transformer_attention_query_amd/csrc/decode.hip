@@ -666,7 +666,8 @@ __global__ __launch_bounds__(kMergeThreads) void decode_merge_kernel(DecodeArgs 
 // Few splits: one thread per (sequence, head, 4 output columns) merges them.
 constexpr int kMergeSmallSplits = 16;
 
-template <typename T>
+// NS bounds n_split (2, 4, 8 or 16): each thread issues NS split loads.
+template <typename T, int NS>
 __global__ __launch_bounds__(256) void decode_merge_small_kernel(DecodeArgs p) {
   constexpr int D = kHeadDim;
   const size_t n_bh = size_t(p.B) * p.Hq;
@@ -679,10 +680,10 @@ __global__ __launch_bounds__(256) void decode_merge_small_kernel(DecodeArgs p) {
   const float* ws_l = ws_m + size_t(p.n_split) * n_bh;
   // all splits' partials are loaded first (indices clamped, splits past
   // n_split weighted by zero), then folded
-  float ms[kMergeSmallSplits], ls[kMergeSmallSplits];
-  f32x4 os[kMergeSmallSplits];
+  float ms[NS], ls[NS];
+  f32x4 os[NS];
 #pragma unroll
-  for (int s = 0; s < kMergeSmallSplits; ++s) {
+  for (int s = 0; s < NS; ++s) {
     const size_t sb = size_t(min(s, p.n_split - 1)) * n_bh + bh;
     ms[s] = ws_m[sb];
     ls[s] = ws_l[sb];
@@ -690,12 +691,12 @@ __global__ __launch_bounds__(256) void decode_merge_small_kernel(DecodeArgs p) {
   }
   float M = ms[0];
 #pragma unroll
-  for (int s = 1; s < kMergeSmallSplits; ++s)
+  for (int s = 1; s < NS; ++s)
     if (s < p.n_split) M = fmaxf(M, ms[s]);
   float den = 0.0f;
   f32x4 acc = zero4();
 #pragma unroll
-  for (int s = 0; s < kMergeSmallSplits; ++s) {
+  for (int s = 0; s < NS; ++s) {
     const float wgt = s < p.n_split ? fast_exp2(ms[s] - M) : 0.0f;
     den += wgt * ls[s];
 #pragma unroll
@@ -775,7 +776,15 @@ hipError_t launch_decode_merge(const DecodeArgs& a, hipStream_t stream) {
   if (e != hipSuccess || a.n_split == 1) return e;
   if (a.n_split <= kMergeSmallSplits) {
     const long long threads = (long long)a.B * a.Hq * (kHeadDim / 4);
-    hipLaunchKernelGGL(decode_merge_small_kernel<T>, dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, stream, a);
+    const dim3 grid((unsigned)((threads + 255) / 256));
+    if (a.n_split <= 2)
+      hipLaunchKernelGGL((decode_merge_small_kernel<T, 2>), grid, dim3(256), 0, stream, a);
+    else if (a.n_split <= 4)
+      hipLaunchKernelGGL((decode_merge_small_kernel<T, 4>), grid, dim3(256), 0, stream, a);
+    else if (a.n_split <= 8)
+      hipLaunchKernelGGL((decode_merge_small_kernel<T, 8>), grid, dim3(256), 0, stream, a);
+    else
+      hipLaunchKernelGGL((decode_merge_small_kernel<T, kMergeSmallSplits>), grid, dim3(256), 0, stream, a);
   } else {
     hipLaunchKernelGGL(decode_merge_kernel<T>, dim3((unsigned)(a.B * a.Hq * (kHeadDim / kMergeCols))),
                        dim3(kMergeThreads), 0, stream, a);
