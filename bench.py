@@ -1,25 +1,39 @@
 """Benchmark of the relative-attention hot path on one MI355X.
 
 A step is one prefill call (the whole forward: scores, relative bias, mask,
-online softmax, PV, epilogue) of the sliding-window layer (B=1, T=8192,
-Hq=16, Hkv=2, D=128, d_r=128, rel_extent=1024, window=1024, bf16) on inputs
-already resident in HBM.  The line also reports the split-KV decode of 64
-sequences x 8192 keys (KV GB/s), each against its roofline, and the fp64 CPU
-oracle timed on a bounded sample of the prefill workload; the paged decode,
-the extend (chunked prefill) and the attention prologue of an 8192-token
-prefill (K/V ShortConv, Q/K RMSNorm, cache write; HBM GB/s) ride along.
+online softmax, PV, epilogue) of the full-attention layer with the length
+log-scale (B=2, T=32768, Hq=16, Hkv=2, D=128, d_r=128, rel_extent=1024,
+causal, s = 1.25, bf16), the largest prefill that fits one GPU, on inputs
+already resident in HBM.  Its algorithmic TFLOP/s is the headline `value`,
+with the kernel's fraction of the bf16 MFMA peak in `roofline`.
+
+The same line carries one object per other named workload, each with its own
+roofline and the fp64 CPU oracle timed on a bounded sample of it:
+  * tiny_fp32       B=1 T=256 Hq=4 Hkv=1 d_r=32 E=64, fp32 (launch-bound)
+  * swa_prefill_8k  B=1 T=8192 Hq=16 Hkv=2 d_r=128 E=1024 W=1024
+  * decode_64x8k    64 sequences x 1 token over 8192 keys (KV GB/s vs HBM)
+  * decode_1x1m_log 1 sequence x 1 token over 2^20 keys, s = 5/3
+and the rows the library adds beside the forward (paged and MXFP8 decode,
+extend over a paged cache, the attention prologue, the backward).
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+                       [--only NAME[,NAME...]]
        python bench.py --copy-calibration   (a plain 1 GiB device copy, for
-       scaling the HBM byte counters FETCH_SIZE / WRITE_SIZE under rocprofv3)
+           scaling the HBM byte counters FETCH_SIZE / WRITE_SIZE)
+       python bench.py --traffic-from FETCH_CSV WRITE_CSV --kernel-key KEY
+                       --kernel-match SUBSTR[,SUBSTR...] --src FILE[,FILE...]
+           (turn two rocprofv3 --pmc counter CSVs into the per-launch HBM
+           bytes of profiles/traffic.json; see `traffic_from_counters`)
 """
 
 from __future__ import annotations
 
 import argparse
+import csv
 import hashlib
 import json
 import os
+import platform
 import sys
 import time
 
@@ -28,15 +42,22 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA, published
+PEAK_F32_TFLOPS = 157.3     # MI355X fp32 vector, published (the fp32 path runs fp32 MFMA / VALU)
 PEAK_HBM_GBPS = 8000.0      # MI355X HBM3E, published
-PREFILL_WORKLOAD = "swa_prefill_8k"
-DECODE_WORKLOAD = "decode_64x8k"
+METRIC = "relative-attention prefill TFLOP/s + decode KV GB/s (% of MI355X peak)"
+HEADLINE = "full_prefill_32k_log"
+PREFILL_WORKLOADS = ["tiny_fp32", "swa_prefill_8k", "full_prefill_32k_log"]
+DECODE_WORKLOADS = ["decode_64x8k", "decode_1x1m_log"]
+EXTRA = ["decode_paged", "decode_mx", "extend", "prologue", "backward"]
 EXTEND_WORKLOAD = "extend_4x1k_8k_paged"
 PAGED_DECODE_WORKLOAD = "decode_paged_64x8k"
 PROLOGUE_WORKLOAD = "prologue_8k"
 BACKWARD_WORKLOAD = "swa_backward_8k"
-PREFILL_KERNEL = "prefill_dma_kernel"  # the bf16 path for eight or more query heads per kv head
-DECODE_KERNEL = "decode_split_kernel"
+TRAFFIC_JSON = os.path.join(ROOT, "profiles", "traffic.json")
+
+
+# ----------------------------------------------------------------------------
+# algorithmic work
 
 
 def prefill_work(T: int, Hq: int, D: int, d_r: int, E: int, W: int, rows=None):
@@ -73,7 +94,33 @@ def decode_bytes(B: int, L: int, Hq: int, Hkv: int, D: int, d_r: int, E: int, W:
     return kv + per_seq + E * d_r * elem, kv
 
 
-def _src_hash(*names):
+def decode_bytes_mx(B: int, L: int, Hq: int, Hkv: int, D: int, d_r: int, E: int, W: int) -> int:
+    """Algorithmic bytes of one decode call over MXFP8 caches: per visible key
+    and kv head the K and V codes (D bytes each) and scales (D/32 bytes
+    each); q, r and out per sequence (bf16) and P once, as for bf16."""
+    vis = min(L, W) if W > 0 else L
+    kv = B * vis * Hkv * 2 * (D + D // 32)
+    per_seq = B * (Hq * D * 2 + Hq * d_r * 2 + Hq * D * 2)
+    return kv + per_seq + E * d_r * 2
+
+
+def prologue_bytes(N: int, B: int, Hq: int, Hkv: int, D: int, W: int, state: bool, elem: int = 2) -> int:
+    """Algorithmic bytes of one prologue call: every q, k and v row read once
+    and written once (q_out, the two caches), the filter and norm weights, and
+    the states (read if given, always written)."""
+    rows = 2 * N * (Hq + 2 * Hkv) * D * elem
+    weights = (2 * Hkv * D * W + 2 * D) * elem
+    st = B * 2 * 3 * Hkv * D * elem
+    return rows + weights + st * (2 if state else 1)
+
+
+# ----------------------------------------------------------------------------
+# counters
+
+
+def src_hash(*names):
+    """Hash of kernel sources: a counter reading is used only while the source
+    it was taken on is unchanged."""
     h = hashlib.sha256()
     for n in names:
         with open(os.path.join(ROOT, "transformer_attention_query_amd", "csrc", n), "rb") as f:
@@ -81,27 +128,92 @@ def _src_hash(*names):
     return h.hexdigest()[:16]
 
 
-def _traffic(kernel: str, src_hash: str):
+PREFILL_SRC = ("prefill.hip", "device_common.hpp")
+DECODE_SRC = ("decode.hip", "device_common.hpp", "mx_common.hpp")
+
+
+def traffic(key: str, src):
     """Measured HBM bytes per launch from the committed counter summary, if it
     was taken on the current kernel source; else None."""
-    path = os.path.join(ROOT, "profiles", "traffic.json")
     try:
-        data = json.load(open(path))
+        data = json.load(open(TRAFFIC_JSON))
     except (OSError, ValueError):
         return None
-    ent = data.get(kernel)
-    if not ent or ent.get("src_hash") != src_hash:
+    ent = data.get(key)
+    if not ent or ent.get("src_hash") != src_hash(*src):
         return None
     return ent.get("bytes_per_launch")
 
 
-def _time_launches(fn, steps: int, warmup: int, stream, before=None):
-    """Run fn() warmup times, then `steps` times between synchronisations.
-    Returns (total ms over the steps, list of per-launch ms from event pairs)."""
+def _counter_means(path: str, counter: str):
+    """Mean counter value per dispatch, by kernel name, from a rocprofv3
+    counter-collection CSV."""
+    acc = {}
+    with open(path) as f:
+        for row in csv.DictReader(f):
+            if row["Counter_Name"] != counter:
+                continue
+            acc.setdefault(row["Kernel_Name"], []).append(float(row["Counter_Value"]))
+    return {k: sum(v) / len(v) for k, v in acc.items()}
+
+
+def traffic_from_counters(fetch_csv: str, write_csv: str, key: str, matches, src, calib=None):
+    """HBM bytes per launch of the kernels whose names contain one of `matches`
+    (summed over them: e.g. a split kernel and its merge make one call).
+
+    FETCH_SIZE and WRITE_SIZE are read in KiB per dispatch; each is scaled by
+    the factor a plain device copy of known size gives for the same counter
+    (`_calibration` in traffic.json: bytes = scale * KiB * 1024)."""
+    data = json.load(open(TRAFFIC_JSON)) if os.path.exists(TRAFFIC_JSON) else {}
+    cal = data.get("_calibration") if calib is None else calib
+    if not cal:
+        raise SystemExit("no _calibration in traffic.json: run the copy calibration first")
+    F = _counter_means(fetch_csv, "FETCH_SIZE")
+    W = _counter_means(write_csv, "WRITE_SIZE")
+    fetch = write = 0.0
+    per = {}
+    for m in matches:
+        names = [k for k in F if m in k]
+        if len(names) != 1:
+            raise SystemExit(f"kernel match {m!r} selects {names}")
+        n = names[0]
+        f = F[n] * 1024 * cal["fetch_scale"]
+        w = W.get(n, 0.0) * 1024 * cal["write_scale"]
+        per[m] = {"fetch_bytes": int(f), "write_bytes": int(w)}
+        fetch += f
+        write += w
+    data[key] = {"src_hash": src_hash(*src), "fetch_bytes": int(fetch), "write_bytes": int(write),
+                 "bytes_per_launch": int(fetch + write), "kernels": per}
+    with open(TRAFFIC_JSON, "w") as f:
+        json.dump(data, f, indent=1)
+    print(json.dumps({key: data[key]}))
+
+
+def calibration_from_counters(fetch_csv: str, write_csv: str, nbytes: int = 1 << 30):
+    """Counter scale factors from the plain copy kernel of `copy_calibration`."""
+    F = _counter_means(fetch_csv, "FETCH_SIZE")
+    W = _counter_means(write_csv, "WRITE_SIZE")
+    fk = max(F.values())
+    wk = max(W.values())
+    cal = {"copy_bytes": nbytes, "FETCH_SIZE_KiB": fk, "WRITE_SIZE_KiB": wk,
+           "fetch_scale": nbytes / (fk * 1024), "write_scale": nbytes / (wk * 1024)}
+    data = json.load(open(TRAFFIC_JSON)) if os.path.exists(TRAFFIC_JSON) else {}
+    data["_calibration"] = cal
+    with open(TRAFFIC_JSON, "w") as f:
+        json.dump(data, f, indent=1)
+    print(json.dumps(cal))
+
+
+# ----------------------------------------------------------------------------
+# timing
+
+
+def _time_launches(fn, steps: int, warmup: int, stream):
+    """Run fn(i) warmup times, then `steps` times between synchronisations,
+    with a HIP event pair on the launch stream around every launch.
+    Returns (total ms over the steps, list of per-launch ms)."""
     import torch
     for i in range(warmup):
-        if before:
-            before(i)
         fn(i)
     torch.cuda.synchronize()
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
@@ -110,8 +222,6 @@ def _time_launches(fn, steps: int, warmup: int, stream, before=None):
     torch.cuda.synchronize()
     t0.record(stream)
     for i in range(steps):
-        if before:
-            before(i)
         ev[i][0].record(stream)
         fn(i)
         ev[i][1].record(stream)
@@ -138,38 +248,164 @@ def _time_batch(fn, steps: int, warmup: int, stream):
     return t0.elapsed_time(t1) / steps
 
 
-def bench_prefill(steps: int, warmup: int):
+def _stats(per):
+    s = sorted(per)
+    return {"avg_launch_us": round(sum(s) / len(s) * 1e3, 2), "median_us": round(s[len(s) // 2] * 1e3, 2),
+            "min_us": round(s[0] * 1e3, 2), "max_us": round(s[-1] * 1e3, 2)}
+
+
+def _roofline(bound, kernel, achieved, peak, unit, tr, per):
+    r = {"bound": bound, "kernel": kernel, "achieved": round(achieved, 2), "peak": peak, "unit": unit,
+         "frac": round(achieved / peak, 4), "traffic": tr}
+    r.update(_stats(per))
+    return r
+
+
+# ----------------------------------------------------------------------------
+# the CPU oracle as a reported baseline
+
+
+def _host():
+    model = platform.processor() or ""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return os.cpu_count(), model
+
+
+def oracle_prefill_time(w, x, target_s: float):
+    """The fp64 oracle, as it stands, on evenly spaced query rows of a prefill
+    workload (all rows when they fit the time target)."""
+    import torch
+    import oracle
+    T = w.T
+    stride_rows = lambda n: list(range(T - 1, -1, -max(1, T // n)))[:n]  # noqa: E731
+    run = lambda rows: oracle.prefill(x["q"], x["k"], x["v"], x["r"], x["P"], w.alpha, w.E, w.W,  # noqa: E731
+                                      w.log_scale, rows=rows)
+    run(stride_rows(4))
+    t = time.perf_counter()
+    run(stride_rows(16))
+    per_row = (time.perf_counter() - t) / 16
+    n = int(max(16, min(T, target_s / max(per_row, 1e-6))))
+    rows = stride_rows(n)
+    reps = 0
+    t = time.perf_counter()
+    while True:  # a workload the oracle finishes in well under a second is repeated
+        run(rows)
+        reps += 1
+        dt = time.perf_counter() - t
+        if dt >= min(1.0, target_s) or len(rows) < T:
+            break
+    dt /= reps
+    flops, _, _ = prefill_work(T, w.Hq, w.D, w.d_r, w.E, w.W, rows=rows)
+    flops *= w.B
+    cpus, model = _host()
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": torch.get_num_threads(), "host_cpus": cpus,
+            "cpu_model": model, "kind": "oracle", "wall_s": round(dt, 2),
+            "sample": f"{len(rows)} of {T} query rows (evenly spaced from the last; every head and sequence) "
+                      f"of {w.name}, fp64 torch-CPU oracle"}
+
+
+def oracle_decode_time(w, x, target_s: float):
+    """The fp64 oracle, as it stands, on the first sequences of a decode
+    workload (all of them when they fit the time target)."""
+    import torch
+    import oracle
+    sub = lambda n: {k: (t[:n] if k in ("q", "k", "v", "r") else t) for k, t in x.items()}  # noqa: E731
+    run = lambda y: oracle.decode(y["q"], y["k"], y["v"], y["r"], y["P"], w.alpha, w.E, w.W, w.log_scale)  # noqa: E731
+    t = time.perf_counter()
+    run(sub(1))
+    per_seq = time.perf_counter() - t
+    n = int(max(1, min(w.B, target_s / max(per_seq, 1e-6))))
+    t = time.perf_counter()
+    if n > 1 or w.B > 1:
+        run(sub(n))
+        dt = time.perf_counter() - t
+    else:
+        dt = per_seq
+    nbytes, _ = decode_bytes(n, w.T, w.Hq, w.Hkv, w.D, w.d_r, w.E, w.W)
+    cpus, model = _host()
+    return {"value": nbytes / dt / 1e9, "unit": "GB/s", "cores": torch.get_num_threads(), "host_cpus": cpus,
+            "cpu_model": model, "kind": "oracle", "wall_s": round(dt, 2),
+            "sample": f"{n} of {w.B} sequences (all {w.Hq} heads, all {w.T} keys) of {w.name}, "
+                      f"fp64 torch-CPU oracle"}
+
+
+# ----------------------------------------------------------------------------
+# workloads
+
+
+def bench_prefill(name: str, steps: int, warmup: int, cpu: bool):
+    """One prefill workload: per-launch HIP events on the launch stream.  The
+    8K workload's inputs (76 MB) would stay in the 256 MB MALL between
+    launches, so it rotates over four copies (304 MB); the 32K workload's
+    inputs (576 MB) exceed the MALL by themselves."""
     import torch
     import transformer_attention_query_amd as ra
     from transformer_attention_query_amd import inputs as tinputs
 
-    w = tinputs.WORKLOADS[PREFILL_WORKLOAD]
-    x = {n: t.cuda() for n, t in tinputs.make_inputs(w, seed=0).items()}
+    w = tinputs.WORKLOADS[name]
+    xc = tinputs.make_inputs(w, seed=0)
+    x = {n: t.cuda() for n, t in xc.items()}
+    n_copies = 4 if name == "swa_prefill_8k" else 1
+    sets = [x] + [{n: t.clone() for n, t in x.items()} for _ in range(n_copies - 1)]
     out = torch.empty_like(x["q"])
     lse = torch.empty(w.B, w.Hq, w.T, dtype=torch.float32, device="cuda")
     stream = torch.cuda.current_stream()
 
-    def step(_i):
-        ra.prefill(x["q"], x["k"], x["v"], x["r"], x["P_cols"], w.alpha, w.E, w.W, w.log_scale, out=out, lse=lse)
+    def step(i):
+        y = sets[i % n_copies]
+        ra.prefill(y["q"], y["k"], y["v"], y["r"], y["P_cols"], w.alpha, w.E, w.W, w.log_scale, out=out, lse=lse)
 
     total_ms, per = _time_launches(step, steps, warmup, stream)
     flops, pairs, rel = prefill_work(w.T, w.Hq, w.D, w.d_r, w.E, w.W)
     flops *= w.B
     ms_step = total_ms / steps
     kernel_ms = sum(per) / len(per)
-    return w, flops, ms_step, kernel_ms, per
+    bf16 = w.dtype == "bf16"
+    G = w.Hq // w.Hkv
+    kernel = "prefill_dma_kernel" if bf16 and G % 8 == 0 else f"prefill_kernel<{'__bf16, 8' if bf16 else 'float, 2'}>"
+    peak = PEAK_BF16_TFLOPS if bf16 else PEAK_F32_TFLOPS
+    achieved = flops / (kernel_ms * 1e-3) / 1e12
+    obj = {"workload": w.name, "value": round(flops / (ms_step * 1e-3) / 1e12, 3), "unit": "TFLOP/s",
+           "ms_per_step": round(ms_step, 5), "dtype": w.dtype,
+           "config": {"workload": w.name, "B": w.B, "T": w.T, "Hq": w.Hq, "Hkv": w.Hkv, "D": w.D, "d_r": w.d_r,
+                      "rel_extent": w.E, "window": w.W, "log_scale": w.log_scale, "alpha": "1/sqrt(128)",
+                      "algorithmic_flops": flops, "visible_pairs": pairs * w.B, "rel_entries": rel * w.B,
+                      "input_copies_rotated": n_copies},
+           "roofline": _roofline("mfma", kernel, achieved, peak, "TFLOP/s",
+                                 traffic(f"prefill_dma_kernel@{w.name}", PREFILL_SRC), per)}
+    if not bf16:
+        obj["roofline"]["note"] = ("fp32 path against the fp32 vector peak; launch-bound at this size "
+                                   "(parity workload)")
+    print(f"# prefill {w.name}: {ms_step * 1e3:.1f} us/step, kernel {kernel_ms * 1e3:.1f} us "
+          f"({achieved:.1f} TFLOP/s)", file=sys.stderr, flush=True)
+    del sets, x, out, lse
+    torch.cuda.empty_cache()
+    if cpu:
+        obj["cpu_baseline"] = oracle_prefill_time(w, xc, 15.0 if name == HEADLINE else 8.0)
+        print(f"# oracle {w.name}: {obj['cpu_baseline']['sample']}, {obj['cpu_baseline']['wall_s']} s",
+              file=sys.stderr, flush=True)
+    return obj
 
 
-def bench_decode(steps: int, warmup: int):
+def bench_decode(name: str, steps: int, warmup: int, cpu: bool):
+    """One decode workload (the split kernel and the merge, per call).  Two
+    copies of the cache, used alternately: each launch reads at least 512 MiB,
+    so the copy it reads was last touched two launches ago, beyond the 256 MB
+    MALL and the L2s."""
     import torch
     import transformer_attention_query_amd as ra
     from transformer_attention_query_amd import inputs as tinputs
 
-    w = tinputs.WORKLOADS[DECODE_WORKLOAD]
-    x = {n: t.cuda() for n, t in tinputs.make_inputs(w, seed=0).items()}
-    # Two copies of the cache, used alternately: each launch reads 512 MiB, so
-    # the copy it reads was last touched two launches ago, far beyond the 256 MB
-    # MALL and the L2s.
+    w = tinputs.WORKLOADS[name]
+    xc = tinputs.make_inputs(w, seed=0)
+    x = {n: t.cuda() for n, t in xc.items()}
     k2 = [x["k"], x["k"].clone()]
     v2 = [x["v"], x["v"].clone()]
     ns, ws_bytes = ra.decode_plan(w.B, w.T, w.Hq, w.Hkv, w.D, w.num_splits, w.W, w.E)
@@ -182,17 +418,24 @@ def bench_decode(steps: int, warmup: int):
 
     total_ms, per = _time_launches(step, steps, warmup, stream)
     nbytes, kv = decode_bytes(w.B, w.T, w.Hq, w.Hkv, w.D, w.d_r, w.E, w.W)
-    return w, nbytes, kv, total_ms / steps, sum(per) / len(per), ns
-
-
-def decode_bytes_mx(B: int, L: int, Hq: int, Hkv: int, D: int, d_r: int, E: int, W: int) -> int:
-    """Algorithmic bytes of one decode call over MXFP8 caches: per visible key
-    and kv head the K and V codes (D bytes each) and scales (D/32 bytes
-    each); q, r and out per sequence (bf16) and P once, as for bf16."""
-    vis = min(L, W) if W > 0 else L
-    kv = B * vis * Hkv * 2 * (D + D // 32)
-    per_seq = B * (Hq * D * 2 + Hq * d_r * 2 + Hq * D * 2)
-    return kv + per_seq + E * d_r * 2
+    ms_step = total_ms / steps
+    kernel_ms = sum(per) / len(per)
+    kgbps = nbytes / (kernel_ms * 1e-3) / 1e9
+    obj = {"workload": w.name, "value": round(nbytes / (ms_step * 1e-3) / 1e9, 1), "unit": "GB/s",
+           "ms_per_step": round(ms_step, 5), "num_splits": ns, "algorithmic_bytes": nbytes, "dtype": "bf16",
+           "config": {"workload": w.name, "B": w.B, "L": w.T, "Hq": w.Hq, "Hkv": w.Hkv, "D": w.D, "d_r": w.d_r,
+                      "rel_extent": w.E, "window": w.W, "log_scale": w.log_scale, "kv_copies_rotated": 2},
+           "roofline": _roofline("hbm", "decode_split_kernel+merge", kgbps, PEAK_HBM_GBPS, "GB/s",
+                                 traffic(f"decode_split_kernel@{w.name}", DECODE_SRC), per)}
+    print(f"# decode {w.name}: {ms_step * 1e3:.1f} us/step, call {kernel_ms * 1e3:.1f} us ({ns} splits, "
+          f"{kgbps:.0f} GB/s)", file=sys.stderr, flush=True)
+    del x, k2, v2, ws
+    torch.cuda.empty_cache()
+    if cpu:
+        obj["cpu_baseline"] = oracle_decode_time(w, xc, 8.0)
+        print(f"# oracle {w.name}: {obj['cpu_baseline']['sample']}, {obj['cpu_baseline']['wall_s']} s",
+              file=sys.stderr, flush=True)
+    return obj
 
 
 def bench_decode_mx(steps: int, warmup: int):
@@ -201,7 +444,7 @@ def bench_decode_mx(steps: int, warmup: int):
     import transformer_attention_query_amd as ra
     from transformer_attention_query_amd import inputs as tinputs
 
-    w = tinputs.WORKLOADS[DECODE_WORKLOAD]
+    w = tinputs.WORKLOADS["decode_64x8k"]
     x = {n: t.cuda() for n, t in tinputs.make_inputs(w, seed=0).items()}
     kc, ks = ra.mx_quantize(x["k"])
     vc, vs = ra.mx_quantize(x["v"])
@@ -219,7 +462,44 @@ def bench_decode_mx(steps: int, warmup: int):
 
     total_ms, per = _time_launches(step, steps, warmup, stream)
     nbytes = decode_bytes_mx(w.B, w.T, w.Hq, w.Hkv, w.D, w.d_r, w.E, w.W)
-    return w, nbytes, total_ms / steps, sum(per) / len(per), ns
+    ms = total_ms / steps
+    k = nbytes / (sum(per) / len(per) * 1e-3) / 1e9
+    print(f"# decode {w.name} (MXFP8 K/V): {ms * 1e3:.1f} us/step ({ns} splits)", file=sys.stderr, flush=True)
+    return {"workload": w.name + " (MXFP8 K/V)", "value": round(nbytes / (ms * 1e-3) / 1e9, 1), "unit": "GB/s",
+            "ms_per_step": round(ms, 5), "num_splits": ns, "algorithmic_bytes": nbytes,
+            "dtype": "mxfp8 K/V, bf16 q/out",
+            "roofline": _roofline("hbm", "decode_split_kernel (MXFP8)+merge", k, PEAK_HBM_GBPS, "GB/s",
+                                  traffic("decode_split_kernel_mx@decode_64x8k", DECODE_SRC), per)}
+
+
+def bench_decode_paged(steps: int, warmup: int):
+    """decode_64x8k over a paged cache: the same bytes through a block table."""
+    import torch
+    import transformer_attention_query_amd as ra
+    from transformer_attention_query_amd import inputs as tinputs
+
+    w = tinputs.WORKLOADS[PAGED_DECODE_WORKLOAD]
+    x = {n: t.cuda() for n, t in tinputs.make_inputs(w, seed=0).items()}
+    # two copies of the page pool, used alternately (each launch reads 512 MiB)
+    kp = [x["k_pages"], x["k_pages"].clone()]
+    vp = [x["v_pages"], x["v_pages"].clone()]
+    ns, ws_bytes = ra.decode_plan(w.B, w.T, w.Hq, w.Hkv, w.D, 0, w.W, w.E)
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device="cuda")
+    stream = torch.cuda.current_stream()
+
+    def step(i):
+        ra.decode_paged(x["q"], kp[i % 2], vp[i % 2], x["r"], x["P_cols"], w.alpha, w.E, w.W, w.log_scale,
+                        x["kv_len"], x["block_table"], w.T, num_splits=ns, workspace=ws)
+
+    total_ms, per = _time_launches(step, steps, warmup, stream)
+    nbytes, _ = decode_bytes(w.B, w.T, w.Hq, w.Hkv, w.D, w.d_r, w.E, w.W)
+    ms = total_ms / steps
+    k = nbytes / (sum(per) / len(per) * 1e-3) / 1e9
+    print(f"# decode {w.name}: {ms * 1e3:.1f} us/step ({ns} splits)", file=sys.stderr, flush=True)
+    return {"workload": w.name, "value": round(nbytes / (ms * 1e-3) / 1e9, 1), "unit": "GB/s",
+            "ms_per_step": round(ms, 5), "num_splits": ns, "algorithmic_bytes": nbytes,
+            "roofline": _roofline("hbm", "decode_split_kernel (paged)+merge", k, PEAK_HBM_GBPS, "GB/s",
+                                  traffic(f"decode_split_kernel_paged@{w.name}", DECODE_SRC), per)}
 
 
 def bench_extend(steps: int, warmup: int):
@@ -244,41 +524,16 @@ def bench_extend(steps: int, warmup: int):
 
     total_ms, per = _time_launches(step, steps, warmup, stream)
     flops, _, _ = prefill_work(w.T, w.Hq, w.D, w.d_r, w.E, w.W, rows=range(w.T - w.n_new, w.T))
-    return w, flops * w.B, total_ms / steps, sum(per) / len(per)
-
-
-def bench_decode_paged(steps: int, warmup: int):
-    """decode_64x8k over a paged cache: the same bytes through a block table."""
-    import torch
-    import transformer_attention_query_amd as ra
-    from transformer_attention_query_amd import inputs as tinputs
-
-    w = tinputs.WORKLOADS[PAGED_DECODE_WORKLOAD]
-    x = {n: t.cuda() for n, t in tinputs.make_inputs(w, seed=0).items()}
-    # two copies of the page pool, used alternately (each launch reads 512 MiB)
-    kp = [x["k_pages"], x["k_pages"].clone()]
-    vp = [x["v_pages"], x["v_pages"].clone()]
-    ns, ws_bytes = ra.decode_plan(w.B, w.T, w.Hq, w.Hkv, w.D, 0, w.W, w.E)
-    ws = torch.empty(ws_bytes, dtype=torch.uint8, device="cuda")
-    stream = torch.cuda.current_stream()
-
-    def step(i):
-        ra.decode_paged(x["q"], kp[i % 2], vp[i % 2], x["r"], x["P_cols"], w.alpha, w.E, w.W, w.log_scale,
-                        x["kv_len"], x["block_table"], w.T, num_splits=ns, workspace=ws)
-
-    total_ms, per = _time_launches(step, steps, warmup, stream)
-    nbytes, _ = decode_bytes(w.B, w.T, w.Hq, w.Hkv, w.D, w.d_r, w.E, w.W)
-    return w, nbytes, total_ms / steps, sum(per) / len(per), ns
-
-
-def prologue_bytes(N: int, B: int, Hq: int, Hkv: int, D: int, W: int, state: bool, elem: int = 2) -> int:
-    """Algorithmic bytes of one prologue call: every q, k and v row read once
-    and written once (q_out, the two caches), the filter and norm weights, and
-    the states (read if given, always written)."""
-    rows = 2 * N * (Hq + 2 * Hkv) * D * elem
-    weights = (2 * Hkv * D * W + 2 * D) * elem
-    st = B * 2 * 3 * Hkv * D * elem
-    return rows + weights + st * (2 if state else 1)
+    flops *= w.B
+    ms = total_ms / steps
+    ach = flops / (sum(per) / len(per) * 1e-3) / 1e12
+    print(f"# extend {w.name}: {ms * 1e3:.1f} us/step", file=sys.stderr, flush=True)
+    return {"workload": w.name, "value": round(flops / (ms * 1e-3) / 1e12, 2), "unit": "TFLOP/s",
+            "ms_per_step": round(ms, 5), "algorithmic_flops": flops,
+            "config": {"B": w.B, "kv_len": w.T, "new_rows": w.n_new, "page_size": w.page_size, "Hq": w.Hq,
+                       "Hkv": w.Hkv, "d_r": w.d_r, "rel_extent": w.E, "window": w.W},
+            "roofline": _roofline("mfma", "prefill_kernel (extend)", ach, PEAK_BF16_TFLOPS, "TFLOP/s",
+                                  traffic(f"prefill_kernel_extend@{w.name}", PREFILL_SRC), per)}
 
 
 def bench_prologue(steps: int, warmup: int):
@@ -299,7 +554,7 @@ def bench_prologue(steps: int, warmup: int):
                     x["q_start"], x["kv_len"], x["k_cache"], x["v_cache"], state_in=st_in, state_out=st_out,
                     q_out=q_out)
 
-    total_ms, _ = _time_launches(step, steps, warmup, stream)
+    total_ms, per = _time_launches(step, steps, warmup, stream)
     # The kernel is short: time it as a batch of launches straight through the
     # C ABI (arguments marshalled once), with no events between them.
     lib = ra.load_library()
@@ -318,7 +573,19 @@ def bench_prologue(steps: int, warmup: int):
     if fn(*args) != 0:
         raise RuntimeError("prologue call failed: " + lib.rel_attn_last_error().decode())
     nbytes = prologue_bytes(N, w.B, w.Hq, w.Hkv, w.D, 4, st_in is not None)
-    return w, nbytes, total_ms / steps, kernel_ms
+    ms = total_ms / steps
+    gk = nbytes / (kernel_ms * 1e-3) / 1e9
+    print(f"# prologue {w.name}: {ms * 1e3:.1f} us/step", file=sys.stderr, flush=True)
+    roof = _roofline("hbm", "prologue_kernel", gk, PEAK_HBM_GBPS, "GB/s",
+                     traffic(f"prologue_kernel@{w.name}", ("prologue.hip", "device_common.hpp", "mx_common.hpp")),
+                     per)
+    roof["avg_launch_us"] = round(kernel_ms * 1e3, 2)
+    roof["timing"] = "avg over back-to-back launches through the C ABI; min/max/median from per-call events"
+    return {"workload": w.name, "value": round(nbytes / (ms * 1e-3) / 1e9, 1), "unit": "GB/s",
+            "ms_per_step": round(ms, 5), "algorithmic_bytes": nbytes,
+            "config": {"B": w.B, "tokens": N, "Hq": w.Hq, "Hkv": w.Hkv, "D": w.D, "conv_width": 4,
+                       "page_size": w.page_size},
+            "roofline": roof}
 
 
 def bench_backward(steps: int, warmup: int):
@@ -350,35 +617,16 @@ def bench_backward(steps: int, warmup: int):
     if fn(*args) != 0:
         raise RuntimeError("backward call failed: " + lib.rel_attn_last_error().decode())
     flops = backward_work(w.T, w.Hq, w.D, w.d_r, w.E, w.W) * w.B
-    return w, flops, total_ms / steps, sum(per) / len(per), ns
-
-
-def cpu_baseline(target_s: float = 15.0):
-    """The fp64 oracle, as it stands, on query rows of the prefill workload."""
-    import torch
-    import oracle
-    from transformer_attention_query_amd import inputs as tinputs
-
-    w = tinputs.WORKLOADS[PREFILL_WORKLOAD]
-    x = tinputs.make_inputs(w, seed=0)
-    threads = torch.get_num_threads()
-    stride_rows = lambda n: list(range(w.T - 1, -1, -max(1, w.T // n)))[:n]  # noqa: E731
-    run = lambda rows: oracle.prefill(x["q"], x["k"], x["v"], x["r"], x["P"], w.alpha, w.E, w.W,  # noqa: E731
-                                      w.log_scale, rows=rows)
-    # warm up, calibrate on 64 rows, then run a sample sized for about target_s
-    run(stride_rows(8))
-    t = time.perf_counter()
-    run(stride_rows(64))
-    per_row = (time.perf_counter() - t) / 64
-    n = int(max(64, min(w.T, target_s / max(per_row, 1e-6))))
-    rows = stride_rows(n)
-    t = time.perf_counter()
-    run(rows)
-    dt = time.perf_counter() - t
-    flops, _, _ = prefill_work(w.T, w.Hq, w.D, w.d_r, w.E, w.W, rows=rows)
-    return {"value": flops * w.B / dt / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
-            "sample": f"{len(rows)} of {w.T} query rows (all {w.Hq} heads, evenly spaced) of {w.name}, "
-                      f"fp64 torch-CPU oracle, {dt:.1f} s wall"}
+    ms = total_ms / steps
+    ach = flops / (sum(per) / len(per) * 1e-3) / 1e12
+    print(f"# backward {w.name}: {ms * 1e3:.1f} us/step ({ns} head splits)", file=sys.stderr, flush=True)
+    return {"workload": w.name, "value": round(flops / (ms * 1e-3) / 1e12, 2), "unit": "TFLOP/s",
+            "ms_per_step": round(ms, 5), "algorithmic_flops": flops, "head_splits": ns,
+            "config": {"B": w.B, "T": w.T, "Hq": w.Hq, "Hkv": w.Hkv, "D": w.D, "d_r": w.d_r, "rel_extent": w.E,
+                       "window": w.W, "log_scale": w.log_scale},
+            "roofline": _roofline("mfma", "bwd_dq_kernel+bwd_dkdv_kernel (+delta, reduce)", ach, PEAK_BF16_TFLOPS,
+                                  "TFLOP/s", traffic(f"backward@{w.name}", ("backward.hip", "device_common.hpp")),
+                                  per)}
 
 
 def copy_calibration(nbytes: int = 1 << 30, reps: int = 3):
@@ -397,15 +645,24 @@ def copy_calibration(nbytes: int = 1 << 30, reps: int = 3):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--no-decode", action="store_true")
-    ap.add_argument("--no-extend", action="store_true")
-    ap.add_argument("--no-prologue", action="store_true")
-    ap.add_argument("--no-backward", action="store_true")
+    ap.add_argument("--only", default="", help="comma-separated workloads / extra sections to run")
     ap.add_argument("--copy-calibration", action="store_true")
+    ap.add_argument("--calibration-from", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"))
+    ap.add_argument("--traffic-from", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"))
+    ap.add_argument("--kernel-key")
+    ap.add_argument("--kernel-match")
+    ap.add_argument("--src")
     args = ap.parse_args()
+    if args.calibration_from:
+        calibration_from_counters(*args.calibration_from)
+        return
+    if args.traffic_from:
+        traffic_from_counters(args.traffic_from[0], args.traffic_from[1], args.kernel_key,
+                              args.kernel_match.split(","), args.src.split(","))
+        return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU only: the relative-attention kernels run on a single MI355X "
               "and this build has no multi-GPU path (--gpus must be 1)", file=sys.stderr)
@@ -421,112 +678,34 @@ def main():
         copy_calibration()
         return
 
-    w, flops, ms_step, kernel_ms, per = bench_prefill(args.steps, args.warmup)
-    print(f"# prefill {w.name}: {ms_step * 1e3:.1f} us/step, kernel {kernel_ms * 1e3:.1f} us "
-          f"(min {min(per) * 1e3:.1f}, max {max(per) * 1e3:.1f})", file=sys.stderr, flush=True)
-    value = flops / (ms_step * 1e-3) / 1e12
-    achieved = flops / (kernel_ms * 1e-3) / 1e12
-    line = {
-        "metric": "relative-attention prefill TFLOP/s + decode KV GB/s (% of MI355X peak)",
-        "value": round(value, 2),
-        "unit": "TFLOP/s",
-        "n_gpus": 1,
-        "steps": args.steps,
-        "warmup": args.warmup,
-        "ms_per_step": round(ms_step, 5),
-        "higher_is_better": True,
-        "scaling": "weak",
-        "vs_baseline": None,
-        "dtype": "bf16",
-        "data": "synthetic",
-        "config": {"workload": w.name, "B": w.B, "T": w.T, "Hq": w.Hq, "Hkv": w.Hkv, "D": w.D, "d_r": w.d_r,
-                   "rel_extent": w.E, "window": w.W, "log_scale": w.log_scale, "alpha": "1/sqrt(128)",
-                   "algorithmic_flops": flops},
-        "roofline": {"bound": "mfma", "kernel": PREFILL_KERNEL, "achieved": round(achieved, 2),
-                     "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
-                     "traffic": _traffic(PREFILL_KERNEL, _src_hash("prefill.hip", "device_common.hpp")),
-                     "avg_launch_us": round(kernel_ms * 1e3, 2)},
-    }
-    if not args.no_decode:
-        dw, nbytes, kv, d_ms, d_kernel_ms, ns = bench_decode(args.steps, args.warmup)
-        gbps = nbytes / (d_ms * 1e-3) / 1e9
-        kgbps = nbytes / (d_kernel_ms * 1e-3) / 1e9
-        print(f"# decode {dw.name}: {d_ms * 1e3:.1f} us/step ({ns} splits)", file=sys.stderr, flush=True)
-        line["decode"] = {"workload": dw.name, "value": round(gbps, 1), "unit": "GB/s", "ms_per_step": round(d_ms, 5),
-                          "num_splits": ns, "algorithmic_bytes": nbytes,
-                          "roofline": {"bound": "hbm", "kernel": DECODE_KERNEL + "+merge", "achieved": round(kgbps, 1),
-                                       "peak": PEAK_HBM_GBPS, "unit": "GB/s",
-                                       "frac": round(kgbps / PEAK_HBM_GBPS, 4),
-                                       "traffic": _traffic(DECODE_KERNEL, _src_hash("decode.hip", "device_common.hpp", "mx_common.hpp")),
-                                       "avg_launch_us": round(d_kernel_ms * 1e3, 2)}}
-    if not args.no_decode:
-        pw, p_bytes, p_ms, p_kernel_ms, p_ns = bench_decode_paged(args.steps, args.warmup)
-        print(f"# decode {pw.name}: {p_ms * 1e3:.1f} us/step ({p_ns} splits)", file=sys.stderr, flush=True)
-        pk = p_bytes / (p_kernel_ms * 1e-3) / 1e9
-        line["decode_paged"] = {"workload": pw.name, "value": round(p_bytes / (p_ms * 1e-3) / 1e9, 1), "unit": "GB/s",
-                                "ms_per_step": round(p_ms, 5), "num_splits": p_ns, "algorithmic_bytes": p_bytes,
-                                "roofline": {"bound": "hbm", "kernel": DECODE_KERNEL + " (paged)+merge",
-                                             "achieved": round(pk, 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
-                                             "frac": round(pk / PEAK_HBM_GBPS, 4),
-                                             "traffic": _traffic(DECODE_KERNEL + "_paged",
-                                                                 _src_hash("decode.hip", "device_common.hpp", "mx_common.hpp")),
-                                             "avg_launch_us": round(p_kernel_ms * 1e3, 2)}}
-    if not args.no_decode:
-        mw, m_bytes, m_ms, m_kernel_ms, m_ns = bench_decode_mx(args.steps, args.warmup)
-        print(f"# decode {mw.name} (MXFP8 K/V): {m_ms * 1e3:.1f} us/step ({m_ns} splits)", file=sys.stderr, flush=True)
-        mk = m_bytes / (m_kernel_ms * 1e-3) / 1e9
-        line["decode_mx"] = {"workload": mw.name + " (MXFP8 K/V)", "value": round(m_bytes / (m_ms * 1e-3) / 1e9, 1),
-                             "unit": "GB/s", "ms_per_step": round(m_ms, 5), "num_splits": m_ns,
-                             "algorithmic_bytes": m_bytes, "dtype": "mxfp8 K/V, bf16 q/out",
-                             "roofline": {"bound": "hbm", "kernel": DECODE_KERNEL + " (MXFP8)+merge",
-                                          "achieved": round(mk, 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
-                                          "frac": round(mk / PEAK_HBM_GBPS, 4),
-                                          "traffic": _traffic(DECODE_KERNEL + "_mx",
-                                                              _src_hash("decode.hip", "device_common.hpp", "mx_common.hpp")),
-                                          "avg_launch_us": round(m_kernel_ms * 1e3, 2)}}
-    if not args.no_extend:
-        ew, e_flops, e_ms, e_kernel_ms = bench_extend(args.steps, args.warmup)
-        print(f"# extend {ew.name}: {e_ms * 1e3:.1f} us/step", file=sys.stderr, flush=True)
-        e_ach = e_flops / (e_kernel_ms * 1e-3) / 1e12
-        line["extend"] = {"workload": ew.name, "value": round(e_flops / (e_ms * 1e-3) / 1e12, 2), "unit": "TFLOP/s",
-                          "ms_per_step": round(e_ms, 5), "algorithmic_flops": e_flops,
-                          "config": {"B": ew.B, "kv_len": ew.T, "new_rows": ew.n_new, "page_size": ew.page_size,
-                                     "Hq": ew.Hq, "Hkv": ew.Hkv, "d_r": ew.d_r, "rel_extent": ew.E, "window": ew.W},
-                          "roofline": {"bound": "mfma", "kernel": "prefill_kernel (extend)",
-                                       "achieved": round(e_ach, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                                       "frac": round(e_ach / PEAK_BF16_TFLOPS, 4),
-                                       "traffic": _traffic("prefill_kernel_extend",
-                                                           _src_hash("prefill.hip", "device_common.hpp")),
-                                       "avg_launch_us": round(e_kernel_ms * 1e3, 2)}}
-    if not args.no_prologue:
-        gw, g_bytes, g_ms, g_kernel_ms = bench_prologue(args.steps, args.warmup)
-        print(f"# prologue {gw.name}: {g_ms * 1e3:.1f} us/step", file=sys.stderr, flush=True)
-        gk = g_bytes / (g_kernel_ms * 1e-3) / 1e9
-        line["prologue"] = {"workload": gw.name, "value": round(g_bytes / (g_ms * 1e-3) / 1e9, 1), "unit": "GB/s",
-                            "ms_per_step": round(g_ms, 5), "algorithmic_bytes": g_bytes,
-                            "config": {"B": gw.B, "tokens": gw.B * gw.n_new, "Hq": gw.Hq, "Hkv": gw.Hkv, "D": gw.D,
-                                       "conv_width": 4, "page_size": gw.page_size},
-                            "roofline": {"bound": "hbm", "kernel": "prologue_kernel", "achieved": round(gk, 1),
-                                         "peak": PEAK_HBM_GBPS, "unit": "GB/s", "frac": round(gk / PEAK_HBM_GBPS, 4),
-                                         "traffic": _traffic("prologue_kernel",
-                                                             _src_hash("prologue.hip", "device_common.hpp", "mx_common.hpp")),
-                                         "avg_launch_us": round(g_kernel_ms * 1e3, 2)}}
-    if not args.no_backward:
-        bw, b_flops, b_ms, b_kernel_ms, b_ns = bench_backward(args.steps, args.warmup)
-        print(f"# backward {bw.name}: {b_ms * 1e3:.1f} us/step ({b_ns} head splits)", file=sys.stderr, flush=True)
-        b_ach = b_flops / (b_kernel_ms * 1e-3) / 1e12
-        line["backward"] = {"workload": bw.name, "value": round(b_flops / (b_ms * 1e-3) / 1e12, 2),
-                            "unit": "TFLOP/s", "ms_per_step": round(b_ms, 5), "algorithmic_flops": b_flops,
-                            "head_splits": b_ns,
-                            "config": {"B": bw.B, "T": bw.T, "Hq": bw.Hq, "Hkv": bw.Hkv, "D": bw.D, "d_r": bw.d_r,
-                                       "rel_extent": bw.E, "window": bw.W, "log_scale": bw.log_scale},
-                            "roofline": {"bound": "mfma", "kernel": "bwd_dq_kernel+bwd_dkdv_kernel (+delta, reduce)",
-                                         "achieved": round(b_ach, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                                         "frac": round(b_ach / PEAK_BF16_TFLOPS, 4),
-                                         "traffic": _traffic("backward", _src_hash("backward.hip", "device_common.hpp")),
-                                         "avg_launch_us": round(b_kernel_ms * 1e3, 2)}}
-    if not args.no_cpu_baseline:
-        line["cpu_baseline"] = cpu_baseline()
+    only = set(s for s in args.only.split(",") if s)
+    want = lambda n: not only or n in only  # noqa: E731
+    cpu = not args.no_cpu_baseline
+
+    line = {"metric": METRIC}
+    objs = {}
+    for name in PREFILL_WORKLOADS:
+        if want(name):
+            objs[name] = bench_prefill(name, args.steps, args.warmup, cpu)
+    for name in DECODE_WORKLOADS:
+        if want(name):
+            objs[name] = bench_decode(name, args.steps, args.warmup, cpu)
+    if HEADLINE in objs:
+        h = objs.pop(HEADLINE)
+        line.update({"value": h["value"], "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
+                     "warmup": args.warmup, "ms_per_step": h["ms_per_step"], "higher_is_better": True,
+                     "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+                     "config": h["config"], "roofline": h["roofline"]})
+        if "cpu_baseline" in h:
+            line["cpu_baseline"] = h["cpu_baseline"]
+    else:
+        line.update({"n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "note": "headline not run (--only)"})
+    line.update(objs)
+    extras = {"decode_paged": bench_decode_paged, "decode_mx": bench_decode_mx, "extend": bench_extend,
+              "prologue": bench_prologue, "backward": bench_backward}
+    for key in EXTRA:
+        if want(key):
+            line[key] = extras[key](args.steps, args.warmup)
     print(json.dumps(line), flush=True)
 
 

@@ -603,6 +603,19 @@ __device__ __attribute__((aligned(16))) const __bf16 kZeroPRow[kMaxDr] = {};
 
 template <int V> struct IntC { static constexpr int value = V; };
 
+// v_max3_f32 without the quieting of NaN inputs that fmaxf implies (callers
+// pass no NaN)
+__device__ __forceinline__ float max3_f32(float x, float y, float z) {
+  float r;
+  asm("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(x), "v"(y), "v"(z));
+  return r;
+}
+
+// RAWQK (alpha > 0): tiles without bias keep the raw scores q.k; the row
+// maximum is scaled once and the exponent takes c1 = s*alpha*log2(e) in
+// place of c2, which saves a multiply per score (and one of two score
+// accumulation chains).
+template <bool RAWQK>
 __global__ __launch_bounds__(512, 1) void prefill_dma_kernel(PrefillArgs p, int n_qt, int n_items) {
   using C = DmaCfg;
   using T = __bf16;
@@ -694,7 +707,7 @@ __global__ __launch_bounds__(512, 1) void prefill_dma_kernel(PrefillArgs p, int 
   auto issue_kp = [&](int kt) {
     const int buf = kt & 1;
     dma16s(kseq, kv_off(kt) + kcol, __builtin_amdgcn_readfirstlane(lds0 + C::OFF_K + buf * C::TILEB));
-    if (E > 0) {
+    if (E > 0 && max(0, q0 - (kt * N + N - 1)) < E) {  // only tiles with bias read their P chunk
       const int d = (chunk0(kt) - 1) * N + drow;
       const T* src = unsigned(d) < unsigned(E)
                          ? reinterpret_cast<const T*>(reinterpret_cast<const char*>(pcg) + unsigned(d) * unsigned(2 * d_r) + pcol)
@@ -788,13 +801,14 @@ __global__ __launch_bounds__(512, 1) void prefill_dma_kernel(PrefillArgs p, int 
     }
   };
   // p = exp2(c2*y - c2*m), its row sum, and the bf16 PV operand
-  auto exps = [&](const f32x16& s, float nm, bf16x8 (&pb)[2], float& psum) {
+  auto exps = [&](const f32x16& s, float cs, float nm, bf16x8 (&pb)[2], float& psum) {
     f32x16 pe;
 #pragma unroll
-    for (int v = 0; v < 16; ++v) pe[v] = fast_exp2(fmaf(s[v], c2, nm));
-    psum = 0.0f;
+    for (int v = 0; v < 16; ++v) pe[v] = fast_exp2(fmaf(s[v], cs, nm));
+    float s8[8];
 #pragma unroll
-    for (int v = 0; v < 16; ++v) psum += pe[v];
+    for (int v = 0; v < 8; ++v) s8[v] = pe[2 * v] + pe[2 * v + 1];
+    psum = ((s8[0] + s8[1]) + (s8[2] + s8[3])) + ((s8[4] + s8[5]) + (s8[6] + s8[7]));
 #pragma unroll
     for (int c16 = 0; c16 < 2; ++c16)
 #pragma unroll
@@ -841,8 +855,10 @@ __global__ __launch_bounds__(512, 1) void prefill_dma_kernel(PrefillArgs p, int 
     } else {
 #pragma unroll
       for (int kk = 0; kk < D / 16; ++kk) mma32(frag_kp(kt_b, kk), qreg[kk], s_cur);
+      if constexpr (!RAWQK) {
 #pragma unroll
-      for (int v = 0; v < 16; ++v) s_cur[v] *= qk_scale;
+        for (int v = 0; v < 16; ++v) s_cur[v] *= qk_scale;
+      }
     }
     if (mask_of(kt_lo)) apply_mask(kt_lo, s_cur);
   }
@@ -857,16 +873,27 @@ __global__ __launch_bounds__(512, 1) void prefill_dma_kernel(PrefillArgs p, int 
   // the loop runs in two parts; the last tile (no next scores) is peeled, and
   // each part is unrolled by two so every LDS address is a lane offset plus a
   // constant.
-  auto begin_tile = [&](int kt, f32x16& s) {
+  // scores of tile kt are raw (units of q.k) when it has no bias
+  auto raw_of = [&](int kt) { return RAWQK && !band_of(kt); };
+  auto begin_tile = [&](int kt, f32x16& s, float& cs) {
     __syncthreads();  // K/P of tile kt+1 and V of tile kt are in LDS; all waves are past iteration kt-1
     if (kt + 2 <= kt_hi) issue_kp(kt + 2);
     if (kt + 1 <= kt_hi) issue_v(kt + 1);
     if (kt > kt_lo && mask_of(kt)) apply_mask(kt, s);
-    // row maximum of tile kt and the (rare) lazy rescale
-    float mx = -INFINITY;
-#pragma unroll
-    for (int v = 0; v < 16; ++v) mx = fmaxf(mx, s[v]);
-    mx = pair_max32(mx);
+    // row maximum of tile kt (scores are never NaN: v_max3 without the
+    // quieting fmaxf would add) and the (rare) lazy rescale
+    const float m0 = max3_f32(s[0], s[1], s[2]), m1 = max3_f32(s[3], s[4], s[5]);
+    const float m2 = max3_f32(s[6], s[7], s[8]), m3 = max3_f32(s[9], s[10], s[11]);
+    const float m5 = max3_f32(s[12], s[13], s[14]);
+    float mx = max3_f32(max3_f32(m0, m1, m2), max3_f32(m3, m5, s[15]), -INFINITY);
+    {
+      const unsigned u = __float_as_uint(mx);
+      const auto r2 = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+      mx = max3_f32(__uint_as_float(r2[0]), __uint_as_float(r2[1]), -INFINITY);
+    }
+    const bool raw = raw_of(kt);
+    if (raw) mx *= qk_scale;  // in units of c2
+    cs = raw ? p.c1 : c2;
     if (__builtin_amdgcn_ballot_w64(mx > m_run + lazy) != 0) {
       const float m_new = fmaxf(m_run, mx);
       const float corr = fast_exp2(c2 * (m_run - m_new));
@@ -882,30 +909,40 @@ __global__ __launch_bounds__(512, 1) void prefill_dma_kernel(PrefillArgs p, int 
   // one iteration whose next tile has no bias; PAR = kt & 1
   auto plain_step = [&](auto par, f32x16& s, f32x16& s_nx, int kt) {
     constexpr int PAR = decltype(par)::value, NP = PAR ^ 1;
-    const float nm = begin_tile(kt, s);
+    float cs;
+    const float nm = begin_tile(kt, s, cs);
     const unsigned char* kt_b = smem + C::OFF_K + NP * C::TILEB;
     const unsigned char* vt_b = smem + C::OFF_V + PAR * C::TILEB;
-    f32x16 s_odd = zero16();
-    s_nx = zero16();
-#pragma unroll
-    for (int kk = 0; kk < D / 16; ++kk) {
-      const bf16x8 kf = frag_kp(kt_b, kk);
-      if (kk & 1) mma32(kf, qreg[kk], s_odd);
-      else mma32(kf, qreg[kk], s_nx);
-    }
     bf16x8 pb[2];
     float psum;
-    exps(s, nm, pb, psum);
-    pv(vt_b, pb);
+    if constexpr (RAWQK) {  // raw scores of tile kt+1: one chain, no scaling
+      s_nx = zero16();
 #pragma unroll
-    for (int v = 0; v < 16; ++v) s_nx[v] = (s_nx[v] + s_odd[v]) * qk_scale;
+      for (int kk = 0; kk < D / 16; ++kk) mma32(frag_kp(kt_b, kk), qreg[kk], s_nx);
+      exps(s, cs, nm, pb, psum);
+      pv(vt_b, pb);
+    } else {
+      f32x16 s_odd = zero16();
+      s_nx = zero16();
+#pragma unroll
+      for (int kk = 0; kk < D / 16; ++kk) {
+        const bf16x8 kf = frag_kp(kt_b, kk);
+        if (kk & 1) mma32(kf, qreg[kk], s_odd);
+        else mma32(kf, qreg[kk], s_nx);
+      }
+      exps(s, cs, nm, pb, psum);
+      pv(vt_b, pb);
+#pragma unroll
+      for (int v = 0; v < 16; ++v) s_nx[v] = (s_nx[v] + s_odd[v]) * qk_scale;
+    }
     l_run += psum;
     dma_wait();  // this wave's parts of the next tiles have landed
   };
   // one iteration whose next tile has bias
   auto band_step = [&](auto par, f32x16& s, f32x16& s_nx, int kt) {
     constexpr int PAR = decltype(par)::value, NP = PAR ^ 1;
-    const float nm = begin_tile(kt, s);
+    float cs;
+    const float nm = begin_tile(kt, s, cs);
     const unsigned char* kt_b = smem + C::OFF_K + NP * C::TILEB;
     const unsigned char* pt_b = smem + C::OFF_P + NP * C::TILEB;
     const unsigned char* vt_b = smem + C::OFF_V + PAR * C::TILEB;
@@ -917,7 +954,7 @@ __global__ __launch_bounds__(512, 1) void prefill_dma_kernel(PrefillArgs p, int 
     for (int kk = 0; kk < D / 16; ++kk) mma32(frag_kp(kt_b, kk), qreg[kk], s_nx);
     bf16x8 pb[2];
     float psum;
-    exps(s, nm, pb, psum);
+    exps(s, cs, nm, pb, psum);
     put_chunk(NP, racc);
     pv(vt_b, pb);
     shear_add(NP, s_nx);
@@ -948,10 +985,11 @@ __global__ __launch_bounds__(512, 1) void prefill_dma_kernel(PrefillArgs p, int 
   if (kt < kt_hi && !band_of(kt_lo)) first_chunk(kt + 1);
   run(band_step, kt_hi);
   {
-    const float nm = begin_tile(kt, s_cur);
+    float cs;
+    const float nm = begin_tile(kt, s_cur, cs);
     bf16x8 pb[2];
     float psum;
-    exps(s_cur, nm, pb, psum);
+    exps(s_cur, cs, nm, pb, psum);
     pv(smem + C::OFF_V + (kt & 1) * C::TILEB, pb);
     l_run += psum;
   }
@@ -988,8 +1026,12 @@ hipError_t launch_prefill_dma(const PrefillArgs& a, hipStream_t stream) {
   const int n_qt = (a.T + 31) / 32;
   const long long n_items = (long long)n_qt * a.B * a.Hkv * (a.Hq / a.Hkv / 8);
   if (n_items > 0x7fffffffLL) return hipErrorInvalidConfiguration;
-  hipLaunchKernelGGL(prefill_dma_kernel, dim3((unsigned)n_items), dim3(DmaCfg::THREADS), 0, stream, a, n_qt,
-                     (int)n_items);
+  if (a.c1 > 0.0f)
+    hipLaunchKernelGGL(prefill_dma_kernel<true>, dim3((unsigned)n_items), dim3(DmaCfg::THREADS), 0, stream, a, n_qt,
+                       (int)n_items);
+  else
+    hipLaunchKernelGGL(prefill_dma_kernel<false>, dim3((unsigned)n_items), dim3(DmaCfg::THREADS), 0, stream, a,
+                       n_qt, (int)n_items);
   return hipGetLastError();
 }
 
