@@ -157,6 +157,15 @@ def _decode(lib, **kw):
                                a["W"], a["ls"], a["ns"], a["ws"], a["wsb"], None)
 
 
+def test_decode_with_no_sequences_is_a_no_op(lib):
+    """B == 0 plans without dividing by the workgroup count and returns RA_OK
+    before touching the workspace (a division by zero here once killed the
+    process)."""
+    rc, ns, need = _plan(lib, 0, 300, 16, 2, E=64)
+    assert rc == RA_OK and ns >= 1
+    assert _decode(lib, B=0) == RA_OK
+
+
 def test_decode_workspace_errors(lib):
     assert _decode(lib) == RA_ERR_WORKSPACE and "NULL" in _err(lib)
     assert _decode(lib, ws=FAKE + 512 + 16, wsb=1 << 30) == RA_ERR_WORKSPACE and "256-byte" in _err(lib)

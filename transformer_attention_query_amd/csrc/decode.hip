@@ -811,7 +811,7 @@ DecodePlan plan_decode(int B, int L, int Hq, int Hkv, int num_splits_req, int wi
     // about 3 us of ~113; counts that do not divide over the CUs (3, 6
     // splits) are slower than either.
     const long long wgs_per_split = (long long)B * Hkv * pl.n_hg;
-    long long want = (256 + wgs_per_split - 1) / wgs_per_split;
+    long long want = wgs_per_split > 0 ? (256 + wgs_per_split - 1) / wgs_per_split : 1;  // B == 0: a no-op call
     const long long cap = (vis + 2 * kDecSplitQuantum - 1) / (2 * kDecSplitQuantum);
     if (want > cap) want = cap;
     ns = (int)(want < 1 ? 1 : want);
