@@ -32,7 +32,9 @@
  * - Work is enqueued on `stream` (a hipStream_t; NULL = the legacy default
  *   stream) and the call returns without synchronising, copying to the host or
  *   reading device data on the host, so calls can be captured in a hipGraph.
- *   The library allocates no device memory and keeps no per-pointer state.
+ *   The library allocates no device memory and keeps no per-pointer state;
+ *   the one device buffer it holds is the fixed decode scratch of
+ *   rel_attn_decode_noalloc (16 MiB per device, from the library's load).
  * - Errors: argument errors are detected on the host before any HIP call and
  *   return a negative code; a failed launch returns RA_ERR_HIP.  In both cases
  *   rel_attn_last_error() returns a message for the calling thread.  The
@@ -188,6 +190,26 @@ int rel_attn_decode(const void* q, const void* k, const void* v, const void* r,
                     int B, int L, int Hq, int Hkv, int D, int d_r,
                     float alpha, int rel_extent, int window, int log_scale,
                     int num_splits, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * rel_attn_decode without the workspace, for callers that cannot allocate
+ * device memory: code under HIP graph capture, tight serving loops, harnesses
+ * that forbid allocation.  Arguments and results are those of
+ * rel_attn_decode (num_splits from rel_attn_decode_plan, or 0); the split
+ * partials and bias rows go instead to a fixed scratch array of 16 MiB per
+ * device, held by the library from its load to the end of the process.  A
+ * shape whose plan needs more (workspace_bytes of rel_attn_decode_plan above
+ * 16 MiB) returns RA_ERR_WORKSPACE.  The first call on a device looks up that
+ * device's copy of the array (hipGetSymbolAddress; nothing is allocated).
+ * All calls on one device share its array: calls that overlap on a device
+ * (on different streams, or from threads without ordering) race and their
+ * results are undefined; calls on one stream are ordered and safe.
+ */
+int rel_attn_decode_noalloc(const void* q, const void* k, const void* v, const void* r,
+                            const void* P_cols, void* out, float* lse, int dtype,
+                            int B, int L, int Hq, int Hkv, int D, int d_r,
+                            float alpha, int rel_extent, int window, int log_scale,
+                            int num_splits, void* stream);
 
 /*
  * Paged decode: one query token per sequence at position kv_len[b]-1 of its

@@ -184,6 +184,44 @@ def test_decode_rejects_bad_arguments(lib, kw, code):
     assert _decode(lib, **kw) == code
 
 
+def _decode_noalloc(lib, **kw):
+    a = dict(q=FAKE, k=FAKE + 16, v=FAKE + 32, r=FAKE + 48, P=FAKE + 64, out=FAKE + 80, lse=None,
+             dtype=RA_BF16, B=2, L=300, Hq=16, Hkv=2, D=128, d_r=128, alpha=0.1, E=64, W=0, ls=0, ns=0)
+    a.update(kw)
+    return lib.rel_attn_decode_noalloc(a["q"], a["k"], a["v"], a["r"], a["P"], a["out"], a["lse"], a["dtype"],
+                                       a["B"], a["L"], a["Hq"], a["Hkv"], a["D"], a["d_r"], a["alpha"], a["E"],
+                                       a["W"], a["ls"], a["ns"], None)
+
+
+NOALLOC_SCRATCH = 16 << 20
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(L=0), RA_ERR_INVALID_ARG),
+    (dict(ns=-1), RA_ERR_INVALID_ARG),
+    (dict(dtype=0), RA_ERR_INVALID_ARG),
+    (dict(D=256), RA_ERR_UNSUPPORTED),
+    (dict(v=None), RA_ERR_INVALID_ARG),
+    (dict(out=FAKE), RA_ERR_INVALID_ARG),
+])
+def test_decode_noalloc_rejects_bad_arguments(lib, kw, code):
+    assert _decode_noalloc(lib, **kw) == code
+
+
+def test_decode_noalloc_rejects_shapes_beyond_its_scratch(lib):
+    """A plan that needs more than the fixed scratch is refused on the host
+    (before any HIP call), with the sizes in the message; B == 0 is a no-op."""
+    B, L, Hq, Hkv, E = 512, 4096, 32, 2, 1024
+    rc, ns, need = _plan(lib, B, L, Hq, Hkv, E=E)
+    assert rc == RA_OK and need > NOALLOC_SCRATCH
+    assert _decode_noalloc(lib, B=B, L=L, Hq=Hq, Hkv=Hkv, E=E) == RA_ERR_WORKSPACE
+    assert str(need) in _err(lib) and str(NOALLOC_SCRATCH) in _err(lib)
+    assert _decode_noalloc(lib, B=0) == RA_OK
+    # the measured decode shapes fit it
+    for B, L in ((64, 8192), (1, 1 << 20)):
+        assert _plan(lib, B, L, 16, 2, E=1024)[2] <= NOALLOC_SCRATCH
+
+
 def test_rel_logits_rejects_bad_arguments(lib):
     f = lib.rel_logits
     assert f(FAKE, FAKE + 16, FAKE + 32, 3, 10, 2, 32, 64, 0, 10, None) == RA_ERR_INVALID_ARG

@@ -13,6 +13,7 @@ from .binding import (  # noqa: F401
     backward,
     backward_plan,
     decode,
+    decode_noalloc,
     decode_mx,
     decode_paged,
     decode_plan,

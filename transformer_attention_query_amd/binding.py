@@ -16,8 +16,8 @@ from typing import Optional, Tuple
 
 import torch
 
-__all__ = ["RelAttnError", "library_path", "load_library", "prefill", "extend", "decode", "decode_paged",
-           "decode_plan",
+__all__ = ["RelAttnError", "library_path", "load_library", "prefill", "extend", "decode", "decode_noalloc",
+           "decode_paged", "decode_plan",
            "rel_logits", "scale_factor", "version"]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -55,6 +55,9 @@ def _declare(lib):
     lib.rel_attn_decode.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32,
                                     f32, i32, i32, i32, i32, vp, sz, vp]
     lib.rel_attn_decode.restype = i32
+    lib.rel_attn_decode_noalloc.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32,
+                                            f32, i32, i32, i32, i32, vp]
+    lib.rel_attn_decode_noalloc.restype = i32
     lib.rel_attn_decode_paged.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, vp, vp, i32, i32, i32,
                                           i32, i32, i32, i32, f32, i32, i32, i32, i32, vp, sz, vp]
     lib.rel_attn_decode_paged.restype = i32
@@ -311,6 +314,54 @@ def decode(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, r: Optional[torch.
                                _DTYPE_CODE[dt], B, L, Hq, Hkv, D, d_r, float(alpha), int(rel_extent),
                                int(window), 1 if log_scale else 0, ns, _ptr(workspace),
                                workspace.numel() * workspace.element_size(), _stream(dev)))
+    return out, lse
+
+
+def decode_noalloc(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, r: Optional[torch.Tensor],
+                   P_cols: Optional[torch.Tensor], alpha: float, rel_extent: int, window: int = 0,
+                   log_scale: bool = False, num_splits: int = 0, return_lse: bool = True,
+                   out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None
+                   ) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+    """``decode`` through rel_attn_decode_noalloc: no workspace, the library's
+    fixed per-device scratch instead (calls that overlap on one GPU race).
+    ``out`` / ``lse`` may be passed preallocated; otherwise they are created
+    here (the C call itself allocates nothing); lse is skipped when
+    ``return_lse`` is false and none is passed."""
+    lib = load_library()
+    dev = q.device
+    dt = q.dtype
+    if dt not in _DTYPE_CODE:
+        raise TypeError(f"unsupported dtype {dt}")
+    _need(q, "q", dt, dev, 3)
+    _need(k, "k", dt, dev, 4)
+    _need(v, "v", dt, dev, 4)
+    B, Hq, D = q.shape
+    L, Hkv = k.shape[1], k.shape[2]
+    if k.shape != (B, L, Hkv, D) or v.shape != k.shape:
+        raise ValueError(f"k/v shape {tuple(k.shape)} does not match q {tuple(q.shape)}")
+    d_r = 0
+    if rel_extent > 0:
+        _need(r, "r", dt, dev, 3)
+        _need(P_cols, "P_cols", dt, dev, 2)
+        d_r = r.shape[2]
+        if r.shape[:2] != (B, Hq):
+            raise ValueError(f"r shape {tuple(r.shape)} does not match q")
+        if P_cols.shape != (rel_extent, d_r):
+            raise ValueError(f"P_cols must be [rel_extent={rel_extent}, d_r={d_r}], got {tuple(P_cols.shape)}")
+    else:
+        r = None
+        P_cols = None
+    if out is None:
+        out = torch.empty_like(q)
+    else:
+        _need(out, "out", dt, dev, 3)
+    if lse is not None:
+        _need(lse, "lse", torch.float32, dev, 2)
+    elif return_lse:
+        lse = torch.empty(B, Hq, dtype=torch.float32, device=dev)
+    _check(lib.rel_attn_decode_noalloc(_ptr(q), _ptr(k), _ptr(v), _ptr(r), _ptr(P_cols), _ptr(out), _ptr(lse),
+                                       _DTYPE_CODE[dt], B, L, Hq, Hkv, D, d_r, float(alpha), int(rel_extent),
+                                       int(window), 1 if log_scale else 0, int(num_splits), _stream(dev)))
     return out, lse
 
 

@@ -10,6 +10,7 @@
 #include <cstdarg>
 #include <cstdint>
 #include <cstdio>
+#include <mutex>
 
 #include "relattn_internal.hpp"
 
@@ -64,6 +65,86 @@ int check_common(int dtype, int B, int Tl, int Hq, int Hkv, int D, int d_r, floa
     if (d_r <= 0 || d_r % 16 != 0 || d_r > relattn::kMaxDr)
       return fail(RA_ERR_UNSUPPORTED, "d_r = %d: supported values are multiples of 16 in [16, 128]", d_r);
   }
+  return RA_OK;
+}
+
+// ---- decode: the checks (host only, before any HIP call) and the launch,
+// shared by rel_attn_decode and rel_attn_decode_noalloc
+int decode_check(const void* q, const void* k, const void* v, const void* r, const void* P_cols, void* out,
+                 float* lse, int dtype, int B, int L, int Hq, int Hkv, int D, int d_r, float alpha, int rel_extent,
+                 int window, int log_scale, int num_splits, relattn::DecodePlan* pl) {
+  int rc = check_common(dtype, B, L, Hq, Hkv, D, d_r, alpha, rel_extent, window, log_scale, "L");
+  if (rc) return rc;
+  if (L == 0) return fail(RA_ERR_INVALID_ARG, "L = 0: the cache must hold at least the query's own token");
+  if ((rc = check_ptr(q, "q", true)) || (rc = check_ptr(k, "k", true)) || (rc = check_ptr(v, "v", true)) ||
+      (rc = check_ptr(out, "out", true)) || (rc = check_ptr(lse, "lse", false)) ||
+      (rc = check_ptr(r, "r", rel_extent > 0)) || (rc = check_ptr(P_cols, "P_cols", rel_extent > 0)))
+    return rc;
+  if (out == q || out == k || out == v || out == r) return fail(RA_ERR_INVALID_ARG, "out aliases an input");
+  if (num_splits < 0) return fail(RA_ERR_INVALID_ARG, "num_splits = %d < 0", num_splits);
+  if ((long long)B * L > 0x7fffffffLL)
+    return fail(RA_ERR_UNSUPPORTED, "B * L = %lld too large", (long long)B * L);
+  *pl = relattn::plan_decode(B, L, Hq, Hkv, num_splits, window, rel_extent);
+  return RA_OK;
+}
+
+int decode_launch(const void* q, const void* k, const void* v, const void* r, const void* P_cols, void* out,
+                  float* lse, int dtype, int B, int L, int Hq, int Hkv, int d_r, float alpha, int rel_extent,
+                  int window, int log_scale, const relattn::DecodePlan& pl, void* workspace, void* stream) {
+  const double s = scale_of(log_scale, L);
+  relattn::DecodeArgs a;
+  a.q = q; a.k = k; a.v = v; a.r = r; a.pc = P_cols; a.out = out; a.lse = lse;
+  a.ws = static_cast<float*>(workspace);
+  a.B = B; a.L = L; a.Hq = Hq; a.Hkv = Hkv; a.d_r = rel_extent > 0 ? d_r : 16; a.E = rel_extent; a.W = window;
+  a.c1 = (float)(s * (double)alpha * 1.4426950408889634);
+  a.c2 = (float)(s * 1.4426950408889634);
+  a.n_split = pl.n_split;
+  a.chunk = pl.chunk;
+  a.kv_lo = pl.kv_lo;
+  a.n_hg = pl.n_hg;
+  a.rl_base = pl.rl_base;
+  a.rl_stride = pl.rl_stride;
+  a.rl = reinterpret_cast<const float*>(static_cast<char*>(workspace) + pl.ws_partial_bytes);
+  hipError_t e = relattn::launch_decode(dtype, a, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(RA_ERR_HIP, "decode launch failed: %s", hipGetErrorString(e));
+  return ok();
+}
+
+// ---- the fixed scratch of rel_attn_decode_noalloc: one array per device,
+// held from the library's load to the end of the process.  In host code the
+// array's name stands for the device copy only through hipGetSymbolAddress,
+// which is called once per device (with that device current) and cached.
+constexpr size_t kNoAllocScratchBytes = size_t(16) << 20;
+static __device__ __attribute__((aligned(256))) unsigned char scratch[kNoAllocScratchBytes];
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+int scratch_of_stream(void* stream, void** out) {
+  int cur = 0;
+  hipError_t e = hipGetDevice(&cur);
+  if (e != hipSuccess) return fail(RA_ERR_HIP, "hipGetDevice failed: %s", hipGetErrorString(e));
+  int dev = cur;
+  if (stream != nullptr) {
+    e = hipStreamGetDevice(static_cast<hipStream_t>(stream), &dev);
+    if (e != hipSuccess) return fail(RA_ERR_HIP, "hipStreamGetDevice failed: %s", hipGetErrorString(e));
+  }
+  if (dev < 0 || dev >= kMaxDevices) return fail(RA_ERR_UNSUPPORTED, "device %d: at most %d devices", dev, kMaxDevices);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    if (dev != cur && (e = hipSetDevice(dev)) != hipSuccess)
+      return fail(RA_ERR_HIP, "hipSetDevice(%d) failed: %s", dev, hipGetErrorString(e));
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (dev != cur) {
+      const hipError_t e2 = hipSetDevice(cur);
+      if (e == hipSuccess && e2 != hipSuccess) e = e2;
+    }
+    if (e != hipSuccess || p == nullptr)
+      return fail(RA_ERR_HIP, "hipGetSymbolAddress of the decode scratch failed: %s", hipGetErrorString(e));
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
   return RA_OK;
 }
 
@@ -370,16 +451,10 @@ int rel_attn_decode(const void* q, const void* k, const void* v, const void* r, 
                     float* lse, int dtype, int B, int L, int Hq, int Hkv, int D, int d_r, float alpha,
                     int rel_extent, int window, int log_scale, int num_splits, void* workspace,
                     size_t workspace_bytes, void* stream) {
-  int rc = check_common(dtype, B, L, Hq, Hkv, D, d_r, alpha, rel_extent, window, log_scale, "L");
+  relattn::DecodePlan pl;
+  int rc = decode_check(q, k, v, r, P_cols, out, lse, dtype, B, L, Hq, Hkv, D, d_r, alpha, rel_extent, window,
+                        log_scale, num_splits, &pl);
   if (rc) return rc;
-  if (L == 0) return fail(RA_ERR_INVALID_ARG, "L = 0: the cache must hold at least the query's own token");
-  if ((rc = check_ptr(q, "q", true)) || (rc = check_ptr(k, "k", true)) || (rc = check_ptr(v, "v", true)) ||
-      (rc = check_ptr(out, "out", true)) || (rc = check_ptr(lse, "lse", false)) ||
-      (rc = check_ptr(r, "r", rel_extent > 0)) || (rc = check_ptr(P_cols, "P_cols", rel_extent > 0)))
-    return rc;
-  if (out == q || out == k || out == v || out == r) return fail(RA_ERR_INVALID_ARG, "out aliases an input");
-  if (num_splits < 0) return fail(RA_ERR_INVALID_ARG, "num_splits = %d < 0", num_splits);
-  relattn::DecodePlan pl = relattn::plan_decode(B, L, Hq, Hkv, num_splits, window, rel_extent);
   if (B == 0) return ok();
   if (workspace == nullptr) return fail(RA_ERR_WORKSPACE, "workspace is NULL (need %zu bytes)", pl.ws_bytes);
   if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0)
@@ -387,26 +462,25 @@ int rel_attn_decode(const void* q, const void* k, const void* v, const void* r, 
   if (workspace_bytes < pl.ws_bytes)
     return fail(RA_ERR_WORKSPACE, "workspace of %zu bytes is smaller than the %zu the plan needs", workspace_bytes,
                 pl.ws_bytes);
-  if ((long long)B * L > 0x7fffffffLL)
-    return fail(RA_ERR_UNSUPPORTED, "B * L = %lld too large", (long long)B * L);
+  return decode_launch(q, k, v, r, P_cols, out, lse, dtype, B, L, Hq, Hkv, d_r, alpha, rel_extent, window, log_scale,
+                       pl, workspace, stream);
+}
 
-  const double s = scale_of(log_scale, L);
-  relattn::DecodeArgs a;
-  a.q = q; a.k = k; a.v = v; a.r = r; a.pc = P_cols; a.out = out; a.lse = lse;
-  a.ws = static_cast<float*>(workspace);
-  a.B = B; a.L = L; a.Hq = Hq; a.Hkv = Hkv; a.d_r = rel_extent > 0 ? d_r : 16; a.E = rel_extent; a.W = window;
-  a.c1 = (float)(s * (double)alpha * 1.4426950408889634);
-  a.c2 = (float)(s * 1.4426950408889634);
-  a.n_split = pl.n_split;
-  a.chunk = pl.chunk;
-  a.kv_lo = pl.kv_lo;
-  a.n_hg = pl.n_hg;
-  a.rl_base = pl.rl_base;
-  a.rl_stride = pl.rl_stride;
-  a.rl = reinterpret_cast<const float*>(static_cast<char*>(workspace) + pl.ws_partial_bytes);
-  hipError_t e = relattn::launch_decode(dtype, a, static_cast<hipStream_t>(stream));
-  if (e != hipSuccess) return fail(RA_ERR_HIP, "decode launch failed: %s", hipGetErrorString(e));
-  return ok();
+int rel_attn_decode_noalloc(const void* q, const void* k, const void* v, const void* r, const void* P_cols,
+                            void* out, float* lse, int dtype, int B, int L, int Hq, int Hkv, int D, int d_r,
+                            float alpha, int rel_extent, int window, int log_scale, int num_splits, void* stream) {
+  relattn::DecodePlan pl;
+  int rc = decode_check(q, k, v, r, P_cols, out, lse, dtype, B, L, Hq, Hkv, D, d_r, alpha, rel_extent, window,
+                        log_scale, num_splits, &pl);
+  if (rc) return rc;
+  if (B == 0) return ok();
+  if (pl.ws_bytes > kNoAllocScratchBytes)
+    return fail(RA_ERR_WORKSPACE, "this decode needs %zu bytes of scratch; the fixed scratch holds %zu (use "
+                "rel_attn_decode with a workspace)", pl.ws_bytes, kNoAllocScratchBytes);
+  void* ws = nullptr;
+  if ((rc = scratch_of_stream(stream, &ws))) return rc;
+  return decode_launch(q, k, v, r, P_cols, out, lse, dtype, B, L, Hq, Hkv, d_r, alpha, rel_extent, window, log_scale,
+                       pl, ws, stream);
 }
 
 int rel_attn_decode_paged(const void* q, const void* k_pages, const void* v_pages, const void* r,
