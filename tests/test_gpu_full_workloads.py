@@ -1,8 +1,9 @@
 """GPU parity at the full sizes of the five named workloads, in the launch
-configuration bench.py times.  Where the oracle cannot finish the whole
-output quickly (the 8K sliding-window and 2x32K causal prefills) it checks
-sampled query rows, chosen to include every tile edge, the rel_extent and
-window edges and the last row; decode is compared in full."""
+configuration bench.py times.  The tiny fp32 and 8K sliding-window prefills
+and both decodes are compared over their whole outputs.  The 2x32K causal
+prefill, whose full oracle would take minutes, is compared on every 16th
+query row counted from the last, plus every tile edge, the rel_extent edge
+and the first rows."""
 
 import random
 
@@ -32,11 +33,11 @@ def test_prefill_workload(name):
     out, lse = ra.prefill(xd["q"], xd["k"], xd["v"], xd["r"], xd["P_cols"], w.alpha, w.E, w.W, w.log_scale)
     torch.cuda.synchronize()
     del xd
-    if w.T <= 256:
+    if w.T <= 8192:
         ref, lref = oracle.prefill(x["q"], x["k"], x["v"], x["r"], x["P"], w.alpha, w.E, w.W, w.log_scale)
         assert_close(out, ref, x["q"].dtype, name, lse, lref)
         return
-    rows = _rows(w.T, 24, 1)
+    rows = sorted(set(_rows(w.T, 24, 1)) | set(range(w.T - 1, -1, -16)))
     ref, lref = oracle.prefill(x["q"], x["k"], x["v"], x["r"], x["P"], w.alpha, w.E, w.W, w.log_scale, rows=rows)
     assert_close(out[:, rows], ref, x["q"].dtype, name, lse[:, :, rows], lref)
 

@@ -66,10 +66,11 @@ def test_prefill_matches_oracle(case):
 
 @pytest.mark.parametrize("heads", [(8, 2), (8, 1)], ids=["G4", "G8"])
 @pytest.mark.parametrize("W", [0, 300])
-@pytest.mark.parametrize("variant", ["P_x50", "alpha_0"])
+@pytest.mark.parametrize("variant", ["P_x50", "alpha_0", "alpha_neg"])
 def test_prefill_bias_sensitivity(variant, W, heads):
     """Large-bias variants where a shear or rel_extent slip changes the output by O(1).
-    G8 (eight query heads per kv head) takes the eight-heads-per-workgroup kernel."""
+    G8 (eight query heads per kv head) takes the eight-heads-per-workgroup kernel;
+    alpha <= 0 takes its form that scales every score before the row max."""
     T, E = 777, 200
     Hq, Hkv = heads
     x = tinputs.make_prefill_inputs(1, T, Hq, Hkv, 128, 64, E, "bf16", seed=5)
@@ -78,7 +79,7 @@ def test_prefill_bias_sensitivity(variant, W, heads):
         x["P"] = (x["P"].float() * 50).to(torch.bfloat16)
         x["P_cols"] = x["P"].t().contiguous()
     else:
-        alpha = 0.0
+        alpha = 0.0 if variant == "alpha_0" else -2.0 * ALPHA
         x["P"] = (x["P"].float() * 25).to(torch.bfloat16)
         x["P_cols"] = x["P"].t().contiguous()
     out, lse = _run_prefill(_cuda(x), alpha, E, W, False)
@@ -93,6 +94,22 @@ def test_prefill_log_scale_sampled_rows():
     rows = [0, 1, 299, 300, 301, 2047, 4095, 4096, 4999]
     ref, lref = oracle.prefill(x["q"], x["k"], x["v"], x["r"], x["P"], ALPHA, E, 0, True, rows=rows)
     assert_close(out[:, rows], ref, torch.bfloat16, "log-scale", lse[:, :, rows], lref)
+
+
+def test_prefill_log_scale_large_bias_eight_heads_per_kv_head():
+    """Eight query heads per kv head (the eight-heads-per-workgroup kernel),
+    T > 4096 so the log-scale s exceeds 1, and P scaled by 50 so the bias
+    dominates the scores: s must multiply both terms, and the band edge at
+    rel_extent must sit at the right distance."""
+    T, E = 4500, 1024
+    x = tinputs.make_prefill_inputs(1, T, 8, 1, 128, 128, E, "bf16", seed=12)
+    x["P"] = (x["P"].float() * 50).to(torch.bfloat16)
+    x["P_cols"] = x["P"].t().contiguous()
+    assert oracle.scale_factor(T, True) > 1.01
+    out, lse = _run_prefill(_cuda(x), ALPHA, E, 0, True)
+    rows = [0, 1, 31, 32, 1022, 1023, 1024, 1025, 1055, 1056, 2047, 2048, 3000, 4095, 4096, 4097, 4498, 4499]
+    ref, lref = oracle.prefill(x["q"], x["k"], x["v"], x["r"], x["P"], ALPHA, E, 0, True, rows=rows)
+    assert_close(out[:, rows], ref, torch.bfloat16, "G8 log-scale P x50", lse[:, :, rows], lref)
 
 
 def test_prefill_weights_via_identity_v():
