@@ -26,9 +26,14 @@
  * - P is passed distance-major: P_cols[E][d_r] with P_cols[d][c] = P[c][d],
  *   i.e. row d holds the d_r coefficients that r is dotted with for distance d
  *   (the layout of a linear-layer weight mapping d_r features to E outputs).
+ *   The pages index P by column, P[:, d]; taking its transpose makes the d_r
+ *   coefficients of one distance contiguous, which is what every kernel
+ *   reads (one distance per MFMA row), so no call needs a transposed copy.
  * - Supported shapes: D == 128; d_r a multiple of 16 with 16 <= d_r <= 128
  *   (ignored when rel_extent == 0); Hq % Hkv == 0.  Others return
- *   RA_ERR_UNSUPPORTED.
+ *   RA_ERR_UNSUPPORTED.  The pages fix no d_r; the bound of 128 is what the
+ *   prefill kernel can hold of r in registers as MFMA operands beside q, S
+ *   and O at two waves per SIMD.
  * - Work is enqueued on `stream` (a hipStream_t; NULL = the legacy default
  *   stream) and the call returns without synchronising, copying to the host or
  *   reading device data on the host, so calls can be captured in a hipGraph.
@@ -161,12 +166,18 @@ int rel_attn_prologue(const void* q_in, const void* k_in, const void* v_in,
 
 /*
  * Decode plan: a pure function of the shape.  Writes the number of KV splits
- * the decode call will use (num_splits_req > 0 asks for that many; the plan
- * may use fewer so that every split holds at least one 32-key step; 0 lets
- * the library choose from B*Hkv, the visible length min(L, window) and the GPU
- * size) and the workspace size in bytes the caller must provide: the split
- * partials plus one row of relative logits per (sequence, query head),
- * padded (all zeros when rel_extent == 0).
+ * the decode call will use and the workspace size in bytes the caller must
+ * provide.  The split count is the num_splits of the split-KV decode that the
+ * vLLM page ("vLLM 宣布 Day-0 支持 TML Inkling 模型", section "vLLM 集成与优化",
+ * the paragraph on the sheared-bias FA4 kernel) picks per batch from the
+ * batch size, tensor parallelism and KV length: num_splits_req > 0 asks for
+ * that many (the plan may use fewer so that every split holds at least one
+ * 256-key turn); 0 lets the library choose from B*Hkv, the visible length
+ * min(L, window) and the GPU size.  The workspace holds the split partials
+ * plus one row of relative logits per (sequence, query head), padded, for
+ * the shapes whose bias takes the pre-pass (all zeros when rel_extent == 0).
+ * window and rel_extent are inputs because the visible length sets the
+ * splits and the extent sets the length of those rows.
  */
 int rel_attn_decode_plan(int B, int L, int Hq, int Hkv, int D, int num_splits_req, int window,
                          int rel_extent, int* num_splits_out, size_t* workspace_bytes_out);
@@ -179,11 +190,14 @@ int rel_attn_decode_plan(int B, int L, int Hq, int Hkv, int D, int num_splits_re
  * num_splits and workspace come from rel_attn_decode_plan with the same shape
  * (workspace: device memory, 256-byte aligned, at least workspace_bytes; its
  * contents on entry are ignored and on return are unspecified).  The KV range
- * is split into num_splits chunks; each chunk's partial softmax state is
- * merged by log-sum-exp in a last kernel on the same stream.  A first
- * kernel writes each (sequence, head)'s relative-logit row s * r.P[:, d] into
- * the workspace (zeros when rel_extent == 0); the split kernel adds it by
- * distance.
+ * is split into num_splits chunks (the split-KV decode of the vLLM page,
+ * section "vLLM 集成与优化"); each chunk's partial softmax state is merged by
+ * log-sum-exp in a last kernel on the same stream (with one split the split
+ * kernel writes out and lse itself).  The workgroups whose chunk holds keys
+ * within rel_extent of the query make the bias s * r.P[:, L-1-j] of those
+ * keys in LDS; when that region would not fit the LDS budget, a first kernel
+ * writes each (sequence, head)'s relative-logit row into the workspace
+ * instead and the split kernel adds it by distance.
  */
 int rel_attn_decode(const void* q, const void* k, const void* v, const void* r,
                     const void* P_cols, void* out, float* lse, int dtype,
