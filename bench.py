@@ -14,7 +14,8 @@ roofline and the fp64 CPU oracle timed on a bounded sample of it:
   * decode_64x8k    64 sequences x 1 token over 8192 keys (KV GB/s vs HBM)
   * decode_1x1m_log 1 sequence x 1 token over 2^20 keys, s = 5/3
 and the rows the library adds beside the forward (paged and MXFP8 decode,
-extend over a paged cache, the attention prologue, the backward).
+extend over a paged cache in bf16 and in MXFP8, the attention prologue, the
+backward).
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
                        [--only NAME[,NAME...]]
@@ -48,7 +49,7 @@ METRIC = "relative-attention prefill TFLOP/s + decode KV GB/s (% of MI355X peak)
 HEADLINE = "full_prefill_32k_log"
 PREFILL_WORKLOADS = ["tiny_fp32", "swa_prefill_8k", "full_prefill_32k_log"]
 DECODE_WORKLOADS = ["decode_64x8k", "decode_1x1m_log"]
-EXTRA = ["decode_paged", "decode_mx", "extend", "prologue", "backward"]
+EXTRA = ["decode_paged", "decode_mx", "extend", "extend_mx", "prologue", "backward"]
 EXTEND_WORKLOAD = "extend_4x1k_8k_paged"
 PAGED_DECODE_WORKLOAD = "decode_paged_64x8k"
 PROLOGUE_WORKLOAD = "prologue_8k"
@@ -536,6 +537,39 @@ def bench_extend(steps: int, warmup: int):
                                   traffic(f"prefill_kernel_extend@{w.name}", PREFILL_SRC), per)}
 
 
+def bench_extend_mx(steps: int, warmup: int):
+    """The extend workload over MXFP8 caches (quantised once from the bf16 pages)."""
+    import torch
+    import transformer_attention_query_amd as ra
+    from transformer_attention_query_amd import inputs as tinputs
+
+    w = tinputs.WORKLOADS[EXTEND_WORKLOAD]
+    x = {n: t.cuda() for n, t in tinputs.make_inputs(w, seed=0).items()}
+    paged = w.page_size > 0
+    kc, ks = ra.mx_quantize(x["k_pages"] if paged else x["k"])
+    vc, vs = ra.mx_quantize(x["v_pages"] if paged else x["v"])
+    bt = x["block_table"] if paged else None
+    stream = torch.cuda.current_stream()
+
+    def step(_i):
+        ra.extend_mx(x["q"], kc, ks, vc, vs, x["r"], x["P_cols"], w.alpha, w.E, w.W, w.log_scale, x["q_start"],
+                     x["kv_len"], w.n_new, block_table=bt)
+
+    total_ms, per = _time_launches(step, steps, warmup, stream)
+    flops, _, _ = prefill_work(w.T, w.Hq, w.D, w.d_r, w.E, w.W, rows=range(w.T - w.n_new, w.T))
+    flops *= w.B
+    ms = total_ms / steps
+    ach = flops / (sum(per) / len(per) * 1e-3) / 1e12
+    print(f"# extend {w.name} (MXFP8 K/V): {ms * 1e3:.1f} us/step", file=sys.stderr, flush=True)
+    return {"workload": w.name + "_mx", "value": round(flops / (ms * 1e-3) / 1e12, 2), "unit": "TFLOP/s",
+            "ms_per_step": round(ms, 5), "algorithmic_flops": flops, "kv_format": "MXFP8 (E4M3 + E8M0 per 32)",
+            "config": {"B": w.B, "kv_len": w.T, "new_rows": w.n_new, "page_size": w.page_size, "Hq": w.Hq,
+                       "Hkv": w.Hkv, "d_r": w.d_r, "rel_extent": w.E, "window": w.W},
+            "roofline": _roofline("mfma", "prefill_kernel (extend, MXFP8)", ach, PEAK_BF16_TFLOPS, "TFLOP/s",
+                                  traffic(f"prefill_kernel_extend_mx@{w.name}", PREFILL_SRC), per),
+            "note": "scores on the fp8 MFMA, P.V and r.P on bf16; priced against the bf16 peak"}
+
+
 def bench_prologue(steps: int, warmup: int):
     """The attention prologue of an 8192-token prefill, caches written in place."""
     import torch
@@ -702,7 +736,7 @@ def main():
         line.update({"n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "note": "headline not run (--only)"})
     line.update(objs)
     extras = {"decode_paged": bench_decode_paged, "decode_mx": bench_decode_mx, "extend": bench_extend,
-              "prologue": bench_prologue, "backward": bench_backward}
+              "extend_mx": bench_extend_mx, "prologue": bench_prologue, "backward": bench_backward}
     for key in EXTRA:
         if want(key):
             line[key] = extras[key](args.steps, args.warmup)

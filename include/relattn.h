@@ -119,6 +119,30 @@ int rel_attn_extend(const void* q, const void* k, const void* v, const void* r,
                     void* stream);
 
 /*
+ * rel_attn_extend over MXFP8 caches (page "SGLang and Miles Add Day-0
+ * Support for Inkling", section "Relative Logits Optimization", paragraph
+ * "MXFP8 Support" and Figure 3: the attention kernel reads K and V as MXFP8
+ * and takes Q.K^T as an MXFP8 product).  The caches hold E4M3 codes
+ * k_codes / v_codes [.., Hkv, D] (uint8, the layout of the dtype caches with
+ * one byte per value) and E8M0 scales k_scales / v_scales [.., Hkv, D / 32]
+ * (uint8, any alignment), contiguous ([B, cache_len, ...]) or paged
+ * ([num_pages, page_size, ...]), as rel_attn_prologue_mx and rel_mx_quantize
+ * write them.  q, r, P_cols and out are bf16.  Each new row's query is
+ * quantised to MXFP8 as rel_mx_quantize would quantise it, the scores come
+ * from the MX-scaled fp8 MFMA, V is dequantised to bf16 (exact) for P.V;
+ * the relative bias, masks and softmax are those of rel_attn_extend.
+ * Everything else (shapes, q_start / kv_len / block_table, bounds, no-op
+ * cases) as rel_attn_extend.
+ */
+int rel_attn_extend_mx(const void* q, const void* k_codes, const void* k_scales, const void* v_codes,
+                       const void* v_scales, const void* r, const void* P_cols, void* out, float* lse,
+                       int B, int total_q, int max_q, const int* q_start, const int* kv_len,
+                       int cache_len, const int* block_table, int max_pages, int num_pages, int page_size,
+                       int Hq, int Hkv, int D, int d_r,
+                       float alpha, int rel_extent, int window, int log_scale,
+                       void* stream);
+
+/*
  * Attention prologue: the step before the attention kernels on the new
  * tokens' q, k and v projections (page "SGLang and Miles Add Day-0 Support
  * for Inkling", section "ShortConv Optimization", paragraph "KV ShortConv +

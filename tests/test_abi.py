@@ -289,6 +289,41 @@ def test_extend_empty_is_a_noop(lib):
         assert _extend(lib, q=None, k=None, v=None, out=None, q_start=None, kv_len=None, **kw) == RA_OK
 
 
+def _extend_mx(lib, **kw):
+    a = dict(q=FAKE, kc=FAKE + 0x100, ks=FAKE + 0x200, vc=FAKE + 0x300, vs=FAKE + 0x400, r=FAKE + 0x500,
+             P=FAKE + 0x600, out=FAKE + 0x1000, lse=None, B=2, total_q=10, max_q=8, q_start=FAKE, kv_len=FAKE,
+             cache_len=64, block_table=None, max_pages=0, num_pages=0, page_size=0, Hq=8, Hkv=1, D=128, d_r=64,
+             alpha=0.1, E=32, W=0, ls=0)
+    a.update(kw)
+    return lib.rel_attn_extend_mx(a["q"], a["kc"], a["ks"], a["vc"], a["vs"], a["r"], a["P"], a["out"], a["lse"],
+                                  a["B"], a["total_q"], a["max_q"], a["q_start"], a["kv_len"], a["cache_len"],
+                                  a["block_table"], a["max_pages"], a["num_pages"], a["page_size"], a["Hq"],
+                                  a["Hkv"], a["D"], a["d_r"], a["alpha"], a["E"], a["W"], a["ls"], None)
+
+
+@pytest.mark.parametrize("kw,code,frag", [
+    (dict(ks=None), RA_ERR_INVALID_ARG, "scales"),
+    (dict(vs=None), RA_ERR_INVALID_ARG, "scales"),
+    (dict(kc=None), RA_ERR_INVALID_ARG, "k is NULL"),
+    (dict(out=FAKE + 0x200), RA_ERR_INVALID_ARG, "alias"),
+    (dict(lse=FAKE + 0x400), RA_ERR_INVALID_ARG, "alias"),
+    (dict(block_table=FAKE, page_size=48, max_pages=4, num_pages=8), RA_ERR_UNSUPPORTED, "page_size"),
+    (dict(cache_len=0), RA_ERR_INVALID_ARG, "cache_len"),
+    (dict(D=64), RA_ERR_UNSUPPORTED, "head dim"),
+    (dict(d_r=40), RA_ERR_UNSUPPORTED, "d_r"),
+    (dict(q_start=None), RA_ERR_INVALID_ARG, "q_start"),
+])
+def test_extend_mx_rejects_bad_arguments(lib, kw, code, frag):
+    assert _extend_mx(lib, **kw) == code
+    assert frag in lib.rel_attn_last_error().decode()
+
+
+def test_extend_mx_empty_is_a_noop(lib):
+    for kw in (dict(B=0), dict(total_q=0), dict(max_q=0)):
+        assert _extend_mx(lib, q=None, kc=None, ks=None, vc=None, vs=None, out=None, q_start=None, kv_len=None,
+                          **kw) == RA_OK
+
+
 def _decode_paged(lib, **kw):
     a = dict(q=FAKE, k=FAKE, v=FAKE, r=FAKE, P=FAKE, out=FAKE + 0x1000, lse=None, dtype=RA_BF16, B=2, max_len=100,
              kv_len=FAKE, bt=FAKE, max_pages=4, num_pages=8, page_size=32, Hq=8, Hkv=1, D=128, d_r=64,

@@ -13,7 +13,10 @@
   kernel quantises its fp32 values, so a code may differ from the one the
   fp64 value rounds to); q_out and the state equal the bf16 prologue's.
 * prologue_mx then decode_mx against the oracle's prologue -> MXFP8 ->
-  decode chain."""
+  decode chain.
+* rel_attn_extend_mx (contiguous and paged) against the oracle's extend on
+  the MXFP8 values of q, k and v, at the bf16 bar; a peaky-query case where
+  the rounding of q is visible pins that the kernel quantises q itself."""
 
 import zlib
 
@@ -200,3 +203,89 @@ def test_prologue_mx_then_decode_mx_matches_oracle_chain():
     ref, lref = oracle.extend(oracle.mx_round(q_dec_ref), oracle.mx_round(kcache), oracle.mx_round(vcache), r, P,
                               ALPHA, 128, 0, False, qs1, lens)
     assert_close(out, ref, torch.bfloat16, "chain decode", lse, lref.t().contiguous())
+
+
+# ---------------------------------------------------------------- extend over MXFP8 caches
+
+# name, kv_lens, new_lens, Hq, Hkv, d_r, E, W, log_scale, page_size (0 = contiguous)
+EXTEND_CASES = [
+    ("g8_contig", [300, 64, 1000], [37, 64, 1], 8, 1, 32, 100, 0, False, 0),
+    ("g4_paged32_window", [513, 77, 1], [200, 5, 1], 8, 2, 64, 64, 50, False, 32),
+    ("g8_paged64_empty_seq", [129, 700, 40], [129, 0, 33], 16, 2, 128, 300, 0, False, 64),
+    ("mha_paged128_E1", [260, 31], [100, 31], 3, 3, 16, 1, 0, False, 128),
+    ("g8_log_scale", [5000, 4200], [40, 70], 8, 1, 64, 200, 0, True, 64),
+    ("g16_contig_E0", [700, 333], [300, 333], 16, 1, 32, 0, 0, False, 0),
+    ("g2_whole_sequences_E1024", [1500, 1100], [1500, 1100], 4, 2, 128, 1024, 0, False, 0),
+]
+
+
+def _extend_mx(x, E, W, ls, page):
+    paged = page > 0
+    kc, ks = _mx_cache(x["k_pages"] if paged else x["k"])
+    vc, vs = _mx_cache(x["v_pages"] if paged else x["v"])
+    new = (x["q_start"][1:] - x["q_start"][:-1])
+    out, lse = ra.extend_mx(x["q"].cuda(), kc, ks, vc, vs, x["r"].cuda(), x["P_cols"].cuda() if E > 0 else None,
+                            ALPHA, E, W, ls, x["q_start"].cuda(), x["kv_len"].cuda(), int(new.max()),
+                            block_table=x["block_table"].cuda() if paged else None)
+    torch.cuda.synchronize()
+    return out, lse
+
+
+def _extend_mx_ref(x, E, W, ls):
+    """The oracle's extend on the values the MXFP8 rows stand for: q, k and v
+    through MXFP8 and back (the kernel quantises each new query row itself)."""
+    return oracle.extend(oracle.mx_round(x["q"]), oracle.mx_round(x["k"]), oracle.mx_round(x["v"]), x["r"],
+                         x["P"] if E > 0 else x["P"][:, :0], ALPHA, E, W, ls, x["q_start"].tolist(),
+                         x["kv_len"].tolist())
+
+
+@pytest.mark.parametrize("case", EXTEND_CASES, ids=[c[0] for c in EXTEND_CASES])
+def test_extend_mx_matches_oracle(case):
+    name, kv_lens, new_lens, Hq, Hkv, d_r, E, W, ls, page = case
+    x = tinputs.make_extend_inputs(kv_lens, new_lens, Hq, Hkv, 128, d_r, max(E, 1), "bf16",
+                                   seed=zlib.crc32(name.encode()) % 1000, page_size=page)
+    out, lse = _extend_mx(x, E, W, ls, page)
+    ref, lref = _extend_mx_ref(x, E, W, ls)
+    assert_close(out, ref, torch.bfloat16, name, lse, lref)
+
+
+@pytest.mark.parametrize("heads", [(8, 1), (8, 2)], ids=["G8", "G4"])
+def test_extend_mx_bias_sensitivity_paged(heads):
+    """P x50: the bias dominates the MXFP8 scores, so a slip in the shear, the
+    extent edge or the page mapping changes the output by O(1)."""
+    Hq, Hkv = heads
+    x = tinputs.make_extend_inputs([600, 333], [150, 90], Hq, Hkv, 128, 64, 200, "bf16", seed=19, page_size=32)
+    x["P"] = (x["P"].float() * 50).to(torch.bfloat16)
+    x["P_cols"] = x["P"].t().contiguous()
+    out, lse = _extend_mx(x, 200, 0, False, 32)
+    ref, lref = _extend_mx_ref(x, 200, 0, False)
+    assert_close(out, ref, torch.bfloat16, "mx P_x50", lse, lref)
+
+
+def test_extend_mx_query_quantisation_matters():
+    """Peaky queries (one value per 32-block scaled by 40) make the MXFP8
+    rounding of q visible: the kernel must agree with the oracle on
+    mx_round(q), and differ measurably from attention on the unrounded bf16 q.
+
+    The scaled fp8 MFMA sums its 64 products with about 12 bits (measured on
+    the device: |error| <= 2e-4 of the sum of |products|), so with these
+    large scores the lse bar gets that allowance: 1e-3 + 4e-4 * alpha *
+    max_j sum_d |q_d k_jd| per row."""
+    x = tinputs.make_extend_inputs([400], [400], 8, 1, 128, 32, 64, "bf16", seed=23)
+    q = x["q"].float()
+    q[..., ::32] *= 40.0
+    x["q"] = q.to(torch.bfloat16)
+    out, lse = _extend_mx(x, 64, 0, False, 0)
+    ref, lref = _extend_mx_ref(x, 64, 0, False)
+    assert_close(out, ref, torch.bfloat16, "mx peaky q")
+    qd = oracle.mx_round(x["q"])[:, :, None, :]                    # [T, H, 1, D]
+    kd = oracle.mx_round(x["k"])[0, :, 0][None, None, :, :]        # [1, 1, T, D]
+    T = qd.shape[0]
+    visible = torch.tril(torch.ones(T, T, dtype=torch.bool))[:, None, :]
+    absdot = torch.einsum("thd,jd->thj", qd[:, :, 0].abs(), kd[0, 0].abs()).masked_fill(~visible, 0)
+    allow = 1e-3 + 4e-4 * ALPHA * absdot.amax(-1).t()             # [H, T]
+    err = (lse.cpu().double() - lref).abs()
+    assert bool((err <= allow).all()), f"lse error {err.max().item():.3e} beyond the allowance"
+    plain, _ = oracle.extend(x["q"], oracle.mx_round(x["k"]), oracle.mx_round(x["v"]), x["r"], x["P"], ALPHA, 64, 0,
+                             False, x["q_start"].tolist(), x["kv_len"].tolist())
+    assert (plain - ref).abs().max().item() > 5e-2

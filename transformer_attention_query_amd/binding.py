@@ -49,6 +49,9 @@ def _declare(lib):
     lib.rel_attn_extend.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, vp, vp, i32, vp, i32, i32,
                                     i32, i32, i32, i32, i32, f32, i32, i32, i32, vp]
     lib.rel_attn_extend.restype = i32
+    lib.rel_attn_extend_mx.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, vp, vp, i32, vp, i32, i32,
+                                       i32, i32, i32, i32, i32, f32, i32, i32, i32, vp]
+    lib.rel_attn_extend_mx.restype = i32
     lib.rel_attn_decode_plan.argtypes = [i32, i32, i32, i32, i32, i32, i32, i32,
                                          c.POINTER(i32), c.POINTER(sz)]
     lib.rel_attn_decode_plan.restype = i32
@@ -257,6 +260,62 @@ def extend(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, r: Optional[torch.
                                cache_len, _ptr(block_table), max_pages, num_pages, page_size,
                                Hq, Hkv, D, d_r, float(alpha), int(rel_extent), int(window),
                                1 if log_scale else 0, _stream(dev)))
+    return out, lse
+
+
+def extend_mx(q: torch.Tensor, k_codes: torch.Tensor, k_scales: torch.Tensor, v_codes: torch.Tensor,
+              v_scales: torch.Tensor, r: Optional[torch.Tensor], P_cols: Optional[torch.Tensor], alpha: float,
+              rel_extent: int, window: int, log_scale: bool, q_start: torch.Tensor, kv_len: torch.Tensor,
+              max_q: int, block_table: Optional[torch.Tensor] = None, return_lse: bool = True
+              ) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+    """``extend`` over MXFP8 caches (rel_attn_extend_mx): codes [.., Hkv, D]
+    and scales [.., Hkv, D/32] (uint8) as ``mx_quantize`` / ``prologue_mx``
+    write them, contiguous [B,cache_len,..] or paged [num_pages,page_size,..]
+    with ``block_table``.  q, r, P_cols bf16.  Returns out [total_q,Hq,D] bf16
+    and lse [Hq,total_q] fp32 (or None)."""
+    lib = load_library()
+    dev = q.device
+    _need(q, "q", torch.bfloat16, dev, 3)
+    for name, t in (("k_codes", k_codes), ("v_codes", v_codes), ("k_scales", k_scales), ("v_scales", v_scales)):
+        _need(t, name, torch.uint8, dev, 4)
+    _need(q_start, "q_start", torch.int32, dev, 1)
+    _need(kv_len, "kv_len", torch.int32, dev, 1)
+    total_q, Hq, D = q.shape
+    B = kv_len.shape[0]
+    if q_start.shape[0] != B + 1:
+        raise ValueError(f"q_start must have B+1 = {B + 1} entries, got {q_start.shape[0]}")
+    if v_codes.shape != k_codes.shape or k_scales.shape != k_codes.shape[:3] + (D // 32,) or \
+            v_scales.shape != k_scales.shape:
+        raise ValueError("code and scale shapes do not match")
+    Hkv = k_codes.shape[2]
+    if block_table is None:
+        cache_len, max_pages, num_pages, page_size = k_codes.shape[1], 0, 0, 0
+        if k_codes.shape[0] != B:
+            raise ValueError(f"contiguous caches must be [B={B}, cache_len, Hkv, D], got {tuple(k_codes.shape)}")
+    else:
+        _need(block_table, "block_table", torch.int32, dev, 2)
+        if block_table.shape[0] != B:
+            raise ValueError(f"block_table must be [B={B}, max_pages], got {tuple(block_table.shape)}")
+        cache_len, max_pages, num_pages, page_size = 0, block_table.shape[1], k_codes.shape[0], k_codes.shape[1]
+    d_r = 0
+    if rel_extent > 0:
+        _need(r, "r", torch.bfloat16, dev, 3)
+        _need(P_cols, "P_cols", torch.bfloat16, dev, 2)
+        d_r = r.shape[2]
+        if r.shape[:2] != (total_q, Hq):
+            raise ValueError(f"r shape {tuple(r.shape)} does not match q")
+        if P_cols.shape != (rel_extent, d_r):
+            raise ValueError(f"P_cols must be [rel_extent={rel_extent}, d_r={d_r}], got {tuple(P_cols.shape)}")
+    else:
+        r = None
+        P_cols = None
+    out = torch.empty_like(q)
+    lse = torch.empty(Hq, total_q, dtype=torch.float32, device=dev) if return_lse else None
+    _check(lib.rel_attn_extend_mx(_ptr(q), _ptr(k_codes), _ptr(k_scales), _ptr(v_codes), _ptr(v_scales), _ptr(r),
+                                  _ptr(P_cols), _ptr(out), _ptr(lse), B, total_q, int(max_q), _ptr(q_start),
+                                  _ptr(kv_len), cache_len, _ptr(block_table), max_pages, num_pages, page_size,
+                                  Hq, Hkv, D, d_r, float(alpha), int(rel_extent), int(window),
+                                  1 if log_scale else 0, _stream(dev)))
     return out, lse
 
 

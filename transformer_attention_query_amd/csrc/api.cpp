@@ -148,6 +148,61 @@ int scratch_of_stream(void* stream, void** out) {
   return RA_OK;
 }
 
+// ---- extend with caches in the input dtype, or in MXFP8 (mx: E4M3 codes in
+// k / v and their E8M0 scales; bf16 q, r, P and out)
+int extend_impl(const void* q, const void* k, const void* k_scales, const void* v, const void* v_scales, bool mx,
+                const void* r, const void* P_cols, void* out, float* lse, int dtype, int B, int total_q, int max_q,
+                const int* q_start, const int* kv_len, int cache_len, const int* block_table, int max_pages,
+                int num_pages, int page_size, int Hq, int Hkv, int D, int d_r, float alpha, int rel_extent,
+                int window, int log_scale, void* stream) {
+  int rc = check_common(dtype, B, total_q, Hq, Hkv, D, d_r, alpha, rel_extent, window, log_scale, "total_q");
+  if (rc) return rc;
+  if (max_q < 0) return fail(RA_ERR_INVALID_ARG, "max_q = %d < 0", max_q);
+  if (B == 0 || total_q == 0 || max_q == 0) return ok();
+  if ((rc = check_ptr(q, "q", true)) || (rc = check_ptr(k, "k", true)) || (rc = check_ptr(v, "v", true)) ||
+      (rc = check_ptr(out, "out", true)) || (rc = check_ptr(lse, "lse", false)) ||
+      (rc = check_ptr(r, "r", rel_extent > 0)) || (rc = check_ptr(P_cols, "P_cols", rel_extent > 0)))
+    return rc;
+  if (mx && (k_scales == nullptr || v_scales == nullptr))
+    return fail(RA_ERR_INVALID_ARG, "k_scales and v_scales must not be NULL");
+  if (q_start == nullptr || kv_len == nullptr) return fail(RA_ERR_INVALID_ARG, "q_start and kv_len must not be NULL");
+  if ((reinterpret_cast<uintptr_t>(q_start) | reinterpret_cast<uintptr_t>(kv_len) |
+       reinterpret_cast<uintptr_t>(block_table)) & 3u)
+    return fail(RA_ERR_INVALID_ARG, "q_start, kv_len and block_table must be 4-byte aligned");
+  {
+    const void* ins[7] = {q, k, v, r, P_cols, k_scales, v_scales};
+    for (const void* i : ins)
+      if (i != nullptr && (i == out || i == lse)) return fail(RA_ERR_INVALID_ARG, "out or lse aliases an input");
+  }
+  if (block_table == nullptr) {
+    if (cache_len <= 0) return fail(RA_ERR_INVALID_ARG, "cache_len = %d: contiguous caches need cache_len >= 1", cache_len);
+  } else {
+    if (page_size <= 0 || page_size % 32 != 0)
+      return fail(RA_ERR_UNSUPPORTED, "page_size = %d: supported values are positive multiples of 32", page_size);
+    if (max_pages <= 0 || num_pages <= 0)
+      return fail(RA_ERR_INVALID_ARG, "max_pages = %d and num_pages = %d must be positive", max_pages, num_pages);
+    if ((long long)max_pages * page_size > 0x7fffffffLL)
+      return fail(RA_ERR_UNSUPPORTED, "max_pages * page_size too large");
+  }
+  if ((long long)total_q * Hq > 0x7fffffffLL / relattn::kHeadDim)
+    return fail(RA_ERR_UNSUPPORTED, "total_q * Hq = %lld too large for one launch", (long long)total_q * Hq);
+
+  relattn::PrefillArgs a;
+  a.q = q; a.k = k; a.v = v; a.r = r; a.pc = P_cols; a.out = out; a.lse = lse;
+  a.B = B; a.T = 0; a.Hq = Hq; a.Hkv = Hkv; a.d_r = rel_extent > 0 ? d_r : 16; a.E = rel_extent; a.W = window;
+  a.c1 = (float)((double)alpha * 1.4426950408889634);
+  a.c2 = (float)1.4426950408889634;
+  a.q_start = q_start; a.kv_len = kv_len; a.btab = block_table;
+  a.total_q = total_q; a.max_q = max_q; a.cap = block_table == nullptr ? cache_len : 0;
+  a.max_pages = max_pages; a.num_pages = num_pages; a.page_size = page_size;
+  a.log_scale = log_scale; a.alpha = alpha;
+  a.k_scale = k_scales; a.v_scale = v_scales;
+  hipError_t e = mx ? relattn::launch_extend_mx(a, static_cast<hipStream_t>(stream))
+                    : relattn::launch_extend(dtype, a, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(RA_ERR_HIP, "extend launch failed: %s", hipGetErrorString(e));
+  return ok();
+}
+
 }  // namespace
 
 extern "C" {
@@ -187,44 +242,19 @@ int rel_attn_extend(const void* q, const void* k, const void* v, const void* r, 
                     float* lse, int dtype, int B, int total_q, int max_q, const int* q_start, const int* kv_len,
                     int cache_len, const int* block_table, int max_pages, int num_pages, int page_size, int Hq,
                     int Hkv, int D, int d_r, float alpha, int rel_extent, int window, int log_scale, void* stream) {
-  int rc = check_common(dtype, B, total_q, Hq, Hkv, D, d_r, alpha, rel_extent, window, log_scale, "total_q");
-  if (rc) return rc;
-  if (max_q < 0) return fail(RA_ERR_INVALID_ARG, "max_q = %d < 0", max_q);
-  if (B == 0 || total_q == 0 || max_q == 0) return ok();
-  if ((rc = check_ptr(q, "q", true)) || (rc = check_ptr(k, "k", true)) || (rc = check_ptr(v, "v", true)) ||
-      (rc = check_ptr(out, "out", true)) || (rc = check_ptr(lse, "lse", false)) ||
-      (rc = check_ptr(r, "r", rel_extent > 0)) || (rc = check_ptr(P_cols, "P_cols", rel_extent > 0)))
-    return rc;
-  if (q_start == nullptr || kv_len == nullptr) return fail(RA_ERR_INVALID_ARG, "q_start and kv_len must not be NULL");
-  if ((reinterpret_cast<uintptr_t>(q_start) | reinterpret_cast<uintptr_t>(kv_len) |
-       reinterpret_cast<uintptr_t>(block_table)) & 3u)
-    return fail(RA_ERR_INVALID_ARG, "q_start, kv_len and block_table must be 4-byte aligned");
-  if (out == q || out == k || out == v || out == r) return fail(RA_ERR_INVALID_ARG, "out aliases an input");
-  if (block_table == nullptr) {
-    if (cache_len <= 0) return fail(RA_ERR_INVALID_ARG, "cache_len = %d: contiguous caches need cache_len >= 1", cache_len);
-  } else {
-    if (page_size <= 0 || page_size % 32 != 0)
-      return fail(RA_ERR_UNSUPPORTED, "page_size = %d: supported values are positive multiples of 32", page_size);
-    if (max_pages <= 0 || num_pages <= 0)
-      return fail(RA_ERR_INVALID_ARG, "max_pages = %d and num_pages = %d must be positive", max_pages, num_pages);
-    if ((long long)max_pages * page_size > 0x7fffffffLL)
-      return fail(RA_ERR_UNSUPPORTED, "max_pages * page_size too large");
-  }
-  if ((long long)total_q * Hq > 0x7fffffffLL / relattn::kHeadDim)
-    return fail(RA_ERR_UNSUPPORTED, "total_q * Hq = %lld too large for one launch", (long long)total_q * Hq);
+  return extend_impl(q, k, nullptr, v, nullptr, false, r, P_cols, out, lse, dtype, B, total_q, max_q, q_start, kv_len,
+                     cache_len, block_table, max_pages, num_pages, page_size, Hq, Hkv, D, d_r, alpha, rel_extent,
+                     window, log_scale, stream);
+}
 
-  relattn::PrefillArgs a;
-  a.q = q; a.k = k; a.v = v; a.r = r; a.pc = P_cols; a.out = out; a.lse = lse;
-  a.B = B; a.T = 0; a.Hq = Hq; a.Hkv = Hkv; a.d_r = rel_extent > 0 ? d_r : 16; a.E = rel_extent; a.W = window;
-  a.c1 = (float)((double)alpha * 1.4426950408889634);
-  a.c2 = (float)1.4426950408889634;
-  a.q_start = q_start; a.kv_len = kv_len; a.btab = block_table;
-  a.total_q = total_q; a.max_q = max_q; a.cap = block_table == nullptr ? cache_len : 0;
-  a.max_pages = max_pages; a.num_pages = num_pages; a.page_size = page_size;
-  a.log_scale = log_scale; a.alpha = alpha;
-  hipError_t e = relattn::launch_extend(dtype, a, static_cast<hipStream_t>(stream));
-  if (e != hipSuccess) return fail(RA_ERR_HIP, "extend launch failed: %s", hipGetErrorString(e));
-  return ok();
+int rel_attn_extend_mx(const void* q, const void* k_codes, const void* k_scales, const void* v_codes,
+                       const void* v_scales, const void* r, const void* P_cols, void* out, float* lse, int B,
+                       int total_q, int max_q, const int* q_start, const int* kv_len, int cache_len,
+                       const int* block_table, int max_pages, int num_pages, int page_size, int Hq, int Hkv, int D,
+                       int d_r, float alpha, int rel_extent, int window, int log_scale, void* stream) {
+  return extend_impl(q, k_codes, k_scales, v_codes, v_scales, true, r, P_cols, out, lse, RA_BF16, B, total_q, max_q,
+                     q_start, kv_len, cache_len, block_table, max_pages, num_pages, page_size, Hq, Hkv, D, d_r, alpha,
+                     rel_extent, window, log_scale, stream);
 }
 
 }  // extern "C"

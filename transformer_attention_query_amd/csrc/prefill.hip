@@ -49,12 +49,20 @@
 #include <climits>
 
 #include "device_common.hpp"
+#include "mx_common.hpp"
 #include "relattn_internal.hpp"
 
 namespace relattn {
 namespace {
 
 constexpr float kLazyRescaleLog2 = 8.0f;
+
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+typedef unsigned char u8;
+
+// MXFP8 K tile of the extend form over MXFP8 caches: E4M3 codes [N keys][KCS
+// bytes] and the E8M0 scales [N keys][4], in the K tile's LDS.
+constexpr int kMxKcs = kHeadDim + 16;
 
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef short s16x8 __attribute__((ext_vector_type(8)));
@@ -138,8 +146,15 @@ struct PrefillCfg {
 // contiguous or paged; see rel_attn_extend).  Positions are global: query
 // row t of sequence b sits at kv_len[b] - n_b + t, and query tiles are
 // aligned to multiples of M positions, so the chunk arithmetic is unchanged.
-template <typename T, int WAVES, bool EXT>
+// MX (bf16, EXT): the caches hold MXFP8 (E4M3 codes, one E8M0 scale per 32
+// values of D; page "SGLang and Miles Add Day-0 Support for Inkling",
+// section "Relative Logits Optimization", paragraph "MXFP8 Support").  The
+// query is quantised to MXFP8 the same way and the scores come from the
+// MX-scaled fp8 MFMA (v_mfma_scale_f32_32x32x64_f8f6f4, two per 32x32
+// tile); V is dequantised to bf16 (exactly) when its tile is staged.
+template <typename T, int WAVES, bool EXT, bool MX = false>
 __global__ __launch_bounds__(WAVES * 64, 1) void prefill_kernel(PrefillArgs p, int n_qt, int n_items, int hpw) {
+  static_assert(!MX || (EXT && sizeof(T) == 2), "MXFP8 caches: the bf16 extend form");
   using C = PrefillCfg<T, WAVES>;
   using VS = PreV<T, C::N>;
   constexpr int N = C::N;
@@ -225,10 +240,52 @@ __global__ __launch_bounds__(WAVES * 64, 1) void prefill_kernel(PrefillArgs p, i
 
   // ---- this lane's query and relative feature, as MFMA B operands
   v8_t<T> qreg[D / 16];
-  {
+  i32x8 qx[2];             // MX: the query's E4M3 bytes for score MFMA m = 0, 1
+  int qsc[2] = {127, 127};  // MX: E8M0 scale this lane supplies to MFMA m
+  if constexpr (!MX) {
     const T* qrow = qg + (qrow_of(qvalid ? qa : pos0) * Hq + h) * D + 8 * h2;
 #pragma unroll
     for (int kk = 0; kk < D / 16; ++kk) qreg[kk] = ld8_or_zero<T>(qrow + kk * 16, qvalid);
+  } else {
+    // Operand layout of the 32x32x64 scaled MFMA (checked on the device):
+    // lane (h2, a) holds, for row/column a, bytes k = 16*h2 + t (t < 16) and
+    // 32 + 16*h2 + (t - 16) (t >= 16) of the instruction's 64, and supplies
+    // the scale of row/column a for its 32-value block h2.  Score MFMA m
+    // covers d = 64m .. 64m+63, so this lane holds half h2 of each of the
+    // four d-blocks of its query; each block's maximum joins the two halves
+    // (lanes l and l ^ 32).
+    const T* qrow = qg + (qrow_of(qvalid ? qa : pos0) * Hq + h) * D + 16 * h2;
+    float qv[4][16];  // [block][t]: d = 32*block + 16*h2 + t
+#pragma unroll
+    for (int blk = 0; blk < 4; ++blk) {
+      const v8_t<T> x0 = ld8_or_zero<T>(qrow + 32 * blk, qvalid);
+      const v8_t<T> x1 = ld8_or_zero<T>(qrow + 32 * blk + 8, qvalid);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        qv[blk][e] = float(x0[e]);
+        qv[blk][8 + e] = float(x1[e]);
+      }
+    }
+    int sh[4];
+#pragma unroll
+    for (int blk = 0; blk < 4; ++blk) {
+      float amax = 0.0f;
+#pragma unroll
+      for (int t = 0; t < 16; ++t) amax = fmaxf(amax, fabsf(qv[blk][t]));
+      sh[blk] = mx_shared_exp(pair_max32(amax));
+    }
+#pragma unroll
+    for (int m = 0; m < 2; ++m) {
+#pragma unroll
+      for (int w4 = 0; w4 < 4; ++w4) {
+        const float* lo = &qv[2 * m][4 * w4];
+        const float* hi = &qv[2 * m + 1][4 * w4];
+        qx[m][w4] = int(e4m3_pack4(lo[0], lo[1], lo[2], lo[3], sh[2 * m]));
+        qx[m][4 + w4] = int(e4m3_pack4(hi[0], hi[1], hi[2], hi[3], sh[2 * m + 1]));
+      }
+      // arithmetic pick (an indexed pick would put sh[] in scratch memory)
+      qsc[m] = 127 + sh[2 * m] + h2 * (sh[2 * m + 1] - sh[2 * m]);
+    }
   }
   v8_t<T> rreg[kMaxDr / 16];  // zero past d_r
   {
@@ -256,40 +313,77 @@ __global__ __launch_bounds__(WAVES * 64, 1) void prefill_kernel(PrefillArgs p, i
   // plain prefill), or slot j % page_size of page btab[b][j / page_size] of
   // a paged one (page_size a multiple of N, so a tile lies in one page; page
   // ids are clamped to the pool).
-  const size_t kv_row_stride = size_t(Hkv) * D;
   const size_t seq_rows = EXT ? size_t(p.cap) : size_t(T_);
-  const T* kbase = kg + (size_t(b) * seq_rows * Hkv + kvh) * D;
-  const T* vbase = vg + (size_t(b) * seq_rows * Hkv + kvh) * D;
   v8_t<T> kpre[C::KV_VECS], vpre[C::KV_VECS];
+  // MX: codes of the same 8 values (one byte each) and the scale of their block
+  uint2 kcpre[C::KV_VECS], vcpre[C::KV_VECS];
+  unsigned kspre[C::KV_VECS], vspre[C::KV_VECS];
   auto fetch_kv = [&](int kt) {
     const int j0 = kt * N;
-    const T* kb = kbase;
-    const T* vb = vbase;
+    // cache row (of Hkv heads) of key j0's page start, or of the sequence's key 0
+    size_t r0 = size_t(b) * seq_rows;
     int jpage0 = 0;  // first key of the tile's page
     if constexpr (EXT) {
       if (p.btab != nullptr) {
         const int pg = min(max(p.btab[size_t(b) * p.max_pages + j0 / p.page_size], 0), p.num_pages - 1);
         jpage0 = j0 - j0 % p.page_size;
-        kb = kg + (size_t(pg) * p.page_size * Hkv + kvh) * D;
-        vb = vg + (size_t(pg) * p.page_size * Hkv + kvh) * D;
+        r0 = size_t(pg) * p.page_size;
       }
     }
 #pragma unroll
     for (int i = 0; i < C::KV_VECS; ++i) {
       const int vid = tid + i * C::THREADS;
       const int j = min(j0 + (vid >> 4), T_ - 1);  // rows past T: clamped, masked later
-      const size_t off = size_t(j - jpage0) * kv_row_stride + (vid & 15) * 8;
-      kpre[i] = ld8<T>(kb + off);
-      vpre[i] = ld8<T>(vb + off);
+      const size_t row = (r0 + size_t(j - jpage0)) * Hkv + kvh;
+      if constexpr (MX) {
+        const u8* kc = static_cast<const u8*>(p.k);
+        const u8* vc = static_cast<const u8*>(p.v);
+        const u8* ksc = static_cast<const u8*>(p.k_scale);
+        const u8* vsc = static_cast<const u8*>(p.v_scale);
+        kcpre[i] = *reinterpret_cast<const uint2*>(kc + row * D + (vid & 15) * 8);
+        vcpre[i] = *reinterpret_cast<const uint2*>(vc + row * D + (vid & 15) * 8);
+        kspre[i] = ksc[row * (D / kMxBlock) + (vid & 15) / 4];
+        vspre[i] = vsc[row * (D / kMxBlock) + (vid & 15) / 4];
+      } else {
+        kpre[i] = ld8<T>(kg + row * D + (vid & 15) * 8);
+        vpre[i] = ld8<T>(vg + row * D + (vid & 15) * 8);
+      }
     }
   };
+  u8* Kc = reinterpret_cast<u8*>(Ks);  // MX: K codes [N][kMxKcs], then scales [N][4]
+  u8* Ksc = Kc + N * kMxKcs;
   auto store_kv = [&]() {
 #pragma unroll
     for (int i = 0; i < C::KV_VECS; ++i) {
       const int vid = tid + i * C::THREADS;
       const int row = vid >> 4, c8 = vid & 15;
-      st8<T>(Ks + row * C::KS + c8 * 8, kpre[i]);
-      VS::store(Vs, row, c8, vpre[i]);
+      if constexpr (MX) {
+        *reinterpret_cast<uint2*>(Kc + row * kMxKcs + c8 * 8) = kcpre[i];
+        if ((c8 & 3) == 0) Ksc[row * 4 + c8 / 4] = u8(kspre[i]);
+        // V codes -> bf16 (exact: a 4-bit significand times a power of two)
+        typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+        const float sc = e8m0_float(vspre[i]);
+        const bf16x2 a0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(vcpre[i].x, sc, false);
+        const bf16x2 a1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(vcpre[i].x, sc, true);
+        const bf16x2 a2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(vcpre[i].y, sc, false);
+        const bf16x2 a3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(vcpre[i].y, sc, true);
+        VS::store(Vs, row, c8, v8_t<T>{a0[0], a0[1], a1[0], a1[1], a2[0], a2[1], a3[0], a3[1]});
+      } else {
+        st8<T>(Ks + row * C::KS + c8 * 8, kpre[i]);
+        VS::store(Vs, row, c8, vpre[i]);
+      }
+    }
+  };
+  // MX scores: S^T += K Q^T over d = 64m .. 64m+63 for m = 0, 1 (see the query's layout)
+  auto mx_scores = [&](f32x16& acc) __attribute__((always_inline)) {
+#pragma unroll
+    for (int m = 0; m < 2; ++m) {
+      const u8* kr = Kc + a * kMxKcs + 64 * m + 16 * h2;
+      const uint4 lo = *reinterpret_cast<const uint4*>(kr);
+      const uint4 hi = *reinterpret_cast<const uint4*>(kr + 32);
+      const i32x8 ka = {int(lo.x), int(lo.y), int(lo.z), int(lo.w), int(hi.x), int(hi.y), int(hi.z), int(hi.w)};
+      const int ksc = Ksc[a * 4 + 2 * m + h2];
+      acc = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(ka, qx[m], acc, 0, 0, 0, ksc, 0, qsc[m]);
     }
   };
 
@@ -387,9 +481,10 @@ __global__ __launch_bounds__(WAVES * 64, 1) void prefill_kernel(PrefillArgs p, i
         {
           const T* pr = Pr + ((c - 1) & (nqb - 1)) * (N * C::PS) + a * C::PS + 8 * h2;
           const T* kr = Ks + a * C::KS + 8 * h2;
+          if constexpr (MX) mx_scores(s);
 #pragma unroll
           for (int kk = 0; kk < D / 16; ++kk) {
-            mma32(ld8<T>(kr + kk * 16), qreg[kk], s);
+            if constexpr (!MX) mma32(ld8<T>(kr + kk * 16), qreg[kk], s);
             mma32(ld8<T>(pr + kk * 16), rreg[kk], racc);
           }
         }
@@ -414,6 +509,10 @@ __global__ __launch_bounds__(WAVES * 64, 1) void prefill_kernel(PrefillArgs p, i
 #pragma unroll
         for (int v = 0; v < 16; ++v) s[v] = fmaf(s[v], qk_scale, src[-(8 * (v >> 2) + (v & 3))]);
         wave_lds_fence();
+      } else if constexpr (MX) {
+        mx_scores(s);
+#pragma unroll
+        for (int v = 0; v < 16; ++v) s[v] *= qk_scale;
       } else {
         f32x16 s_odd = zero16();  // two chains keep the matrix cores busy
 #pragma unroll
@@ -520,7 +619,7 @@ __global__ __launch_bounds__(WAVES * 64, 1) void prefill_kernel(PrefillArgs p, i
   }
 }
 
-template <typename T, int WAVES, bool EXT = false>
+template <typename T, int WAVES, bool EXT = false, bool MX = false>
 hipError_t launch_prefill_tiles(const PrefillArgs& a, hipStream_t stream) {
   // heads per workgroup: the largest power of two <= WAVES dividing Hq/Hkv
   const int G = a.Hq / a.Hkv;
@@ -532,8 +631,8 @@ hipError_t launch_prefill_tiles(const PrefillArgs& a, hipStream_t stream) {
   const long long n_items = (long long)n_qt * a.B * a.Hkv * (G / hpw);
   if (n_items > 0x7fffffffLL) return hipErrorInvalidConfiguration;
   if (n_items == 0) return hipSuccess;
-  hipLaunchKernelGGL((prefill_kernel<T, WAVES, EXT>), dim3((unsigned)n_items), dim3(PrefillCfg<T, WAVES>::THREADS), 0,
-                     stream, a, n_qt, (int)n_items, hpw);
+  hipLaunchKernelGGL((prefill_kernel<T, WAVES, EXT, MX>), dim3((unsigned)n_items),
+                     dim3(PrefillCfg<T, WAVES>::THREADS), 0, stream, a, n_qt, (int)n_items, hpw);
   return hipGetLastError();
 }
 
@@ -1040,6 +1139,11 @@ hipError_t launch_prefill_dma(const PrefillArgs& a, hipStream_t stream) {
 hipError_t launch_extend(int dtype, const PrefillArgs& a, hipStream_t stream) {
   if (dtype == 1) return launch_prefill_tiles<__bf16, 8, true>(a, stream);
   return launch_prefill_tiles<float, 2, true>(a, stream);
+}
+
+hipError_t launch_extend_mx(const PrefillArgs& a, hipStream_t stream) {
+  static_assert(kMxKcs * 32 + 32 * 4 <= PrefillCfg<__bf16, 8>::LDS_K, "MXFP8 K tile fits the K tile's LDS");
+  return launch_prefill_tiles<__bf16, 8, true, true>(a, stream);
 }
 
 hipError_t launch_prefill(int dtype, const PrefillArgs& a, hipStream_t stream) {

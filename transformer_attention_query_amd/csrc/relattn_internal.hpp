@@ -34,6 +34,10 @@ struct PrefillArgs {
   int max_pages = 0, num_pages = 0, page_size = 0;
   int log_scale = 0;             // s per sequence from kv_len (c1, c2 unused then)
   float alpha = 0.0f;
+  // extend over MXFP8 caches (rel_attn_extend_mx): k and v hold E4M3 codes
+  // [.., Hkv, D] and these their E8M0 scales [.., Hkv, D / 32]
+  const void* k_scale = nullptr;
+  const void* v_scale = nullptr;
 };
 
 struct DecodeArgs {
@@ -154,6 +158,8 @@ hipError_t launch_prologue(int dtype, const PrologueArgs& a, hipStream_t stream)
 // bf16 inputs, MXFP8 caches
 hipError_t launch_prologue_mx(const PrologueArgs& a, hipStream_t stream);
 hipError_t launch_extend(int dtype, const PrefillArgs& a, hipStream_t stream);
+// bf16 q / r / P / out, MXFP8 caches
+hipError_t launch_extend_mx(const PrefillArgs& a, hipStream_t stream);
 hipError_t launch_decode(int dtype, const DecodeArgs& a, hipStream_t stream);
 hipError_t launch_decode_paged(int dtype, const DecodeArgs& a, hipStream_t stream);
 // MXFP8 K/V caches, bf16 q / r / P / out; paged when a.btab is set
