@@ -21,6 +21,7 @@ Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
                        [--only NAME[,NAME...]]
        python bench.py --copy-calibration   (a plain 1 GiB device copy, for
            scaling the HBM byte counters FETCH_SIZE / WRITE_SIZE)
+       python bench.py --hbm-ceiling   (plain copy and sum rates: a yardstick)
        python bench.py --traffic-from FETCH_CSV WRITE_CSV --kernel-key KEY
                        --kernel-match SUBSTR[,SUBSTR...] --src FILE[,FILE...]
            (turn two rocprofv3 --pmc counter CSVs into the per-launch HBM
@@ -129,7 +130,7 @@ def src_hash(*names):
     return h.hexdigest()[:16]
 
 
-PREFILL_SRC = ("prefill.hip", "device_common.hpp")
+PREFILL_SRC = ("prefill.hip", "device_common.hpp", "mx_common.hpp")
 DECODE_SRC = ("decode.hip", "device_common.hpp", "mx_common.hpp")
 
 
@@ -380,7 +381,7 @@ def bench_prefill(name: str, steps: int, warmup: int, cpu: bool):
                       "algorithmic_flops": flops, "visible_pairs": pairs * w.B, "rel_entries": rel * w.B,
                       "input_copies_rotated": n_copies},
            "roofline": _roofline("mfma", kernel, achieved, peak, "TFLOP/s",
-                                 traffic(f"prefill_dma_kernel@{w.name}", PREFILL_SRC), per)}
+                                 traffic(f"{kernel.split('<')[0]}@{w.name}", PREFILL_SRC), per)}
     if not bf16:
         obj["roofline"]["note"] = ("fp32 path against the fp32 vector peak; launch-bound at this size "
                                    "(parity workload)")
@@ -676,6 +677,51 @@ def copy_calibration(nbytes: int = 1 << 30, reps: int = 3):
     print(json.dumps({"copy_bytes": nbytes, "reps": reps}), flush=True)
 
 
+def hbm_ceiling(nbytes: int = 4 << 30, reps: int = 10):
+    """What plain streaming reaches on this GPU, as a yardstick for the decode
+    fractions: a read-only kernel (libhbmprobe.so, built beside the library:
+    16-byte loads, four in flight per thread, grid-stride) over nbytes at
+    several grid sizes, and torch's device-to-device copy (reads and writes
+    nbytes); HIP events around `reps` back-to-back runs after one warm-up."""
+    import ctypes
+    import torch
+    from transformer_attention_query_amd import build as _build
+    lib = ctypes.CDLL(_build.PROBE_LIB)
+    lib.hbm_read_probe.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
+    lib.hbm_read_probe.restype = ctypes.c_int
+    src = torch.ones(nbytes // 4, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    stream = torch.cuda.current_stream()
+    out = {}
+
+    def timed(fn):
+        fn()
+        torch.cuda.synchronize()
+        t0 = torch.cuda.Event(enable_timing=True)
+        t1 = torch.cuda.Event(enable_timing=True)
+        t0.record(stream)
+        for _ in range(reps):
+            fn()
+        t1.record(stream)
+        torch.cuda.synchronize()
+        return t0.elapsed_time(t1) / reps
+
+    for blocks in (2048, 8192, 16384, 32768, 65536):
+        sink = torch.empty(blocks * 256, dtype=torch.int32, device="cuda")
+
+        def read():
+            rc = lib.hbm_read_probe(src.data_ptr(), nbytes, blocks, sink.data_ptr(), stream.cuda_stream)
+            if rc != 0:
+                raise RuntimeError(f"hbm_read_probe returned {rc}")
+        ms = timed(read)
+        out[f"read_{blocks}x256"] = {"bytes": nbytes, "us": round(ms * 1e3, 1),
+                                     "GB_per_s": round(nbytes / (ms * 1e-3) / 1e9, 1)}
+    ms = timed(lambda: dst.copy_(src))
+    out["torch_copy"] = {"bytes": 2 * nbytes, "us": round(ms * 1e3, 1),
+                         "GB_per_s": round(2 * nbytes / (ms * 1e-3) / 1e9, 1)}
+    print(json.dumps({"hbm_ceiling": out, "peak_GB_per_s": PEAK_HBM_GBPS}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -684,6 +730,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--only", default="", help="comma-separated workloads / extra sections to run")
     ap.add_argument("--copy-calibration", action="store_true")
+    ap.add_argument("--hbm-ceiling", action="store_true", help="time a plain copy and a plain sum (yardstick)")
     ap.add_argument("--calibration-from", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"))
     ap.add_argument("--traffic-from", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"))
     ap.add_argument("--kernel-key")
@@ -710,6 +757,9 @@ def main():
         sys.exit(1)
     if args.copy_calibration:
         copy_calibration()
+        return
+    if args.hbm_ceiling:
+        hbm_ceiling()
         return
 
     only = set(s for s in args.only.split(",") if s)

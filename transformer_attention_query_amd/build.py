@@ -20,6 +20,9 @@ CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD_DIR = os.path.join(ROOT, "_build")
 LIB = os.path.join(HERE, "librelattn.so")
+# a plain streaming-read kernel for bench.py's HBM yardstick (not part of the ABI)
+PROBE_SOURCE = "hbm_probe.hip"
+PROBE_LIB = os.path.join(HERE, "libhbmprobe.so")
 
 SOURCES = ["api.cpp", "prefill.hip", "decode.hip", "rel_logits.hip", "prologue.hip", "mx.hip", "backward.hip"]
 ARCH = "gfx950"
@@ -64,8 +67,14 @@ def build(verbose: bool = True) -> str:
     if res.returncode != 0:
         raise RuntimeError(f"link failed:\n{' '.join(cmd)}\n{res.stdout}\n{res.stderr}")
     os.replace(tmp, LIB)
+    probe_obj = _compile(PROBE_SOURCE)
+    cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", probe_obj, "-o", PROBE_LIB + ".tmp"]
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    if res.returncode != 0:
+        raise RuntimeError(f"link failed:\n{' '.join(cmd)}\n{res.stdout}\n{res.stderr}")
+    os.replace(PROBE_LIB + ".tmp", PROBE_LIB)
     if verbose:
-        print(f"built {LIB}")
+        print(f"built {LIB} and {PROBE_LIB}")
     return LIB
 
 
