@@ -109,3 +109,31 @@ def test_decode_noalloc_refuses_beyond_its_scratch():
     P = torch.zeros(E, 16, dtype=torch.bfloat16, device="cuda")
     with pytest.raises(RuntimeError, match="scratch"):
         ra.decode_noalloc(q, k, k, r, P, ALPHA, E)
+
+
+def test_decode_noalloc_replays_from_a_captured_graph():
+    """The caller it is for: a HIP graph captured around the call (outputs
+    passed in, nothing allocated inside), replayed three times with eager
+    calls in between that reuse the same scratch on other inputs; every
+    replay equals the eager rel_attn_decode result bit for bit."""
+    x, xd = _inputs("noalloc_graph", "bf16", 4, 3000, 16, 2, 128, 512)
+    y, yd = _inputs("noalloc_graph_other", "bf16", 2, 5000, 16, 2, 128, 1024)
+    ref_o, ref_l = ra.decode(xd["q"], xd["k"], xd["v"], xd["r"], xd["P_cols"], ALPHA, 512)
+    out = torch.empty_like(xd["q"])
+    lse = torch.empty(xd["q"].shape[:2], dtype=torch.float32, device=out.device)
+    run = lambda: ra.decode_noalloc(xd["q"], xd["k"], xd["v"], xd["r"], xd["P_cols"], ALPHA, 512,  # noqa: E731
+                                    out=out, lse=lse)
+    run()  # the device's scratch address is looked up outside the capture
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        run()
+    for i in range(3):
+        out.fill_(0)
+        lse.fill_(0)
+        o2, l2 = ra.decode_noalloc(yd["q"], yd["k"], yd["v"], yd["r"], yd["P_cols"], ALPHA, 1024)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out, ref_o) and torch.equal(lse, ref_l), f"replay {i}"
+        assert torch.isfinite(o2.float()).all()
