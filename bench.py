@@ -250,16 +250,34 @@ def _time_batch(fn, steps: int, warmup: int, stream):
     return t0.elapsed_time(t1) / steps
 
 
+def _time_calls(fn, steps: int, warmup: int, stream):
+    """Short library calls (decode: a split kernel and a merge, ~0.1-0.2 ms):
+    the timed region is `steps` calls back to back between one pair of HIP
+    events on the launch stream, so no event sits between the kernels of
+    consecutive calls (an event pair around every call adds ~2-5 us of
+    event processing to each 100-200 us call).  Returns (ms per call over
+    the timed region, per-call ms from a second pass with an event pair
+    around every call, for the spread)."""
+    ms = _time_batch(fn, steps, warmup, stream)
+    _, per = _time_launches(fn, steps, 1, stream)
+    return ms, per
+
+
 def _stats(per):
     s = sorted(per)
     return {"avg_launch_us": round(sum(s) / len(s) * 1e3, 2), "median_us": round(s[len(s) // 2] * 1e3, 2),
             "min_us": round(s[0] * 1e3, 2), "max_us": round(s[-1] * 1e3, 2)}
 
 
-def _roofline(bound, kernel, achieved, peak, unit, tr, per):
+def _roofline(bound, kernel, achieved, peak, unit, tr, per, avg_ms=None):
     r = {"bound": bound, "kernel": kernel, "achieved": round(achieved, 2), "peak": peak, "unit": unit,
          "frac": round(achieved / peak, 4), "traffic": tr}
-    r.update(_stats(per))
+    if avg_ms is None:
+        r.update(_stats(per))
+    else:  # timed region of back-to-back calls; the spread from per-call events
+        r["avg_launch_us"] = round(avg_ms * 1e3, 2)
+        r["timing"] = "one HIP event pair around the timed calls"
+        r.update({"per_call_events_" + k: v for k, v in _stats(per).items()})
     return r
 
 
@@ -418,17 +436,16 @@ def bench_decode(name: str, steps: int, warmup: int, cpu: bool):
         ra.decode(x["q"], k2[i % 2], v2[i % 2], x["r"], x["P_cols"], w.alpha, w.E, w.W, w.log_scale,
                   num_splits=ns, workspace=ws)
 
-    total_ms, per = _time_launches(step, steps, warmup, stream)
+    ms_step, per = _time_calls(step, steps, warmup, stream)
     nbytes, kv = decode_bytes(w.B, w.T, w.Hq, w.Hkv, w.D, w.d_r, w.E, w.W)
-    ms_step = total_ms / steps
-    kernel_ms = sum(per) / len(per)
+    kernel_ms = ms_step
     kgbps = nbytes / (kernel_ms * 1e-3) / 1e9
     obj = {"workload": w.name, "value": round(nbytes / (ms_step * 1e-3) / 1e9, 1), "unit": "GB/s",
            "ms_per_step": round(ms_step, 5), "num_splits": ns, "algorithmic_bytes": nbytes, "dtype": "bf16",
            "config": {"workload": w.name, "B": w.B, "L": w.T, "Hq": w.Hq, "Hkv": w.Hkv, "D": w.D, "d_r": w.d_r,
                       "rel_extent": w.E, "window": w.W, "log_scale": w.log_scale, "kv_copies_rotated": 2},
            "roofline": _roofline("hbm", "decode_split_kernel+merge", kgbps, PEAK_HBM_GBPS, "GB/s",
-                                 traffic(f"decode_split_kernel@{w.name}", DECODE_SRC), per)}
+                                 traffic(f"decode_split_kernel@{w.name}", DECODE_SRC), per, kernel_ms)}
     print(f"# decode {w.name}: {ms_step * 1e3:.1f} us/step, call {kernel_ms * 1e3:.1f} us ({ns} splits, "
           f"{kgbps:.0f} GB/s)", file=sys.stderr, flush=True)
     del x, k2, v2, ws
@@ -462,16 +479,15 @@ def bench_decode_mx(steps: int, warmup: int):
         ra.decode_mx(x["q"], c[0], c[1], c[2], c[3], x["r"], x["P_cols"], w.alpha, w.E, w.W, w.log_scale,
                      num_splits=ns, workspace=ws)
 
-    total_ms, per = _time_launches(step, steps, warmup, stream)
+    ms, per = _time_calls(step, steps, warmup, stream)
     nbytes = decode_bytes_mx(w.B, w.T, w.Hq, w.Hkv, w.D, w.d_r, w.E, w.W)
-    ms = total_ms / steps
-    k = nbytes / (sum(per) / len(per) * 1e-3) / 1e9
+    k = nbytes / (ms * 1e-3) / 1e9
     print(f"# decode {w.name} (MXFP8 K/V): {ms * 1e3:.1f} us/step ({ns} splits)", file=sys.stderr, flush=True)
     return {"workload": w.name + " (MXFP8 K/V)", "value": round(nbytes / (ms * 1e-3) / 1e9, 1), "unit": "GB/s",
             "ms_per_step": round(ms, 5), "num_splits": ns, "algorithmic_bytes": nbytes,
             "dtype": "mxfp8 K/V, bf16 q/out",
             "roofline": _roofline("hbm", "decode_split_kernel (MXFP8)+merge", k, PEAK_HBM_GBPS, "GB/s",
-                                  traffic("decode_split_kernel_mx@decode_64x8k", DECODE_SRC), per)}
+                                  traffic("decode_split_kernel_mx@decode_64x8k", DECODE_SRC), per, ms)}
 
 
 def bench_decode_paged(steps: int, warmup: int):
@@ -493,15 +509,14 @@ def bench_decode_paged(steps: int, warmup: int):
         ra.decode_paged(x["q"], kp[i % 2], vp[i % 2], x["r"], x["P_cols"], w.alpha, w.E, w.W, w.log_scale,
                         x["kv_len"], x["block_table"], w.T, num_splits=ns, workspace=ws)
 
-    total_ms, per = _time_launches(step, steps, warmup, stream)
+    ms, per = _time_calls(step, steps, warmup, stream)
     nbytes, _ = decode_bytes(w.B, w.T, w.Hq, w.Hkv, w.D, w.d_r, w.E, w.W)
-    ms = total_ms / steps
-    k = nbytes / (sum(per) / len(per) * 1e-3) / 1e9
+    k = nbytes / (ms * 1e-3) / 1e9
     print(f"# decode {w.name}: {ms * 1e3:.1f} us/step ({ns} splits)", file=sys.stderr, flush=True)
     return {"workload": w.name, "value": round(nbytes / (ms * 1e-3) / 1e9, 1), "unit": "GB/s",
             "ms_per_step": round(ms, 5), "num_splits": ns, "algorithmic_bytes": nbytes,
             "roofline": _roofline("hbm", "decode_split_kernel (paged)+merge", k, PEAK_HBM_GBPS, "GB/s",
-                                  traffic(f"decode_split_kernel_paged@{w.name}", DECODE_SRC), per)}
+                                  traffic(f"decode_split_kernel_paged@{w.name}", DECODE_SRC), per, ms)}
 
 
 def bench_extend(steps: int, warmup: int):

@@ -68,6 +68,7 @@ CASES = [
     ("mha_E0", 2, 333, 4, 4, 32, 0, 0, False, 3),
     ("g16_short", 4, 65, 16, 1, 64, 64, 0, False, 0),
     ("g8_one_split", 2, 1500, 16, 2, 128, 512, 0, False, 1),
+    ("g8_16_splits", 1, 40000, 16, 2, 128, 1024, 0, False, 16),
 ]
 
 

@@ -160,6 +160,10 @@ DECODE_CASES = [
     # 16 heads per kv head and E = 2048: the in-kernel bias region would not
     # fit the LDS budget, so the bias rows come from the pre-pass
     ("G16_E2048_prepass", "bf16", 1, 3000, 16, 1, 128, 2048, 0, False, 1),
+    # eight and sixteen splits; E = 3000 spans a split boundary
+    ("L40000_s16", "bf16", 2, 40000, 16, 2, 128, 1024, 0, False, 16),
+    ("L40000_s16_log_E3000", "bf16", 1, 40000, 8, 1, 64, 3000, 0, True, 16),
+    ("fp32_L20000_s8", "fp32", 1, 20000, 4, 2, 32, 700, 0, False, 8),
 ]
 
 

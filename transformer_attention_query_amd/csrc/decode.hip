@@ -195,7 +195,11 @@ __global__ __launch_bounds__(kDecWaves * 64, sizeof(T) == 2 ? 2 : 1) void decode
   if (t >= (long long)p.B * p.n_split * p.n_hg) return;  // padding of the last group of 8
   const int hg = (int)(t % p.n_hg);
   long long rest = t / p.n_hg;
-  const int split = (int)(rest % p.n_split);
+  // Splits in reverse order: the last split (whose workgroups also make the
+  // bias) takes the lowest t of its sequence, so with an even split count
+  // and one head group it runs on an even XCD; the odd XCDs of this part
+  // stream a few percent slower (per-workgroup timestamps).
+  const int split = p.n_split - 1 - (int)(rest % p.n_split);
   const int b = (int)(rest / p.n_split);
 
   // keys [ks_lo, ke) of this split; steps start at ks (= ks_lo, or ks_lo
