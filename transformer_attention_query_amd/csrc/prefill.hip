@@ -56,6 +56,10 @@ namespace relattn {
 namespace {
 
 constexpr float kLazyRescaleLog2 = 8.0f;
+// Largest sum of one lane's 16 exponentials (taken against the running
+// maximum) that the DMA kernel's tile loop accepts without raising the
+// maximum: 2^12, so every p stays at most 4096.
+constexpr float kPsumLimit = 4096.0f;
 
 typedef int i32x8 __attribute__((ext_vector_type(8)));
 typedef unsigned char u8;
@@ -702,6 +706,14 @@ __device__ __attribute__((aligned(16))) const __bf16 kZeroPRow[kMaxDr] = {};
 
 template <int V> struct IntC { static constexpr int value = V; };
 
+// A use of x at this point: the code that makes x stays ahead of a following
+// branch instead of being moved past it (the work then overlaps the matrix
+// instructions before the branch).
+template <typename X>
+__device__ __forceinline__ void materialize(const X& x) {
+  asm volatile("" ::"v"(x));
+}
+
 // v_max3_f32 without the quieting of NaN inputs that fmaxf implies (callers
 // pass no NaN)
 __device__ __forceinline__ float max3_f32(float x, float y, float z) {
@@ -758,7 +770,6 @@ __global__ __launch_bounds__(512, 1) void prefill_dma_kernel(PrefillArgs p, int 
   const T* pcg = E > 0 ? static_cast<const T*>(p.pc) : kg;
 
   const float qk_scale = p.c1 / p.c2;
-  const float lazy = kLazyRescaleLog2 / p.c2;
   const float c2 = p.c2;
 
   bf16x8 qreg[D / 16];
@@ -778,8 +789,6 @@ __global__ __launch_bounds__(512, 1) void prefill_dma_kernel(PrefillArgs p, int 
   f32x16 o[D / 32];
 #pragma unroll
   for (int i = 0; i < D / 32; ++i) o[i] = zero16();
-  float m_run = -1e30f;
-  float l_run = 0.0f;
 
   const int i_last = min(q0 + N - 1, T_ - 1);
   const int kt_lo = W > 0 ? max(0, q0 - W + 1) / N : 0;
@@ -791,34 +800,44 @@ __global__ __launch_bounds__(512, 1) void prefill_dma_kernel(PrefillArgs p, int 
   const int dslot = lane & 15;
   const int qk_src = dslot ^ (drow & 7);        // K / P chunk landing in this slot
   const int qv_src = dslot ^ (2 * (drow & 3));  // V chunk landing in this slot
-  // K and V rows of this sequence and kv head: a uniform base plus a 32-bit
-  // byte offset per lane (the host keeps T*Hkv*D*2 below 2^31).
+  // K and V rows of this sequence and kv head: a uniform base advanced to the
+  // tile's first row plus a 32-bit byte offset per lane, clamped to the
+  // sequence's last row (the host keeps T*Hkv*D*2 below 2^31).
   const T* kseq = kg + (size_t(b) * T_ * Hkv + kvh) * D;
   const T* vseq = vg + (size_t(b) * T_ * Hkv + kvh) * D;
   const unsigned rowb = unsigned(Hkv) * D * 2;
+  const unsigned drow_b = unsigned(drow) * rowb;
   const unsigned kcol = 16u * unsigned(qk_src), vcol = 16u * unsigned(qv_src);
   const unsigned pcol = 16u * unsigned(min(qk_src, d_r / 8 - 1));
   const T* const zrow = kZeroPRow + 8 * qk_src;
   const unsigned lds0 = unsigned(reinterpret_cast<size_t>(smem)) + 1024u * unsigned(w);
   auto chunk0 = [&](int kt) { return (q0 - kt * N) / N; };
-  auto kv_off = [&](int kt) { return unsigned(min(kt * N + drow, T_ - 1)) * rowb; };
-  // K and the tile's new distance chunk of P rows (buffer kt & 1)
-  auto issue_kp = [&](int kt) {
-    const int buf = kt & 1;
-    dma16s(kseq, kv_off(kt) + kcol, __builtin_amdgcn_readfirstlane(lds0 + C::OFF_K + buf * C::TILEB));
-    if (E > 0 && max(0, q0 - (kt * N + N - 1)) < E) {  // only tiles with bias read their P chunk
-      const int d = (chunk0(kt) - 1) * N + drow;
-      const T* src = unsigned(d) < unsigned(E)
-                         ? reinterpret_cast<const T*>(reinterpret_cast<const char*>(pcg) + unsigned(d) * unsigned(2 * d_r) + pcol)
-                         : zrow;
-      dma16(src, __builtin_amdgcn_readfirstlane(lds0 + C::OFF_P + buf * C::TILEB));
-    }
+  auto tile_base = [&](const T* seq, int kt) {
+    return reinterpret_cast<const T*>(reinterpret_cast<const char*>(seq) + size_t(unsigned(kt * N) * rowb));
   };
+  auto lane_off = [&](int kt, unsigned col) { return min(drow_b, unsigned(T_ - 1 - kt * N) * rowb) + col; };
+  // K of tile kt (kt <= kt_hi) into K buffer buf
+  auto issue_k = [&](int kt, int buf) {
+    dma16s(tile_base(kseq, kt), lane_off(kt, kcol), __builtin_amdgcn_readfirstlane(lds0 + C::OFF_K + buf * C::TILEB));
+  };
+  // tile kt's new distance chunk of P rows into P buffer buf
+  auto issue_p = [&](int kt, int buf) {
+    const int d = (chunk0(kt) - 1) * N + drow;
+    const T* src = unsigned(d) < unsigned(E)
+                       ? reinterpret_cast<const T*>(reinterpret_cast<const char*>(pcg) + unsigned(d) * unsigned(2 * d_r) + pcol)
+                       : zrow;
+    dma16(src, __builtin_amdgcn_readfirstlane(lds0 + C::OFF_P + buf * C::TILEB));
+  };
+  // V of tile kt into V buffer kt & 1
   auto issue_v = [&](int kt) {
-    const int buf = kt & 1;
-    dma16s(vseq, kv_off(kt) + vcol, __builtin_amdgcn_readfirstlane(lds0 + C::OFF_V + buf * C::TILEB));
+    dma16s(tile_base(vseq, kt), lane_off(kt, vcol), __builtin_amdgcn_readfirstlane(lds0 + C::OFF_V + (kt & 1) * C::TILEB));
   };
   auto band_of = [&](int kt) { return E > 0 && max(0, q0 - (kt * N + N - 1)) < E; };
+  // K and, for a tile with bias, its P chunk (buffer kt & 1)
+  auto issue_kp = [&](int kt) {
+    issue_k(kt, kt & 1);
+    if (band_of(kt)) issue_p(kt, kt & 1);
+  };
   auto mask_of = [&](int kt) {
     const int j0 = kt * N;
     return (j0 + N - 1 > q0) || (W > 0 && q0 + 31 - j0 >= W);
@@ -928,11 +947,16 @@ __global__ __launch_bounds__(512, 1) void prefill_dma_kernel(PrefillArgs p, int 
     }
   };
 
-  // ---- prologue: tile kt_lo in LDS, the scores of tile kt_lo, K and P of
-  // tile kt_lo+1 in flight.  The compiler-visible wait also retires the q and
-  // r loads, so no wait for them lands inside the tile loop.
+  // ---- prologue: tile kt_lo's K (and P) in LDS, its scores, K and P of tile
+  // kt_lo+1 in flight.  The compiler-visible wait also retires the q and r
+  // loads, so no wait for them lands inside the tile loop.  The V buffer that
+  // the first iteration's PV reads (the tile before kt_lo) is zeroed, so that
+  // product adds nothing.
   issue_kp(kt_lo);
-  issue_v(kt_lo);
+  {
+    typedef unsigned u32x4z __attribute__((ext_vector_type(4)));
+    *reinterpret_cast<u32x4z*>(smem + C::OFF_V + ((kt_lo + 1) & 1) * C::TILEB + 16 * tid) = u32x4z{0, 0, 0, 0};
+  }
   dma_wait();
   __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0)
   __syncthreads();
@@ -961,40 +985,51 @@ __global__ __launch_bounds__(512, 1) void prefill_dma_kernel(PrefillArgs p, int 
     }
     if (mask_of(kt_lo)) apply_mask(kt_lo, s_cur);
   }
-  dma_wait();
-
-  // ---- tile loop.  Iteration kt runs the softmax and PV of tile kt and the
-  // scores of tile kt+1 in one straight-line block, so the matrix cores work
-  // on tile kt+1 while the VALU runs tile kt's exponentials, and the PV MFMAs
-  // overlap the next tile's shear.  LDS holds K and P of tile kt+1 and V of
-  // tile kt; the DMA fills K and P of tile kt+2 and V of tile kt+1.  Tiles
-  // with bias are a suffix of the range (the keys nearest the queries), so
-  // the loop runs in two parts; the last tile (no next scores) is peeled, and
-  // each part is unrolled by two so every LDS address is a lane offset plus a
-  // constant.
   // scores of tile kt are raw (units of q.k) when it has no bias
   auto raw_of = [&](int kt) { return RAWQK && !band_of(kt); };
-  auto begin_tile = [&](int kt, f32x16& s, float& cs) {
-    __syncthreads();  // K/P of tile kt+1 and V of tile kt are in LDS; all waves are past iteration kt-1
-    if (kt + 2 <= kt_hi) issue_kp(kt + 2);
-    if (kt + 1 <= kt_hi) issue_v(kt + 1);
-    if (kt > kt_lo && mask_of(kt)) apply_mask(kt, s);
-    // row maximum of tile kt (scores are never NaN: v_max3 without the
-    // quieting fmaxf would add) and the (rare) lazy rescale
+  // row maximum of a score tile in units of c2 (scores are never NaN:
+  // v_max3 without the quieting of fmaxf)
+  auto row_max = [&](const f32x16& s, bool raw) {
     const float m0 = max3_f32(s[0], s[1], s[2]), m1 = max3_f32(s[3], s[4], s[5]);
     const float m2 = max3_f32(s[6], s[7], s[8]), m3 = max3_f32(s[9], s[10], s[11]);
     const float m5 = max3_f32(s[12], s[13], s[14]);
     float mx = max3_f32(max3_f32(m0, m1, m2), max3_f32(m3, m5, s[15]), -INFINITY);
-    {
-      const unsigned u = __float_as_uint(mx);
-      const auto r2 = __builtin_amdgcn_permlane32_swap(u, u, false, false);
-      mx = max3_f32(__uint_as_float(r2[0]), __uint_as_float(r2[1]), -INFINITY);
-    }
-    const bool raw = raw_of(kt);
-    if (raw) mx *= qk_scale;  // in units of c2
-    cs = raw ? p.c1 : c2;
-    if (__builtin_amdgcn_ballot_w64(mx > m_run + lazy) != 0) {
-      const float m_new = fmaxf(m_run, mx);
+    const unsigned u = __float_as_uint(mx);
+    const auto r2 = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+    mx = max3_f32(__uint_as_float(r2[0]), __uint_as_float(r2[1]), -INFINITY);
+    return raw ? mx * qk_scale : mx;
+  };
+  // The running maximum starts at tile kt_lo's and is raised only when a
+  // tile's exponentials (taken against it) sum past kPsumLimit on some lane:
+  // then the tile's true maximum is taken, O and l are rescaled and the
+  // exponentials redone.  Below the limit every p is at most kPsumLimit, so
+  // nothing overflows; the result is exact either way.
+  float m_run = fmaxf(row_max(s_cur, raw_of(kt_lo)), -1e30f);
+  float l_run = 0.0f;
+  dma_wait();
+
+  // ---- tile loop.  Iteration kt runs, in one straight-line block, the
+  // scores of tile kt+1, the softmax of tile kt and the PV product of tile
+  // kt-1 (whose p it kept), so the matrix cores have independent work while
+  // the VALU runs the exponentials.  LDS holds K and P of tile kt+1 and V of
+  // tile kt-1; the DMA fills K and P of tile kt+2 and V of tile kt.  Tiles
+  // with bias are a suffix of the range (the keys nearest the queries), so
+  // the loop runs in two parts; the last tile is peeled, and each part is
+  // unrolled by two so every LDS address is a lane offset plus a constant
+  // and the p of consecutive tiles alternate between two register sets.
+  bf16x8 pbt[2][2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i) pbt[i][0] = pbt[i][1] = zero8<T>();
+  // Each iteration starts with a barrier (K/P of tile kt+1 and V of tile
+  // kt-1 are in LDS; all waves are past iteration kt-1) and issues its DMA
+  // without a branch: past the last tile, tile kt_hi is loaded again into the
+  // free buffer.  P chunks are loaded only by iterations whose next tile has
+  // bias; the first tile with bias that a plain iteration would have loaded
+  // gets its chunk between the two parts of the loop.
+  // the (rare) raise of the running maximum; pb and psum are redone
+  auto settle = [&](const f32x16& s, bool raw, float cs, bf16x8 (&pb)[2], float& psum) {
+    if (__builtin_amdgcn_ballot_w64(psum > kPsumLimit) != 0) {
+      const float m_new = fmaxf(m_run, row_max(s, raw));
       const float corr = fast_exp2(c2 * (m_run - m_new));
       m_run = m_new;
       l_run *= corr;
@@ -1002,24 +1037,28 @@ __global__ __launch_bounds__(512, 1) void prefill_dma_kernel(PrefillArgs p, int 
       for (int i = 0; i < D / 32; ++i)
 #pragma unroll
         for (int v = 0; v < 16; ++v) o[i][v] *= corr;
+      exps(s, cs, -c2 * m_run, pb, psum);
     }
-    return -c2 * m_run;
+    l_run += psum;
   };
   // one iteration whose next tile has no bias; PAR = kt & 1
   auto plain_step = [&](auto par, f32x16& s, f32x16& s_nx, int kt) {
     constexpr int PAR = decltype(par)::value, NP = PAR ^ 1;
-    float cs;
-    const float nm = begin_tile(kt, s, cs);
+    __syncthreads();
+    issue_k(min(kt + 2, kt_hi), PAR);
+    issue_v(kt);
+    constexpr bool raw = RAWQK;  // tiles before the band have no bias
+    const float cs = raw ? p.c1 : c2;
+    const float nm = -c2 * m_run;
     const unsigned char* kt_b = smem + C::OFF_K + NP * C::TILEB;
-    const unsigned char* vt_b = smem + C::OFF_V + PAR * C::TILEB;
-    bf16x8 pb[2];
+    const unsigned char* vt_b = smem + C::OFF_V + NP * C::TILEB;
     float psum;
     if constexpr (RAWQK) {  // raw scores of tile kt+1: one chain, no scaling
       s_nx = zero16();
 #pragma unroll
       for (int kk = 0; kk < D / 16; ++kk) mma32(frag_kp(kt_b, kk), qreg[kk], s_nx);
-      exps(s, cs, nm, pb, psum);
-      pv(vt_b, pb);
+      exps(s, cs, nm, pbt[PAR], psum);
+      pv(vt_b, pbt[NP]);
     } else {
       f32x16 s_odd = zero16();
       s_nx = zero16();
@@ -1029,35 +1068,48 @@ __global__ __launch_bounds__(512, 1) void prefill_dma_kernel(PrefillArgs p, int 
         if (kk & 1) mma32(kf, qreg[kk], s_odd);
         else mma32(kf, qreg[kk], s_nx);
       }
-      exps(s, cs, nm, pb, psum);
-      pv(vt_b, pb);
+      exps(s, cs, nm, pbt[PAR], psum);
+      pv(vt_b, pbt[NP]);
 #pragma unroll
       for (int v = 0; v < 16; ++v) s_nx[v] = (s_nx[v] + s_odd[v]) * qk_scale;
     }
-    l_run += psum;
+    materialize(pbt[PAR][0]);
+    materialize(pbt[PAR][1]);
+    settle(s, raw, cs, pbt[PAR], psum);
+    if (mask_of(kt + 1)) apply_mask(kt + 1, s_nx);
     dma_wait();  // this wave's parts of the next tiles have landed
   };
   // one iteration whose next tile has bias
   auto band_step = [&](auto par, f32x16& s, f32x16& s_nx, int kt) {
     constexpr int PAR = decltype(par)::value, NP = PAR ^ 1;
-    float cs;
-    const float nm = begin_tile(kt, s, cs);
+    __syncthreads();
+    const int kn = min(kt + 2, kt_hi);
+    issue_k(kn, PAR);
+    issue_p(kn, PAR);
+    issue_v(kt);
+    const bool raw = raw_of(kt);
+    const float cs = raw ? p.c1 : c2;
+    const float nm = -c2 * m_run;
     const unsigned char* kt_b = smem + C::OFF_K + NP * C::TILEB;
     const unsigned char* pt_b = smem + C::OFF_P + NP * C::TILEB;
-    const unsigned char* vt_b = smem + C::OFF_V + PAR * C::TILEB;
+    const unsigned char* vt_b = smem + C::OFF_V + NP * C::TILEB;
     f32x16 racc = zero16();
     s_nx = zero16();
 #pragma unroll
     for (int kk = 0; kk < D / 16; ++kk) mma32(frag_kp(pt_b, kk), rreg[kk], racc);
+    put_chunk(NP, racc);
 #pragma unroll
     for (int kk = 0; kk < D / 16; ++kk) mma32(frag_kp(kt_b, kk), qreg[kk], s_nx);
-    bf16x8 pb[2];
     float psum;
-    exps(s, cs, nm, pb, psum);
-    put_chunk(NP, racc);
-    pv(vt_b, pb);
+    exps(s, cs, nm, pbt[PAR], psum);
+    pv(vt_b, pbt[NP]);
     shear_add(NP, s_nx);
-    l_run += psum;
+    materialize(pbt[PAR][0]);
+    materialize(pbt[PAR][1]);
+#pragma unroll
+    for (int v = 0; v < 16; ++v) materialize(s_nx[v]);
+    settle(s, raw, cs, pbt[PAR], psum);
+    if (mask_of(kt + 1)) apply_mask(kt + 1, s_nx);
     dma_wait();  // this wave's parts of the next tiles have landed
   };
   f32x16 s_b;
@@ -1081,17 +1133,29 @@ __global__ __launch_bounds__(512, 1) void prefill_dma_kernel(PrefillArgs p, int 
   };
   const int kt_band = E > 0 ? max(kt_lo, (q0 - E + 1) / N) : kt_hi + 1;  // first tile with bias
   run(plain_step, min(kt_hi, kt_band - 1));
+  if (kt_band >= kt_lo + 2 && kt_band <= kt_hi) {
+    issue_p(kt_band, kt_band & 1);
+    dma_wait();
+  }
   if (kt < kt_hi && !band_of(kt_lo)) first_chunk(kt + 1);
   run(band_step, kt_hi);
-  {
-    float cs;
-    const float nm = begin_tile(kt, s_cur, cs);
-    bf16x8 pb[2];
+  // the last tile: its softmax with the PV of the one before, then its own PV
+  auto last_tile = [&](auto par) {
+    constexpr int PAR = decltype(par)::value, NP = PAR ^ 1;
+    __syncthreads();
+    issue_v(kt);
+    const bool raw = raw_of(kt);
+    const float cs = raw ? p.c1 : c2;
     float psum;
-    exps(s_cur, cs, nm, pb, psum);
-    pv(smem + C::OFF_V + (kt & 1) * C::TILEB, pb);
-    l_run += psum;
-  }
+    exps(s_cur, cs, -c2 * m_run, pbt[PAR], psum);
+    pv(smem + C::OFF_V + NP * C::TILEB, pbt[NP]);
+    settle(s_cur, raw, cs, pbt[PAR], psum);
+    dma_wait();
+    __syncthreads();
+    pv(smem + C::OFF_V + PAR * C::TILEB, pbt[PAR]);
+  };
+  if (kt & 1) last_tile(IntC<1>{});
+  else last_tile(IntC<0>{});
 
   // ---- epilogue: normalise, stage the wave's 32 x D tile in LDS, write whole
   // rows in 16-byte pieces
