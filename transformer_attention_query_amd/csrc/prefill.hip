@@ -832,6 +832,26 @@ __global__ __launch_bounds__(512, 1) void prefill_dma_kernel(PrefillArgs p, int 
   auto issue_v = [&](int kt) {
     dma16s(tile_base(vseq, kt), lane_off(kt, vcol), __builtin_amdgcn_readfirstlane(lds0 + C::OFF_V + (kt & 1) * C::TILEB));
   };
+  // K and V of a plain iteration, issued by waves 0-3 alone (eight rows each).
+  // Measured with per-wave cycle counters on the 32K shape: waves 0-3 reach
+  // the next barrier about 300 cycles per tile before waves 4-7 (their SIMD
+  // partners) and wait there, so they take over the partners' DMA work.
+  const int erow = 8 * (w & 3) + (lane >> 4);
+  const unsigned erow_b0 = unsigned(erow) * rowb, erow_b1 = unsigned(erow + 4) * rowb;
+  const unsigned ekcol0 = 16u * unsigned(dslot ^ (erow & 7)), ekcol1 = 16u * unsigned(dslot ^ ((erow + 4) & 7));
+  const unsigned evcol = 16u * unsigned(dslot ^ (2 * (erow & 3)));
+  const unsigned elds = unsigned(reinterpret_cast<size_t>(smem)) + 2048u * unsigned(w & 3);
+  auto issue_kv4 = [&](int ktk, int buf, int ktv) {
+    if (w < 4) {
+      const unsigned limk = unsigned(T_ - 1 - ktk * N) * rowb, limv = unsigned(T_ - 1 - ktv * N) * rowb;
+      const unsigned lk = __builtin_amdgcn_readfirstlane(elds + C::OFF_K + buf * C::TILEB);
+      const unsigned lv = __builtin_amdgcn_readfirstlane(elds + C::OFF_V + (ktv & 1) * C::TILEB);
+      dma16s(tile_base(kseq, ktk), min(erow_b0, limk) + ekcol0, lk);
+      dma16s(tile_base(kseq, ktk), min(erow_b1, limk) + ekcol1, lk + 1024);
+      dma16s(tile_base(vseq, ktv), min(erow_b0, limv) + evcol, lv);
+      dma16s(tile_base(vseq, ktv), min(erow_b1, limv) + evcol, lv + 1024);
+    }
+  };
   auto band_of = [&](int kt) { return E > 0 && max(0, q0 - (kt * N + N - 1)) < E; };
   // K and, for a tile with bias, its P chunk (buffer kt & 1)
   auto issue_kp = [&](int kt) {
@@ -1045,8 +1065,7 @@ __global__ __launch_bounds__(512, 1) void prefill_dma_kernel(PrefillArgs p, int 
   auto plain_step = [&](auto par, f32x16& s, f32x16& s_nx, int kt) {
     constexpr int PAR = decltype(par)::value, NP = PAR ^ 1;
     __syncthreads();
-    issue_k(min(kt + 2, kt_hi), PAR);
-    issue_v(kt);
+    issue_kv4(min(kt + 2, kt_hi), PAR, kt);
     constexpr bool raw = RAWQK;  // tiles before the band have no bias
     const float cs = raw ? p.c1 : c2;
     const float nm = -c2 * m_run;
