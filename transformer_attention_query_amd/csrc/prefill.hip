@@ -858,10 +858,11 @@ __global__ __launch_bounds__(512, 1) void prefill_dma_kernel(PrefillArgs p, int 
     issue_k(kt, kt & 1);
     if (band_of(kt)) issue_p(kt, kt & 1);
   };
-  auto mask_of = [&](int kt) {
-    const int j0 = kt * N;
-    return (j0 + N - 1 > q0) || (W > 0 && q0 + 31 - j0 >= W);
-  };
+  // A tile needs the mask when it holds a key past one of its queries (tile
+  // qt, the diagonal, and beyond) or one at least W before a query (tiles up
+  // to m_lo): one unsigned comparison.
+  const int m_lo = (W > 0 && q0 + 31 - W >= 0) ? (q0 + 31 - W) / N : -1;
+  auto mask_of = [&](int kt) { return unsigned(kt - m_lo - 1) >= unsigned(qt - m_lo - 1); };
   // Lane byte offsets of the MFMA fragments.  K / P A-operand of k-step kk:
   // row a, chunk (h2 + 2kk) ^ (a & 7); k-steps kk and kk+4 are 128 bytes
   // apart (chunk bit 3 lies outside the swizzle).
