@@ -653,10 +653,10 @@ hipError_t launch_prefill_tiles(const PrefillArgs& a, hipStream_t stream) {
 // for V (the 16 lanes of a transpose read cover the 32 banks once).
 //
 // The tile loop is software-pipelined inside each wave: one iteration runs
-// the softmax and PV of tile t together with the scores and relative logits
-// of tile t+1, in one straight-line block, so the matrix cores work on tile
-// t+1 while the VALU runs tile t's exponentials.  LDS holds K and P of tile
-// t+1 and V of tile t; the DMA fills K and P of tile t+2 and V of tile t+1
+// the scores and relative logits of tile t+1, the softmax of tile t and the
+// PV product of tile t-1 in one straight-line block, so the matrix cores
+// work while the VALU runs tile t's exponentials.  LDS holds K and P of tile
+// t+1 and V of tile t-1; the DMA fills K and P of tile t+2 and V of tile t
 // (all double-buffered by tile parity, one barrier per tile).  The loop is
 // unrolled by two so every LDS address is a per-lane offset plus a constant.
 // P rows for distances outside [0, E) are DMA'd from a zero row.
