@@ -112,6 +112,31 @@ def test_prefill_log_scale_large_bias_eight_heads_per_kv_head():
     assert_close(out[:, rows], ref, torch.bfloat16, "G8 log-scale P x50", lse[:, :, rows], lref)
 
 
+@pytest.mark.parametrize("alpha_sign,W,T,ls", [(1, 0, 1500, False), (1, 700, 1337, True), (-1, 0, 1100, False)])
+def test_prefill_rising_scores_raise_the_running_maximum(alpha_sign, W, T, ls):
+    """Scores that climb by more than 12 log2 units every 32 keys (one
+    dimension of k ramps with the key index, q holds a constant there), so in
+    the eight-heads kernel the exponentials taken against the running maximum
+    overflow the accepted sum on every tile and the maximum is raised, O and l
+    rescaled and the exponentials redone, tile after tile.  alpha < 0 (with
+    the ramp reversed) runs the kernel form that scales every score."""
+    E = 256
+    x = tinputs.make_prefill_inputs(1, T, 8, 1, 128, 64, E, "bf16", seed=17 + T)
+    ramp = torch.arange(T, dtype=torch.float32) * (4.0 * alpha_sign)
+    k = x["k"].float()
+    k[0, :, 0, 0] = ramp
+    x["k"] = k.to(torch.bfloat16)
+    q = x["q"].float()
+    q[..., 0] = 1.0
+    x["q"] = q.to(torch.bfloat16)
+    alpha = alpha_sign * ALPHA
+    # log2 units per 32 keys: s * log2(e) * |alpha| * 4 * 32
+    assert oracle.scale_factor(T, ls) * 1.4427 * ALPHA * 4 * 32 > 16
+    out, lse = _run_prefill(_cuda(x), alpha, E, W, ls)
+    ref, lref = oracle.prefill(x["q"], x["k"], x["v"], x["r"], x["P"], alpha, E, W, ls)
+    assert_close(out, ref, torch.bfloat16, f"rising scores alpha {alpha_sign} W {W}", lse, lref)
+
+
 def test_prefill_weights_via_identity_v():
     """V = identity makes each output row the attention-weight row: masked
     weights are exactly zero and each row sums to one."""
