@@ -27,6 +27,13 @@ CASES = [
     ("g8_log_scale", "bf16", [5000, 4200], [40, 70], 8, 1, 64, 200, 0, True, 64),
     ("fp32_paged32", "fp32", [90, 200], [90, 45], 4, 2, 32, 50, 17, False, 32),
     ("fp32_contig_E0", "fp32", [70, 33], [7, 33], 2, 1, 16, 0, 0, False, 0),
+    # eight or more query heads per kv head take the DMA kernel's extend form
+    # (contiguous, or paged with a power-of-two page size); other page sizes
+    # the tile kernel
+    ("g8_paged32_window", "bf16", [513, 77, 1], [200, 5, 1], 8, 1, 64, 64, 50, False, 32),
+    ("g8_paged96_tile_kernel", "bf16", [400, 250], [130, 250], 8, 1, 64, 100, 0, False, 96),
+    ("g16_contig_window_log", "bf16", [4500, 900], [300, 64], 16, 2, 128, 1024, 700, True, 0),
+    ("g8_paged128_ragged", "bf16", [1111, 37, 2050], [111, 37, 1], 8, 1, 128, 1024, 0, False, 128),
 ]
 
 

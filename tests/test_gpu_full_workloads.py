@@ -1,6 +1,7 @@
-"""GPU parity at the full sizes of the five named workloads, in the launch
-configuration bench.py times.  The tiny fp32 and 8K sliding-window prefills
-and both decodes are compared over their whole outputs.  The 2x32K causal
+"""GPU parity at the full sizes of the five named workloads and of the
+extend workload, in the launch configuration bench.py times.  The tiny fp32
+and 8K sliding-window prefills, both decodes and the extend are compared
+over their whole outputs.  The 2x32K causal
 prefill, whose full oracle would take minutes, is compared on every 16th
 query row counted from the last, plus every tile edge, the rel_extent edge
 and the first rows."""
@@ -53,3 +54,20 @@ def test_decode_workload(name):
     del xd
     ref, lref = oracle.decode(x["q"], x["k"], x["v"], x["r"], x["P"], w.alpha, w.E, w.W, w.log_scale)
     assert_close(out, ref, x["q"].dtype, name, lse, lref)
+
+
+def test_extend_workload():
+    """extend_4x1k_8k_paged as the bench runs it: four sequences of 8192
+    cached keys, the last 1024 of each new, over a paged cache."""
+    w = tinputs.WORKLOADS["extend_4x1k_8k_paged"]
+    x = tinputs.make_inputs(w, seed=0)
+    xd = {n: t.cuda() for n, t in x.items()}
+    paged = w.page_size > 0
+    out, lse = ra.extend(xd["q"], xd["k_pages"] if paged else xd["k"], xd["v_pages"] if paged else xd["v"], xd["r"],
+                         xd["P_cols"], w.alpha, w.E, w.W, w.log_scale, xd["q_start"], xd["kv_len"], w.n_new,
+                         block_table=xd["block_table"] if paged else None)
+    torch.cuda.synchronize()
+    del xd
+    ref, lref = oracle.extend(x["q"], x["k"], x["v"], x["r"], x["P"], w.alpha, w.E, w.W, w.log_scale,
+                              x["q_start"].tolist(), x["kv_len"].tolist())
+    assert_close(out, ref, x["q"].dtype, w.name, lse, lref)

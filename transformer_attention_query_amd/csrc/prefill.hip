@@ -329,7 +329,10 @@ __global__ __launch_bounds__(WAVES * 64, 1) void prefill_kernel(PrefillArgs p, i
     int jpage0 = 0;  // first key of the tile's page
     if constexpr (EXT) {
       if (p.btab != nullptr) {
-        const int pg = min(max(p.btab[size_t(b) * p.max_pages + j0 / p.page_size], 0), p.num_pages - 1);
+        // the table through the constant address space: a scalar load
+        typedef const __attribute__((address_space(4))) int* const_int_ptr;
+        const const_int_ptr bt = (const_int_ptr)(size_t)(p.btab + size_t(b) * p.max_pages);
+        const int pg = min(max(bt[j0 / p.page_size], 0), p.num_pages - 1);
         jpage0 = j0 - j0 % p.page_size;
         r0 = size_t(pg) * p.page_size;
       }
@@ -726,7 +729,9 @@ __device__ __forceinline__ float max3_f32(float x, float y, float z) {
 // maximum is scaled once and the exponent takes c1 = s*alpha*log2(e) in
 // place of c2, which saves a multiply per score (and one of two score
 // accumulation chains).
-template <bool RAWQK>
+// EXT: 0 prefill; 1 and 2 the extend form (rel_attn_extend) over a
+// contiguous (1) or paged (2, power-of-two page size) cache.
+template <bool RAWQK, int EXT = 0>
 __global__ __launch_bounds__(512, 1) void prefill_dma_kernel(PrefillArgs p, int n_qt, int n_items) {
   using C = DmaCfg;
   using T = __bf16;
@@ -736,7 +741,7 @@ __global__ __launch_bounds__(512, 1) void prefill_dma_kernel(PrefillArgs p, int 
   __shared__ __attribute__((aligned(16))) unsigned char smem[C::LDS_TOTAL];
   float* const Rs = reinterpret_cast<float*>(smem + C::OFF_R);
 
-  const int T_ = p.T, Hq = p.Hq, Hkv = p.Hkv, G = Hq / Hkv;
+  const int Hq = p.Hq, Hkv = p.Hkv, G = Hq / Hkv;
   const int d_r = p.d_r, E = p.E, W = p.W;
 
   // ---- workgroup -> (32-query tile, batch, kv head, group of 8 heads),
@@ -759,9 +764,34 @@ __global__ __launch_bounds__(512, 1) void prefill_dma_kernel(PrefillArgs p, int 
   const int a = lane & 31;
   const int h = kvh * G + hs * 8 + w;
 
-  const int q0 = qt * N;
+  // T_: keys (and positions) of this sequence.  Extend: its new rows are
+  // positions [pos0, T_), packed from row row0 of q, r and out; query tiles
+  // are aligned to 32 in positions, so the distance chunks are those of a
+  // prefill, and rows before pos0 are neither loaded nor stored.
+  int T_ = p.T, pos0 = 0, row0 = 0, qt_abs = qt;
+  float c1 = p.c1, c2 = p.c2;
+  if constexpr (EXT != 0) {
+    const int cap = EXT == 2 ? p.max_pages * p.page_size : p.cap;
+    T_ = max(0, min(p.kv_len[b], cap));
+    row0 = min(max(p.q_start[b], 0), p.total_q);
+    const int n = max(0, min(min(p.q_start[b + 1] - p.q_start[b], min(T_, p.max_q)), p.total_q - row0));
+    pos0 = T_ - n;
+    qt_abs = pos0 / N + qt;
+    if (n == 0 || qt_abs * N >= T_) return;
+    if (p.log_scale) {  // s = max(1, ln(kv_len) / ln(4096)), one per sequence
+      const float sc = fmaxf(1.0f, logf(float(T_)) * (1.0f / 8.317766166719343f));
+      c2 = sc * 1.4426950408889634f;
+      c1 = c2 * p.alpha;
+    }
+  }
+  const int q0 = qt_abs * N;
   const int qa = q0 + a;
-  const bool qvalid = qa < T_;
+  const bool qvalid = qa >= pos0 && qa < T_;
+  // packed row of query position x (prefill: b*T + x)
+  auto qrow_of = [&](int x) -> size_t {
+    if constexpr (EXT != 0) return size_t(row0 + x - pos0);
+    else return size_t(b) * T_ + x;
+  };
 
   const T* qg = static_cast<const T*>(p.q);
   const T* kg = static_cast<const T*>(p.k);
@@ -769,19 +799,18 @@ __global__ __launch_bounds__(512, 1) void prefill_dma_kernel(PrefillArgs p, int 
   const T* rg = static_cast<const T*>(p.r);
   const T* pcg = E > 0 ? static_cast<const T*>(p.pc) : kg;
 
-  const float qk_scale = p.c1 / p.c2;
-  const float c2 = p.c2;
+  const float qk_scale = c1 / c2;
 
   bf16x8 qreg[D / 16];
   {
-    const T* qrow = qg + ((size_t(b) * T_ + (qvalid ? qa : 0)) * Hq + h) * D + 8 * h2;
+    const T* qrow = qg + (qrow_of(qvalid ? qa : pos0) * Hq + h) * D + 8 * h2;
 #pragma unroll
     for (int kk = 0; kk < D / 16; ++kk) qreg[kk] = ld8_or_zero<T>(qrow + kk * 16, qvalid);
   }
   bf16x8 rreg[kMaxDr / 16];  // zero past d_r
   {
     const int nkr = d_r / 16;
-    const T* rrow = rg + ((size_t(b) * T_ + (qvalid ? qa : 0)) * Hq + h) * d_r + 8 * h2;
+    const T* rrow = rg + (qrow_of(qvalid ? qa : pos0) * Hq + h) * d_r + 8 * h2;
 #pragma unroll
     for (int kk = 0; kk < kMaxDr / 16; ++kk) rreg[kk] = ld8_or_zero<T>(rrow + kk * 16, E > 0 && qvalid && kk < nkr);
   }
@@ -802,23 +831,46 @@ __global__ __launch_bounds__(512, 1) void prefill_dma_kernel(PrefillArgs p, int 
   const int qv_src = dslot ^ (2 * (drow & 3));  // V chunk landing in this slot
   // K and V rows of this sequence and kv head: a uniform base advanced to the
   // tile's first row plus a 32-bit byte offset per lane, clamped to the
-  // sequence's last row (the host keeps T*Hkv*D*2 below 2^31).
-  const T* kseq = kg + (size_t(b) * T_ * Hkv + kvh) * D;
-  const T* vseq = vg + (size_t(b) * T_ * Hkv + kvh) * D;
+  // sequence's last row (prefill: the host keeps T*Hkv*D*2 below 2^31).
+  // Extend: row b*cap + j of a contiguous cache, or slot j % page_size of
+  // page btab[b][j / page_size] (a tile lies in one page; page ids clamped
+  // to the pool).
+  const T* kseq = kg + (EXT != 0 ? size_t(kvh) : (size_t(b) * T_ * Hkv + kvh)) * D;
+  const T* vseq = vg + (EXT != 0 ? size_t(kvh) : (size_t(b) * T_ * Hkv + kvh)) * D;
   const unsigned rowb = unsigned(Hkv) * D * 2;
+  const int page_shift = EXT == 2 ? __builtin_ctz(unsigned(p.page_size)) : 0;
   const unsigned drow_b = unsigned(drow) * rowb;
   const unsigned kcol = 16u * unsigned(qk_src), vcol = 16u * unsigned(qv_src);
   const unsigned pcol = 16u * unsigned(min(qk_src, d_r / 8 - 1));
   const T* const zrow = kZeroPRow + 8 * qk_src;
   const unsigned lds0 = unsigned(reinterpret_cast<size_t>(smem)) + 1024u * unsigned(w);
   auto chunk0 = [&](int kt) { return (q0 - kt * N) / N; };
-  auto tile_base = [&](const T* seq, int kt) {
-    return reinterpret_cast<const T*>(reinterpret_cast<const char*>(seq) + size_t(unsigned(kt * N) * rowb));
+  // page of tile kt (paged extend; 0 otherwise)
+  // (the table is read through the constant address space: scalar loads,
+  // which the vector-memory wait closing each iteration does not count)
+  typedef const __attribute__((address_space(4))) int* const_int_ptr;
+  const_int_ptr btab_row = EXT == 2 ? (const_int_ptr)(size_t)(p.btab + size_t(b) * p.max_pages) : nullptr;
+  auto page_of = [&](int kt) {
+    if constexpr (EXT == 2) return min(max(btab_row[(kt * N) >> page_shift], 0), p.num_pages - 1);
+    else return 0;
+  };
+  // address of tile kt's first row; pg = page_of(kt), looked up ahead of
+  // time by the loop (a scalar load waited for at the DMA issue would stall
+  // the issuing waves every tile)
+  auto tile_base = [&](const T* seq, int kt, int pg) {
+    const int j0 = kt * N;
+    if constexpr (EXT == 0) {
+      return reinterpret_cast<const T*>(reinterpret_cast<const char*>(seq) + size_t(unsigned(j0) * rowb));
+    } else {
+      size_t row = size_t(b) * p.cap + j0;  // cache row of the tile's first key
+      if constexpr (EXT == 2) row = (size_t(pg) << page_shift) + (j0 & (p.page_size - 1));
+      return reinterpret_cast<const T*>(reinterpret_cast<const char*>(seq) + row * rowb);
+    }
   };
   auto lane_off = [&](int kt, unsigned col) { return min(drow_b, unsigned(T_ - 1 - kt * N) * rowb) + col; };
   // K of tile kt (kt <= kt_hi) into K buffer buf
-  auto issue_k = [&](int kt, int buf) {
-    dma16s(tile_base(kseq, kt), lane_off(kt, kcol), __builtin_amdgcn_readfirstlane(lds0 + C::OFF_K + buf * C::TILEB));
+  auto issue_k = [&](int kt, int buf, int pg) {
+    dma16s(tile_base(kseq, kt, pg), lane_off(kt, kcol), __builtin_amdgcn_readfirstlane(lds0 + C::OFF_K + buf * C::TILEB));
   };
   // tile kt's new distance chunk of P rows into P buffer buf
   auto issue_p = [&](int kt, int buf) {
@@ -829,8 +881,8 @@ __global__ __launch_bounds__(512, 1) void prefill_dma_kernel(PrefillArgs p, int 
     dma16(src, __builtin_amdgcn_readfirstlane(lds0 + C::OFF_P + buf * C::TILEB));
   };
   // V of tile kt into V buffer kt & 1
-  auto issue_v = [&](int kt) {
-    dma16s(tile_base(vseq, kt), lane_off(kt, vcol), __builtin_amdgcn_readfirstlane(lds0 + C::OFF_V + (kt & 1) * C::TILEB));
+  auto issue_v = [&](int kt, int pg) {
+    dma16s(tile_base(vseq, kt, pg), lane_off(kt, vcol), __builtin_amdgcn_readfirstlane(lds0 + C::OFF_V + (kt & 1) * C::TILEB));
   };
   // K and V of a plain iteration, issued by waves 0-3 alone (eight rows each).
   // Measured with per-wave cycle counters on the 32K shape: waves 0-3 reach
@@ -841,28 +893,28 @@ __global__ __launch_bounds__(512, 1) void prefill_dma_kernel(PrefillArgs p, int 
   const unsigned ekcol0 = 16u * unsigned(dslot ^ (erow & 7)), ekcol1 = 16u * unsigned(dslot ^ ((erow + 4) & 7));
   const unsigned evcol = 16u * unsigned(dslot ^ (2 * (erow & 3)));
   const unsigned elds = unsigned(reinterpret_cast<size_t>(smem)) + 2048u * unsigned(w & 3);
-  auto issue_kv4 = [&](int ktk, int buf, int ktv) {
+  auto issue_kv4 = [&](int ktk, int buf, int ktv, int pgk, int pgv) {
     if (w < 4) {
       const unsigned limk = unsigned(T_ - 1 - ktk * N) * rowb, limv = unsigned(T_ - 1 - ktv * N) * rowb;
       const unsigned lk = __builtin_amdgcn_readfirstlane(elds + C::OFF_K + buf * C::TILEB);
       const unsigned lv = __builtin_amdgcn_readfirstlane(elds + C::OFF_V + (ktv & 1) * C::TILEB);
-      dma16s(tile_base(kseq, ktk), min(erow_b0, limk) + ekcol0, lk);
-      dma16s(tile_base(kseq, ktk), min(erow_b1, limk) + ekcol1, lk + 1024);
-      dma16s(tile_base(vseq, ktv), min(erow_b0, limv) + evcol, lv);
-      dma16s(tile_base(vseq, ktv), min(erow_b1, limv) + evcol, lv + 1024);
+      dma16s(tile_base(kseq, ktk, pgk), min(erow_b0, limk) + ekcol0, lk);
+      dma16s(tile_base(kseq, ktk, pgk), min(erow_b1, limk) + ekcol1, lk + 1024);
+      dma16s(tile_base(vseq, ktv, pgv), min(erow_b0, limv) + evcol, lv);
+      dma16s(tile_base(vseq, ktv, pgv), min(erow_b1, limv) + evcol, lv + 1024);
     }
   };
   auto band_of = [&](int kt) { return E > 0 && max(0, q0 - (kt * N + N - 1)) < E; };
   // K and, for a tile with bias, its P chunk (buffer kt & 1)
   auto issue_kp = [&](int kt) {
-    issue_k(kt, kt & 1);
+    issue_k(kt, kt & 1, page_of(kt));
     if (band_of(kt)) issue_p(kt, kt & 1);
   };
   // A tile needs the mask when it holds a key past one of its queries (tile
   // qt, the diagonal, and beyond) or one at least W before a query (tiles up
   // to m_lo): one unsigned comparison.
   const int m_lo = (W > 0 && q0 + 31 - W >= 0) ? (q0 + 31 - W) / N : -1;
-  auto mask_of = [&](int kt) { return unsigned(kt - m_lo - 1) >= unsigned(qt - m_lo - 1); };
+  auto mask_of = [&](int kt) { return unsigned(kt - m_lo - 1) >= unsigned(qt_abs - m_lo - 1); };
   // Lane byte offsets of the MFMA fragments.  K / P A-operand of k-step kk:
   // row a, chunk (h2 + 2kk) ^ (a & 7); k-steps kk and kk+4 are 128 bytes
   // apart (chunk bit 3 lies outside the swizzle).
@@ -1041,6 +1093,8 @@ __global__ __launch_bounds__(512, 1) void prefill_dma_kernel(PrefillArgs p, int 
   bf16x8 pbt[2][2];
 #pragma unroll
   for (int i = 0; i < 2; ++i) pbt[i][0] = pbt[i][1] = zero8<T>();
+  // pages of the K tile and the V tile the next iteration loads
+  int pg_k = page_of(min(kt_lo + 2, kt_hi)), pg_v = page_of(kt_lo);
   // Each iteration starts with a barrier (K/P of tile kt+1 and V of tile
   // kt-1 are in LDS; all waves are past iteration kt-1) and issues its DMA
   // without a branch: past the last tile, tile kt_hi is loaded again into the
@@ -1066,9 +1120,14 @@ __global__ __launch_bounds__(512, 1) void prefill_dma_kernel(PrefillArgs p, int 
   auto plain_step = [&](auto par, f32x16& s, f32x16& s_nx, int kt) {
     constexpr int PAR = decltype(par)::value, NP = PAR ^ 1;
     __syncthreads();
-    issue_kv4(min(kt + 2, kt_hi), PAR, kt);
+    // pages for the next iteration, loaded ahead of this iteration's DMA
+    // (both end at its closing wait)
+    const int pgk_n = page_of(min(kt + 3, kt_hi)), pgv_n = page_of(kt + 1);
+    issue_kv4(min(kt + 2, kt_hi), PAR, kt, pg_k, pg_v);
+    pg_k = pgk_n;
+    pg_v = pgv_n;
     constexpr bool raw = RAWQK;  // tiles before the band have no bias
-    const float cs = raw ? p.c1 : c2;
+    const float cs = raw ? c1 : c2;
     const float nm = -c2 * m_run;
     const unsigned char* kt_b = smem + C::OFF_K + NP * C::TILEB;
     const unsigned char* vt_b = smem + C::OFF_V + NP * C::TILEB;
@@ -1104,11 +1163,14 @@ __global__ __launch_bounds__(512, 1) void prefill_dma_kernel(PrefillArgs p, int 
     constexpr int PAR = decltype(par)::value, NP = PAR ^ 1;
     __syncthreads();
     const int kn = min(kt + 2, kt_hi);
-    issue_k(kn, PAR);
+    const int pgk_n = page_of(min(kt + 3, kt_hi)), pgv_n = page_of(kt + 1);  // next iteration's pages
+    issue_k(kn, PAR, pg_k);
     issue_p(kn, PAR);
-    issue_v(kt);
+    issue_v(kt, pg_v);
+    pg_k = pgk_n;
+    pg_v = pgv_n;
     const bool raw = raw_of(kt);
-    const float cs = raw ? p.c1 : c2;
+    const float cs = raw ? c1 : c2;
     const float nm = -c2 * m_run;
     const unsigned char* kt_b = smem + C::OFF_K + NP * C::TILEB;
     const unsigned char* pt_b = smem + C::OFF_P + NP * C::TILEB;
@@ -1163,9 +1225,9 @@ __global__ __launch_bounds__(512, 1) void prefill_dma_kernel(PrefillArgs p, int 
   auto last_tile = [&](auto par) {
     constexpr int PAR = decltype(par)::value, NP = PAR ^ 1;
     __syncthreads();
-    issue_v(kt);
+    issue_v(kt, pg_v);
     const bool raw = raw_of(kt);
-    const float cs = raw ? p.c1 : c2;
+    const float cs = raw ? c1 : c2;
     float psum;
     exps(s_cur, cs, -c2 * m_run, pbt[PAR], psum);
     pv(smem + C::OFF_V + NP * C::TILEB, pbt[NP]);
@@ -1198,30 +1260,43 @@ __global__ __launch_bounds__(512, 1) void prefill_dma_kernel(PrefillArgs p, int 
     const int i = lane + 64 * it;
     const int row = i >> 4, cv = i & 15;
     const int q = q0 + row;
-    if (q < T_)
-      *reinterpret_cast<u32x4*>(static_cast<T*>(p.out) + ((size_t(b) * T_ + q) * Hq + h) * D + cv * 8) =
+    if (q >= pos0 && q < T_)
+      *reinterpret_cast<u32x4*>(static_cast<T*>(p.out) + (qrow_of(q) * Hq + h) * D + cv * 8) =
           *reinterpret_cast<const u32x4*>(ot + row * OS + cv * 8);
   }
-  if (p.lse != nullptr && h2 == 0 && qvalid) p.lse[(size_t(b) * Hq + h) * T_ + qa] = (p.c2 * m_run + log2f(l_tot)) * kLn2;
+  if (p.lse != nullptr && h2 == 0 && qvalid) {
+    const size_t li = EXT != 0 ? size_t(h) * p.total_q + qrow_of(qa) : (size_t(b) * Hq + h) * T_ + qa;
+    p.lse[li] = (c2 * m_run + log2f(l_tot)) * kLn2;
+  }
 }
 
+template <int EXT>
 hipError_t launch_prefill_dma(const PrefillArgs& a, hipStream_t stream) {
-  const int n_qt = (a.T + 31) / 32;
+  // extend: the tiles of a sequence cover max_q rows at any alignment
+  const int n_qt = EXT != 0 ? (a.max_q + 31) / 32 + 1 : (a.T + 31) / 32;
   const long long n_items = (long long)n_qt * a.B * a.Hkv * (a.Hq / a.Hkv / 8);
   if (n_items > 0x7fffffffLL) return hipErrorInvalidConfiguration;
+  if (n_items == 0) return hipSuccess;
   if (a.c1 > 0.0f)
-    hipLaunchKernelGGL(prefill_dma_kernel<true>, dim3((unsigned)n_items), dim3(DmaCfg::THREADS), 0, stream, a, n_qt,
-                       (int)n_items);
-  else
-    hipLaunchKernelGGL(prefill_dma_kernel<false>, dim3((unsigned)n_items), dim3(DmaCfg::THREADS), 0, stream, a,
+    hipLaunchKernelGGL((prefill_dma_kernel<true, EXT>), dim3((unsigned)n_items), dim3(DmaCfg::THREADS), 0, stream, a,
                        n_qt, (int)n_items);
+  else
+    hipLaunchKernelGGL((prefill_dma_kernel<false, EXT>), dim3((unsigned)n_items), dim3(DmaCfg::THREADS), 0, stream,
+                       a, n_qt, (int)n_items);
   return hipGetLastError();
 }
 
 }  // namespace
 
 hipError_t launch_extend(int dtype, const PrefillArgs& a, hipStream_t stream) {
-  if (dtype == 1) return launch_prefill_tiles<__bf16, 8, true>(a, stream);
+  if (dtype == 1) {
+    // the DMA kernel for eight or more query heads per kv head (P addressed
+    // with 32-bit offsets; a paged cache with a power-of-two page size)
+    const bool dma = (a.Hq / a.Hkv) % 8 == 0 && (long long)a.E * a.d_r * 2 < (1LL << 31);
+    if (dma && a.btab == nullptr) return launch_prefill_dma<1>(a, stream);
+    if (dma && (a.page_size & (a.page_size - 1)) == 0) return launch_prefill_dma<2>(a, stream);
+    return launch_prefill_tiles<__bf16, 8, true>(a, stream);
+  }
   return launch_prefill_tiles<float, 2, true>(a, stream);
 }
 
@@ -1236,7 +1311,7 @@ hipError_t launch_prefill(int dtype, const PrefillArgs& a, hipStream_t stream) {
     // byte offsets.
     const bool offsets32 = (long long)a.T * a.Hkv * kHeadDim * 2 < (1LL << 31) &&
                            (long long)a.E * a.d_r * 2 < (1LL << 31);
-    if ((a.Hq / a.Hkv) % 8 == 0 && offsets32) return launch_prefill_dma(a, stream);
+    if ((a.Hq / a.Hkv) % 8 == 0 && offsets32) return launch_prefill_dma<0>(a, stream);
     return launch_prefill_tiles<__bf16, 8>(a, stream);
   }
   return launch_prefill_tiles<float, 2>(a, stream);
