@@ -549,8 +549,8 @@ def bench_extend(steps: int, warmup: int):
             "ms_per_step": round(ms, 5), "algorithmic_flops": flops,
             "config": {"B": w.B, "kv_len": w.T, "new_rows": w.n_new, "page_size": w.page_size, "Hq": w.Hq,
                        "Hkv": w.Hkv, "d_r": w.d_r, "rel_extent": w.E, "window": w.W},
-            "roofline": _roofline("mfma", "prefill_kernel (extend)", ach, PEAK_BF16_TFLOPS, "TFLOP/s",
-                                  traffic(f"prefill_kernel_extend@{w.name}", PREFILL_SRC), per)}
+            "roofline": _roofline("mfma", "prefill_dma_kernel (extend)", ach, PEAK_BF16_TFLOPS, "TFLOP/s",
+                                  traffic(f"prefill_dma_kernel_extend@{w.name}", PREFILL_SRC), per)}
 
 
 def bench_extend_mx(steps: int, warmup: int):
