@@ -261,10 +261,15 @@ __global__ __launch_bounds__(THREADS, 1) void bwd_dq_kernel(BackwardArgs p, int 
   auto dr_chunk = [&](int k, const bf16x8* g) {
     const __bf16* ps = slot(k);
 #pragma unroll
-    for (int c16 = 0; c16 < 2; ++c16)
+    for (int c16 = 0; c16 < 2; ++c16) {
+      bf16x8 pt[kMaxDr / 32];
+#pragma unroll
+      for (int cb = 0; cb < kMaxDr / 32; ++cb) pt[cb] = frag_tr<XS>(ps, c16, cb, lane);
+      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int cb = 0; cb < kMaxDr / 32; ++cb)
-        if (cb < (d_r + 31) / 32) mma32(frag_tr<XS>(ps, c16, cb, lane), g[c16], dr[cb]);
+        if (cb < (d_r + 31) / 32) mma32(pt[cb], g[c16], dr[cb]);
+    }
   };
 
   for (int kt = kt_lo; kt <= kt_hi; ++kt) {
@@ -289,13 +294,27 @@ __global__ __launch_bounds__(THREADS, 1) void bwd_dq_kernel(BackwardArgs p, int 
       const bool wmask = (j0 + N - 1 > qw0) || (W > 0 && qw0 + 31 - j0 >= W);
       const int c = c0 + qb;
 
-      // S^T = K Q^T: lane a's column is query a, register v key 8(v/4) + 4 h2 + v%4
+      // S^T = K Q^T: lane a's column is query a, register v key 8(v/4) + 4 h2 + v%4;
+      // dP^T = V dout^T.  One wave per SIMD: every fragment is read from LDS
+      // before the first product (the scheduling barrier keeps them there), so
+      // each product does not wait for its own read.
+      bf16x8 kf[D / 16], vf[D / 16];
+#pragma unroll
+      for (int kk = 0; kk < D / 16; ++kk) kf[kk] = ld8<__bf16>(Ks + a * XS + 8 * h2 + 16 * kk);
+#pragma unroll
+      for (int kk = 0; kk < D / 16; ++kk) vf[kk] = ld8<__bf16>(Vs + a * RS + 8 * h2 + 16 * kk);
+      __builtin_amdgcn_sched_barrier(0);
       f32x16 s = zero16(), s2 = zero16();
 #pragma unroll
       for (int kk = 0; kk < D / 16; ++kk) {
-        const bf16x8 kf = ld8<__bf16>(Ks + a * XS + 8 * h2 + 16 * kk);
-        if (kk & 1) mma32(kf, qreg[kk], s2);
-        else mma32(kf, qreg[kk], s);
+        if (kk & 1) mma32(kf[kk], qreg[kk], s2);
+        else mma32(kf[kk], qreg[kk], s);
+      }
+      f32x16 dp = zero16(), dp2 = zero16();
+#pragma unroll
+      for (int kk = 0; kk < D / 16; ++kk) {
+        if (kk & 1) mma32(vf[kk], doreg[kk], dp2);
+        else mma32(vf[kk], doreg[kk], dp);
       }
       if (wband) {
         // R^T of chunks c-1 (new) and c (kept from the previous tile, or made
@@ -303,8 +322,12 @@ __global__ __launch_bounds__(THREADS, 1) void bwd_dq_kernel(BackwardArgs p, int 
         f32x16 racc = zero16();
         {
           const __bf16* pr = slot(c - 1) + a * XS + 8 * h2;
+          bf16x8 pf[kMaxDr / 16];
 #pragma unroll
-          for (int kk = 0; kk < kMaxDr / 16; ++kk) mma32(ld8<__bf16>(pr + 16 * kk), rreg[kk], racc);
+          for (int kk = 0; kk < kMaxDr / 16; ++kk) pf[kk] = ld8<__bf16>(pr + 16 * kk);
+          __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+          for (int kk = 0; kk < kMaxDr / 16; ++kk) mma32(pf[kk], rreg[kk], racc);
         }
         if (rlast != c) {
           rprev = zero16();
@@ -343,23 +366,19 @@ __global__ __launch_bounds__(THREADS, 1) void bwd_dq_kernel(BackwardArgs p, int 
           if (dd < 0 || (W > 0 && dd >= W)) s[v] = -INFINITY;
         }
       }
-      // dP^T = V dout^T
-      f32x16 dp = zero16(), dp2 = zero16();
-#pragma unroll
-      for (int kk = 0; kk < D / 16; ++kk) {
-        const bf16x8 vf = ld8<__bf16>(Vs + a * RS + 8 * h2 + 16 * kk);
-        if (kk & 1) mma32(vf, doreg[kk], dp2);
-        else mma32(vf, doreg[kk], dp);
-      }
       // dS^T = P^T (dP^T - delta)
 #pragma unroll
       for (int v = 0; v < 16; ++v) s[v] = fast_exp2(fmaf(s[v], c2, -lse2)) * (dp[v] + dp2[v] - dl);
       // dq^T += K^T dS^T
 #pragma unroll
       for (int c16 = 0; c16 < 2; ++c16) {
+        bf16x8 kt_f[D / 32];
+#pragma unroll
+        for (int db = 0; db < D / 32; ++db) kt_f[db] = frag_tr<XS>(Ks, c16, db, lane);
+        __builtin_amdgcn_sched_barrier(0);
         const bf16x8 sb = to_bf16x8(s, c16);
 #pragma unroll
-        for (int db = 0; db < D / 32; ++db) mma32(frag_tr<XS>(Ks, c16, db, lane), sb, dq[db]);
+        for (int db = 0; db < D / 32; ++db) mma32(kt_f[db], sb, dq[db]);
       }
       if (wband) {
         // dS^T to the wave's buffer, row a (query), column b (key)
@@ -614,13 +633,27 @@ __global__ __launch_bounds__(THREADS, 1) void bwd_dkdv_kernel(BackwardArgs p, in
       if (!wdead) {
         const bool wband = E > 0 && max(0, i0 - (j0w + N - 1)) < E;
         const bool wmask = (j0w + N - 1 > i0) || (W > 0 && i0 + 31 - j0w >= W) || i0 + 31 >= T;
-        // S = Q K^T: lane a's column is key a, register v query 8(v/4) + 4 h2 + v%4
+        // S = Q K^T: lane a's column is key a, register v query 8(v/4) + 4 h2 + v%4;
+        // dP = dout V^T.  One wave per SIMD: every fragment is read from LDS
+        // before the first product (the scheduling barrier keeps them there),
+        // so each product does not wait for its own read.
+        bf16x8 qf[D / 16], df[D / 16];
+#pragma unroll
+        for (int kk = 0; kk < D / 16; ++kk) qf[kk] = ld8<__bf16>(Qs + a * XS + 8 * h2 + 16 * kk);
+#pragma unroll
+        for (int kk = 0; kk < D / 16; ++kk) df[kk] = ld8<__bf16>(Ds + a * XS + 8 * h2 + 16 * kk);
+        __builtin_amdgcn_sched_barrier(0);
         f32x16 s = zero16(), s2 = zero16();
 #pragma unroll
         for (int kk = 0; kk < D / 16; ++kk) {
-          const bf16x8 qf = ld8<__bf16>(Qs + a * XS + 8 * h2 + 16 * kk);
-          if (kk & 1) mma32(qf, kreg[kk], s2);
-          else mma32(qf, kreg[kk], s);
+          if (kk & 1) mma32(qf[kk], kreg[kk], s2);
+          else mma32(qf[kk], kreg[kk], s);
+        }
+        f32x16 dp = zero16(), dp2 = zero16();
+#pragma unroll
+        for (int kk = 0; kk < D / 16; ++kk) {
+          if (kk & 1) mma32(df[kk], vreg[kk], dp2);
+          else mma32(df[kk], vreg[kk], dp);
         }
         if (wband) {
           // R^T of the wave's chunks cw-1 and cw (query a of the tile and key b
@@ -631,10 +664,22 @@ __global__ __launch_bounds__(THREADS, 1) void bwd_dkdv_kernel(BackwardArgs p, in
           const __bf16* p1 = slot(cw) + a * RS + 8 * h2;
           const __bf16* rt = Rr + a * RS + 8 * h2;
 #pragma unroll
-          for (int kk = 0; kk < kMaxDr / 16; ++kk) {
-            const bf16x8 rf = ld8<__bf16>(rt + 16 * kk);
-            mma32(ld8<__bf16>(p0 + 16 * kk), rf, r0);
-            mma32(ld8<__bf16>(p1 + 16 * kk), rf, r1);
+          for (int half = 0; half < kMaxDr / 64; ++half) {
+            // four fragments of each operand at a time (all eight would spill)
+            bf16x8 rf[4], f0[4], f1[4];
+#pragma unroll
+            for (int k4 = 0; k4 < 4; ++k4) {
+              const int kk = 4 * half + k4;
+              rf[k4] = ld8<__bf16>(rt + 16 * kk);
+              f0[k4] = ld8<__bf16>(p0 + 16 * kk);
+              f1[k4] = ld8<__bf16>(p1 + 16 * kk);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int k4 = 0; k4 < 4; ++k4) {
+              mma32(f0[k4], rf[k4], r0);
+              mma32(f1[k4], rf[k4], r1);
+            }
           }
 #pragma unroll
           for (int g4 = 0; g4 < 4; ++g4) {
@@ -669,14 +714,6 @@ __global__ __launch_bounds__(THREADS, 1) void bwd_dkdv_kernel(BackwardArgs p, in
             if (dd < 0 || (W > 0 && dd >= W) || qi >= T) s[v] = -INFINITY;
           }
         }
-        // dP = dout V^T
-        f32x16 dp = zero16(), dp2 = zero16();
-#pragma unroll
-        for (int kk = 0; kk < D / 16; ++kk) {
-          const bf16x8 df = ld8<__bf16>(Ds + a * XS + 8 * h2 + 16 * kk);
-          if (kk & 1) mma32(df, vreg[kk], dp2);
-          else mma32(df, vreg[kk], dp);
-        }
         // P and dS = P (dP - delta), per query row
         f32x16 pp;
 #pragma unroll
@@ -693,12 +730,19 @@ __global__ __launch_bounds__(THREADS, 1) void bwd_dkdv_kernel(BackwardArgs p, in
         // dv^T += dout^T P, dk^T += Q^T dS
 #pragma unroll
         for (int c16 = 0; c16 < 2; ++c16) {
+          bf16x8 fd[D / 32], fq[D / 32];
+#pragma unroll
+          for (int db = 0; db < D / 32; ++db) {
+            fd[db] = frag_tr<XS>(Ds, c16, db, lane);
+            fq[db] = frag_tr<XS>(Qs, c16, db, lane);
+          }
+          __builtin_amdgcn_sched_barrier(0);
           const bf16x8 pb = to_bf16x8(pp, c16);
           const bf16x8 sb = to_bf16x8(s, c16);
 #pragma unroll
           for (int db = 0; db < D / 32; ++db) {
-            mma32(frag_tr<XS>(Ds, c16, db, lane), pb, dv[db]);
-            mma32(frag_tr<XS>(Qs, c16, db, lane), sb, dk[db]);
+            mma32(fd[db], pb, dv[db]);
+            mma32(fq[db], sb, dk[db]);
           }
         }
       }
