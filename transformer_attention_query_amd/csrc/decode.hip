@@ -6,7 +6,8 @@
 // single query i = L-1 the bias of key j is s * r.P[:, L-1-j] when
 // L-1-j < E.  The visible keys (all of them, or the last `window`) are cut
 // into num_splits contiguous chunks (the split-KV "num_splits" of the vLLM
-// page, section on the sheared-bias FA4 kernel); each workgroup owns one
+// page, section on the sheared-bias FA4 kernel; the first chunks a few
+// quanta longer than the last, which also makes the bias); each workgroup owns one
 // (sequence, split, kv head, group of up to 16 query heads), its waves take
 // interleaved 32-key steps, and it streams its chunk of K and V exactly once
 // for every query head of the group.  The
@@ -204,18 +205,22 @@ __global__ __launch_bounds__(kDecWaves * 64, sizeof(T) == 2 ? 2 : 1) void decode
 
   // keys [ks_lo, ke) of this split; steps start at ks (= ks_lo, or ks_lo
   // rounded down to 32 keys in the paged form, the keys below ks_lo masked)
-  int Lb = L, ks_lo = p.kv_lo + split * p.chunk;
+  // the first n_extra splits take extra more keys (the last split, which
+  // also makes the bias, that many fewer)
+  const int off = split * p.chunk + min(split, p.n_extra) * p.extra;
+  const int len = p.chunk + (split < p.n_extra ? p.extra : 0);
+  int Lb = L, ks_lo = p.kv_lo + off;
   float c1 = p.c1, bscale = 1.0f;
   if constexpr (PAGED) {
     Lb = min(max(p.kv_len[b], 1), min(L, p.max_pages * p.page_size));
-    ks_lo = ((p.W > 0 && Lb > p.W) ? Lb - p.W : 0) + split * p.chunk;
+    ks_lo = ((p.W > 0 && Lb > p.W) ? Lb - p.W : 0) + off;
     if (p.log_scale) {  // s = max(1, ln(kv_len) / ln(4096)), one per sequence
       bscale = fmaxf(1.0f, logf(float(Lb)) * (1.0f / 8.317766166719343f));
       c1 = bscale * p.alpha * 1.4426950408889634f;
     }
   }
   const int ks = PAGED ? (ks_lo & ~31) : ks_lo;
-  const int ke = min(ks_lo + p.chunk, Lb);
+  const int ke = min(ks_lo + len, Lb);
   const bool empty = ks_lo >= Lb;  // a split past a short sequence's keys
 
   const int hin = hg * 16 + c;  // head within the kv group
@@ -486,13 +491,11 @@ __global__ __launch_bounds__(kDecWaves * 64, sizeof(T) == 2 ? 2 : 1) void decode
   constexpr int NB = kDecDepth;
   constexpr int STRIDE = kDecWaves * kDecKeys;
   CH ring[NB];
-  // steps of this split: the plan's chunk, or (paged) up to the sequence's
-  // end in whole ring turns; none for an empty split
-  int j_end = ks + p.chunk;
-  if constexpr (PAGED) {
-    const int span = ke - ks;
-    j_end = empty ? ks : ks + min(p.chunk + 32, (span + NB * STRIDE - 1) / (NB * STRIDE) * (NB * STRIDE));
-  }
+  // steps of this split: its keys in whole ring turns (paged: up to the
+  // sequence's end); none for an empty split
+  const int span = ke - ks;
+  int j_end = ks + min(len, (span + NB * STRIDE - 1) / (NB * STRIDE) * (NB * STRIDE));
+  if constexpr (PAGED) j_end = empty ? ks : ks + min(len + 32, (span + NB * STRIDE - 1) / (NB * STRIDE) * (NB * STRIDE));
 #pragma unroll
   for (int bfi = 0; bfi < NB - 1; ++bfi) fetch(ks + w * kDecKeys + bfi * STRIDE, ring[bfi]);
   if constexpr (BL) {
@@ -719,6 +722,28 @@ hipError_t launch_decode_t(const DecodeArgs& a_in, hipStream_t stream) {
   DecodeArgs a = a_in;
   const long long grid = ((long long)a.B * a.n_hg * a.n_split + 7) / 8 * 8 * a.Hkv;
   if (grid > 0x7fffffffLL) return hipErrorInvalidConfiguration;
+  // The split that holds the last E keys also makes their bias before its
+  // loop.  Measured on 64 x 8K keys (bf16 and MXFP8 caches), that costs about
+  // as long as streaming K and V of half as many bytes as those E rows of P
+  // (every workgroup of the split reads the same rows, mostly from cache).
+  // The first splits take over that many keys (rounded to whole quanta, and
+  // at least one quantum stays with the last split), so the splits finish
+  // together: 106.2 -> 103.7 us (bf16), 67.0 -> 65.5 us (MXFP8).
+  a.extra = 0;
+  a.n_extra = 0;
+  if (a.E > 0 && a.n_split >= 2) {
+    const int vis = (a.W > 0 && a.L > a.W) ? a.W : a.L;
+    const size_t key_bytes = MX ? 2 * (kHeadDim + kHeadDim / 32) : 2 * kHeadDim * sizeof(T);
+    const size_t p_bytes = size_t(a.E < a.chunk ? a.E : a.chunk) * a.d_r * sizeof(T);
+    int q = (int)((p_bytes / (2 * key_bytes) + kDecSplitQuantum / 2) / kDecSplitQuantum);
+    const int last = vis - (a.n_split - 1) * a.chunk;
+    q = min(q, (last - 1) / kDecSplitQuantum);
+    if (q > 0) {
+      const int per = (q + a.n_split - 2) / (a.n_split - 1);
+      a.extra = per * kDecSplitQuantum;
+      a.n_extra = q / per;
+    }
+  }
   // Bias made in the split kernel when its LDS region leaves room for the
   // kernel's occupancy (two workgroups per CU for bf16, one for fp32): a
   // split's keys with bias span at most min(E, chunk) + 31 entries from its
@@ -726,7 +751,7 @@ hipError_t launch_decode_t(const DecodeArgs& a_in, hipStream_t stream) {
   if (a.E > 0) {
     constexpr size_t kLdsPerCu = 160 * 1024;
     const size_t budget = kLdsPerCu / (sizeof(T) == 2 ? 2 : 1) - dec_static_lds<T>();
-    const int span = (a.E < a.chunk ? a.E : a.chunk) + 31;
+    const int span = (a.E < a.chunk + a.extra ? a.E : a.chunk + a.extra) + 31;
     const int cols = (span + 15) / 16 * 16;
     const int ld = cols + 4;
     const int G = a.Hq / a.Hkv;

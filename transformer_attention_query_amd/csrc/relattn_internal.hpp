@@ -54,6 +54,8 @@ struct DecodeArgs {
   float c1, c2;
   int n_split;      // splits of the visible key range
   int chunk;        // keys per split (multiple of 32)
+  int extra = 0;    // the first n_extra splits hold chunk + extra keys (set by the launcher)
+  int n_extra = 0;
   int kv_lo;        // first visible key (L - W for a window, else 0)
   int n_hg;         // groups of 16 query heads per kv head
   int rl_base;      // key j reads bias row entry j - L + rl_base
