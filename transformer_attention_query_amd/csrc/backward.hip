@@ -17,10 +17,11 @@
 //                      of one head and walks the visible key tiles.  S^T = K Q^T
 //                      and the sheared bias as in the forward; dP^T = V dout^T;
 //                      dq^T += K^T dS^T (K read transposed from LDS); for band
-//                      tiles the wave writes dS^T to a private LDS buffer and
-//                      reads it back along the diagonals (the shear run
-//                      backwards) as the B operand of dr^T += P_cols^T G^T,
-//                      G[i][d] = ds_{i,i-d}, over the tile's 64 distances.
+//                      tiles the wave writes dS^T (bf16) to a private LDS ring
+//                      that also holds the previous tile's, and reads it back
+//                      along the diagonals (the shear run backwards) as the B
+//                      operand of dr^T += P_cols^T G^T, G[i][d] = ds_{i,i-d},
+//                      one 32-distance chunk per tile.
 //   bwd_dkdv_kernel    key-major: a wave owns 32 keys (their K and V rows stay
 //                      in registers as MFMA operands) and walks the query tiles
 //                      that see them, for each head of a subset of the group.
@@ -38,12 +39,20 @@ namespace relattn {
 namespace {
 
 typedef short s16x4 __attribute__((ext_vector_type(4)));
-typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 
 __device__ __forceinline__ s16x4 lds_read_tr(const __bf16* p) {
   return __builtin_amdgcn_ds_read_tr16_b64_v4i16(
       (lds_s16x4*)((__attribute__((address_space(3))) char*)((__attribute__((address_space(3))) void*)p)));
+}
+
+// One bf16 from LDS.  Volatile, because the compiler would otherwise merge
+// runs of these into 8-byte reads at 2-byte-aligned addresses, which the LDS
+// serves slowly (measured: the whole backward 5 % slower than with single
+// reads).
+__device__ __forceinline__ __bf16 lds_ld_bf16(const __bf16* p) {
+  return *((const volatile __attribute__((address_space(3))) __bf16*)((const __attribute__((address_space(3))) void*)p));
 }
 
 // A operand of X^T for a row-major bf16 tile X [rows][STRIDE] in LDS:
@@ -75,7 +84,7 @@ constexpr int THREADS = 64 * WAVES;
 constexpr int XS = D + 24;     // stride of tiles read both by rows and transposed (304-byte rows)
 constexpr int RS = D + 8;      // stride of tiles read by rows only (272-byte rows)
 constexpr int LS = 2 * N + 4;  // shear buffer row stride (floats)
-constexpr int GS = 34;         // dS^T buffer row stride (floats), inside the shear buffer
+constexpr int DSS = 104;       // dS^T ring row stride (bf16): three 32-key slots + pad
 constexpr int VECS = N * (D / 8) / THREADS;  // 16-byte vectors per thread for a 32 x 128 tile
 static_assert(VECS == 2, "tile split");
 
@@ -143,7 +152,8 @@ struct DqLds {
   static constexpr size_t V = size_t(N) * RS * 2;
   static constexpr size_t P = size_t(WAVES + 1) * N * XS * 2;
   static constexpr size_t R = size_t(WAVES) * N * LS * 4;
-  static constexpr size_t TOTAL = K + V + P + R;
+  static constexpr size_t G = size_t(WAVES) * N * DSS * 2;
+  static constexpr size_t TOTAL = K + V + P + R + G;
   static_assert(TOTAL <= 160 * 1024, "LDS of one workgroup");
 };
 
@@ -251,13 +261,28 @@ __global__ __launch_bounds__(THREADS, 1) void bwd_dq_kernel(BackwardArgs p, int 
   f32x16 rprev = zero16();
   int rlast = INT_MIN;
   // dr runs one distance chunk per tile: chunk c of a tile takes its entries
-  // with offset delta <= a from this tile's dS and those with delta > a from
-  // the previous tile's (where it was chunk c-1), carried here as bf16
-  // operands; glast names the chunk the carry belongs to.
-  bf16x8 gcar[2];
-  gcar[0] = zero8<__bf16>();
-  gcar[1] = zero8<__bf16>();
+  // with offset o <= a from this tile's dS and those with o > a from the
+  // previous tile's (where it was chunk c-1); glast names the chunk the
+  // previous tile's entries still owe.  Row a of the wave's dS^T ring (bf16)
+  // has three 32-key slots: a tile of parity p stores its row at slots p and
+  // 2 and reads entry o at index 64 - 32p + a - o.  For p = 0 that is slot 2
+  // (this tile, o <= a) or slot 1 (the previous, odd tile); for p = 1 slot 1
+  // (this tile) or slot 0 (the previous, even tile): one read per entry, no
+  // selection.  An odd tile's copy in slot 2 is never read.
+  __bf16* grow = reinterpret_cast<__bf16*>(smem + DqLds::K + DqLds::V + DqLds::P + DqLds::R) + (w * N + a) * DSS;
   int glast = INT_MIN;
+  auto zero_slot = [&](int off) {  // this lane's 16 entries of one slot
+    st8<__bf16>(grow + off + 16 * h2, zero8<__bf16>());
+    st8<__bf16>(grow + off + 16 * h2 + 8, zero8<__bf16>());
+  };
+  auto read_g = [&](int par, bf16x8* g) {
+    // k-slot t of step c16 is offset o = 16 c16 + 8(t/4) + 4 h2 + t%4
+    const __bf16* rb = grow + (64 - 32 * par) + a - 4 * h2 - 27;
+#pragma unroll
+    for (int c16 = 0; c16 < 2; ++c16)
+#pragma unroll
+      for (int t = 0; t < 8; ++t) g[c16][t] = lds_ld_bf16(rb + 27 - (16 * c16 + 8 * (t >> 2) + (t & 3)));
+  };
   auto dr_chunk = [&](int k, const bf16x8* g) {
     const __bf16* ps = slot(k);
 #pragma unroll
@@ -284,11 +309,16 @@ __global__ __launch_bounds__(THREADS, 1) void bwd_dq_kernel(BackwardArgs p, int 
     const bool wdead = qw0 >= T || j0 > qw0 + 31 || (W > 0 && qw0 - (j0 + N - 1) >= W);
     const bool wband = !wdead && E > 0 && max(0, qw0 - (j0 + N - 1)) < E;
     if (!wband && glast != INT_MIN) {
-      // the carried chunk's other entries fall on this tile, which adds none
-      // (tiles after a band tile are band tiles or entirely masked); the ring
-      // still holds the chunk (it is this tile's chunk c)
-      dr_chunk(glast, gcar);
+      // the owed chunk's other entries fall on this tile, which adds none
+      // (tiles after a band tile are band tiles or entirely masked): its slot
+      // reads as zero.  The P ring still holds the chunk (this tile's chunk c).
+      zero_slot(64 - 32 * (kt & 1));
+      wave_lds_fence();
+      bf16x8 g[2];
+      read_g(kt & 1, g);
+      dr_chunk(glast, g);
       glast = INT_MIN;
+      wave_lds_fence();
     }
     if (!wdead) {
       const bool wmask = (j0 + N - 1 > qw0) || (W > 0 && qw0 + 31 - j0 >= W);
@@ -370,49 +400,35 @@ __global__ __launch_bounds__(THREADS, 1) void bwd_dq_kernel(BackwardArgs p, int 
 #pragma unroll
       for (int v = 0; v < 16; ++v) s[v] = fast_exp2(fmaf(s[v], c2, -lse2)) * (dp[v] + dp2[v] - dl);
       // dq^T += K^T dS^T
+      bf16x8 sb[2];
 #pragma unroll
       for (int c16 = 0; c16 < 2; ++c16) {
         bf16x8 kt_f[D / 32];
 #pragma unroll
         for (int db = 0; db < D / 32; ++db) kt_f[db] = frag_tr<XS>(Ks, c16, db, lane);
         __builtin_amdgcn_sched_barrier(0);
-        const bf16x8 sb = to_bf16x8(s, c16);
+        sb[c16] = to_bf16x8(s, c16);
 #pragma unroll
-        for (int db = 0; db < D / 32; ++db) mma32(kt_f[db], sb, dq[db]);
+        for (int db = 0; db < D / 32; ++db) mma32(kt_f[db], sb[c16], dq[db]);
       }
       if (wband) {
-        // dS^T to the wave's buffer, row a (query), column b (key)
-        float* gs = rs + a * GS;
+        // dS^T (the bf16 operands of the dq product) to row a of the ring:
+        // key 8 g4 + 4 h2 + e is element 4 g4 + e of the lane's sixteen
+        const int par = kt & 1;
+        if (glast != c) zero_slot(32 * (1 - par));  // no previous tile owes this chunk
 #pragma unroll
-        for (int g4 = 0; g4 < 4; ++g4)
+        for (int g4 = 0; g4 < 4; ++g4) {
+          bf16x4 x;
 #pragma unroll
-          for (int e = 0; e < 4; e += 2) {
-            f32x2 x;
-            x[0] = s[4 * g4 + e];
-            x[1] = s[4 * g4 + e + 1];
-            *reinterpret_cast<f32x2*>(gs + 8 * g4 + 4 * h2 + e) = x;
-          }
+          for (int e = 0; e < 4; ++e) x[e] = sb[g4 >> 1][4 * (g4 & 1) + e];
+          *reinterpret_cast<bf16x4*>(grow + 32 * par + 8 * g4 + 4 * h2) = x;
+          *reinterpret_cast<bf16x4*>(grow + 64 + 8 * g4 + 4 * h2) = x;
+        }
         wave_lds_fence();
-        // dr^T += P_cols^T G^T, G[a][32k + o] = dS[a][key a + 32(c - k) - o]:
-        // k-slot t of step c16 is offset o = 16 c16 + 8(t/4) + 4 h2 + t%4 of a
-        // chunk.  Offsets o <= a of chunk c read key a - o of this tile;
-        // offsets o > a read key a + 32 - o, which belongs to chunk c-1 here
-        // (chunk c's are in the carry).  Both are key (a - o) mod 32.
-        const bool carry_ok = glast == c;
-        bf16x8 gb[2], gn[2];
-#pragma unroll
-        for (int c16 = 0; c16 < 2; ++c16)
-#pragma unroll
-          for (int t = 0; t < 8; ++t) {
-            const int o = 16 * c16 + 8 * (t >> 2) + 4 * h2 + (t & 3);
-            const __bf16 x = __bf16(gs[(a - o) & (N - 1)]);
-            const bool low = o <= a;
-            gb[c16][t] = low ? x : (carry_ok ? gcar[c16][t] : __bf16(0.0f));
-            gn[c16][t] = low ? __bf16(0.0f) : x;
-          }
-        dr_chunk(c, gb);
-        gcar[0] = gn[0];
-        gcar[1] = gn[1];
+        // dr^T += P_cols^T G^T, G[a][32k + o] = dS[a][key a + 32(c - k) - o]
+        bf16x8 g[2];
+        read_g(par, g);
+        dr_chunk(c, g);
         glast = c - 1;
         wave_lds_fence();
       }
@@ -425,7 +441,13 @@ __global__ __launch_bounds__(THREADS, 1) void bwd_dq_kernel(BackwardArgs p, int 
     }
   }
 
-  if (glast != INT_MIN) dr_chunk(glast, gcar);  // the last carry (no further tile adds to it)
+  if (glast != INT_MIN) {  // the last owed chunk (no further tile adds to it)
+    zero_slot(64 - 32 * ((kt_hi + 1) & 1));
+    wave_lds_fence();
+    bf16x8 g[2];
+    read_g((kt_hi + 1) & 1, g);
+    dr_chunk(glast, g);
+  }
 
   // ---- epilogue: dq = s alpha dq^T^T, dr = s dr^T^T through a per-wave LDS
   // staging tile, written back as whole rows
