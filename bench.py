@@ -22,6 +22,8 @@ Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
        python bench.py --copy-calibration   (a plain 1 GiB device copy, for
            scaling the HBM byte counters FETCH_SIZE / WRITE_SIZE)
        python bench.py --hbm-ceiling   (plain copy and sum rates: a yardstick)
+       python bench.py --ceilings   (plain MFMA, exp, LDS-read rates and the
+           shader clock: yardsticks beside the published peaks)
        python bench.py --traffic-from FETCH_CSV WRITE_CSV --kernel-key KEY
                        --kernel-match SUBSTR[,SUBSTR...] --src FILE[,FILE...]
            (turn two rocprofv3 --pmc counter CSVs into the per-launch HBM
@@ -694,7 +696,7 @@ def copy_calibration(nbytes: int = 1 << 30, reps: int = 3):
 
 def hbm_ceiling(nbytes: int = 4 << 30, reps: int = 10):
     """What plain streaming reaches on this GPU, as a yardstick for the decode
-    fractions: a read-only kernel (libhbmprobe.so, built beside the library:
+    fractions: a read-only kernel (libceilings.so, built beside the library:
     16-byte loads, four in flight per thread, grid-stride) over nbytes at
     several grid sizes, and torch's device-to-device copy (reads and writes
     nbytes); HIP events around `reps` back-to-back runs after one warm-up."""
@@ -737,6 +739,79 @@ def hbm_ceiling(nbytes: int = 4 << 30, reps: int = 10):
     print(json.dumps({"hbm_ceiling": out, "peak_GB_per_s": PEAK_HBM_GBPS}), flush=True)
 
 
+def compute_ceilings():
+    """What plain code of each kind reaches on this GPU (libceilings.so):
+    back-to-back bf16 32x32x16 MFMAs with four independent accumulators per
+    wave at 1, 2 and 4 waves per SIMD; independent v_exp_f32 chains; 16-byte
+    LDS reads; and the shader clock against the 100 MHz real-time counter.
+    HIP events around one launch after a warm-up launch."""
+    import ctypes
+    import torch
+    from transformer_attention_query_amd import build as _build
+    lib = ctypes.CDLL(_build.PROBE_LIB)
+    lib.ceiling_threads.argtypes = [ctypes.c_int]
+    lib.ceiling_threads.restype = ctypes.c_size_t
+    lib.compute_probe.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
+    lib.compute_probe.restype = ctypes.c_int
+    lib.clock_probe.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]
+    lib.clock_probe.restype = ctypes.c_int
+    stream = torch.cuda.current_stream()
+    n_cu = torch.cuda.get_device_properties(0).multi_processor_count
+
+    def timed(fn):
+        fn()
+        torch.cuda.synchronize()
+        t0 = torch.cuda.Event(enable_timing=True)
+        t1 = torch.cuda.Event(enable_timing=True)
+        t0.record(stream)
+        fn()
+        t1.record(stream)
+        torch.cuda.synchronize()
+        return t0.elapsed_time(t1) * 1e-3  # seconds
+
+    def probe(kind, blocks, iters):
+        sink = torch.empty(int(lib.ceiling_threads(blocks)), dtype=torch.int32, device="cuda")
+
+        def run():
+            rc = lib.compute_probe(kind, blocks, iters, sink.data_ptr(), stream.cuda_stream)
+            if rc != 0:
+                raise RuntimeError(f"compute_probe({kind}) returned {rc}")
+        return timed(run)
+
+    out = {"compute_units": n_cu}
+    blocks = 256
+    sink = torch.empty(int(lib.ceiling_threads(blocks)), dtype=torch.int32, device="cuda")
+    ticks = torch.zeros(2 * blocks, dtype=torch.int64, device="cuda")
+    rc = lib.clock_probe(blocks, 200000, ticks.data_ptr(), sink.data_ptr(), stream.cuda_stream)
+    torch.cuda.synchronize()
+    if rc != 0:
+        raise RuntimeError(f"clock_probe returned {rc}")
+    t = ticks.view(blocks, 2).double().cpu()
+    mhz = float((t[:, 0] / t[:, 1]).median()) * 100.0
+    out["shader_clock_MHz"] = round(mhz, 1)
+    mfma = {}
+    for waves_per_simd in (1, 2, 4):
+        blocks = n_cu * waves_per_simd
+        iters = 20000
+        sec = probe(0, blocks, iters)
+        flops = blocks * 4 * iters * 4 * 32768
+        tf = flops / sec / 1e12
+        mfma[f"{waves_per_simd}_wave_per_simd"] = {"TFLOP_per_s": round(tf, 1), "frac_of_peak": round(tf / PEAK_BF16_TFLOPS, 4)}
+    out["mfma_bf16_32x32x16"] = mfma
+    blocks, iters = 4 * n_cu, 5000
+    sec = probe(1, blocks, iters)
+    n_exp = blocks * 256 * iters * 8
+    out["v_exp_f32"] = {"G_per_s": round(n_exp / sec / 1e9, 1),
+                        "per_clock_per_cu": round(n_exp / sec / (mhz * 1e6) / n_cu, 1)}
+    for kind, name in ((2, "lds_read_b128_consecutive"), (3, "lds_read_b128_fragment_rows")):
+        blocks, iters = 4 * n_cu, 5000
+        sec = probe(kind, blocks, iters)
+        nbytes = blocks * 256 * iters * 4 * 16
+        out[name] = {"TB_per_s": round(nbytes / sec / 1e12, 2),
+                     "bytes_per_clock_per_cu": round(nbytes / sec / (mhz * 1e6) / n_cu, 1)}
+    print(json.dumps({"ceilings": out, "peak_bf16_TFLOP_per_s": PEAK_BF16_TFLOPS}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -746,6 +821,7 @@ def main():
     ap.add_argument("--only", default="", help="comma-separated workloads / extra sections to run")
     ap.add_argument("--copy-calibration", action="store_true")
     ap.add_argument("--hbm-ceiling", action="store_true", help="time a plain copy and a plain sum (yardstick)")
+    ap.add_argument("--ceilings", action="store_true", help="plain MFMA, exp and LDS rates and the shader clock")
     ap.add_argument("--calibration-from", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"))
     ap.add_argument("--traffic-from", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"))
     ap.add_argument("--kernel-key")
@@ -775,6 +851,9 @@ def main():
         return
     if args.hbm_ceiling:
         hbm_ceiling()
+        return
+    if args.ceilings:
+        compute_ceilings()
         return
 
     only = set(s for s in args.only.split(",") if s)

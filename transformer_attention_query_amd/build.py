@@ -20,9 +20,9 @@ CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD_DIR = os.path.join(ROOT, "_build")
 LIB = os.path.join(HERE, "librelattn.so")
-# a plain streaming-read kernel for bench.py's HBM yardstick (not part of the ABI)
-PROBE_SOURCE = "hbm_probe.hip"
-PROBE_LIB = os.path.join(HERE, "libhbmprobe.so")
+# yardstick kernels for bench.py (streaming read, MFMA, exp, LDS, clock; not part of the ABI)
+PROBE_SOURCE = "ceilings.hip"
+PROBE_LIB = os.path.join(HERE, "libceilings.so")
 
 SOURCES = ["api.cpp", "prefill.hip", "decode.hip", "rel_logits.hip", "prologue.hip", "mx.hip", "backward.hip"]
 ARCH = "gfx950"
