@@ -58,6 +58,10 @@ CONTIGUOUS = [
     # the in-LDS path next to them
     ("bf16_g8_E1024_lds", "bf16", 2, 3000, 16, 2, 128, 1024, 0, False, 0, False),
     ("fp32_g16_E1024_lds", "fp32", 1, 2000, 16, 1, 128, 1024, 0, False, 1, False),
+    # the first splits one quantum longer than the last: the bias keys then
+    # span the last two splits
+    ("bf16_g8_E1200_lead_s2", "bf16", 2, 2000, 16, 2, 128, 1200, 0, False, 2, False),
+    ("bf16_g8_E1024_lead_s4", "bf16", 1, 4000, 16, 2, 128, 1024, 0, False, 4, False),
 ]
 
 
@@ -82,6 +86,9 @@ PAGED = [
     ("bf16_g16_E2048_W1500", "bf16", [3001, 2222, 1500], 16, 1, 128, 2048, 1500, False, 128, 1, True),
     ("fp32_g16_E1600_mod4", "fp32", [1800, 1601, 1702, 1403], 16, 1, 32, 1600, 0, False, 32, 1, True),
     ("bf16_g16_E600_lds", "bf16", [3000, 2049, 2502, 1999], 16, 1, 128, 600, 0, False, 64, 1, False),
+    # two splits, the first one quantum longer: the bias of the shorter
+    # sequences spans both, one sequence has no keys in the second
+    ("bf16_g8_E1000_lead_s2", "bf16", [2000, 1500, 1999, 64], 16, 2, 128, 1000, 0, False, 64, 2, False),
 ]
 
 
