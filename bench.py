@@ -837,7 +837,7 @@ def main():
         return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU only: the relative-attention kernels run on a single MI355X "
-              "and this build has no multi-GPU path (--gpus must be 1)", file=sys.stderr)
+              "and the library has no multi-GPU path (--gpus must be 1)", file=sys.stderr)
         sys.exit(2)
 
     import torch
